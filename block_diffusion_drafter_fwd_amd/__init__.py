@@ -1,0 +1,17 @@
+"""MI355X-native DFlash block-diffusion drafter forward.
+
+The computation lives in ``libdflash.so`` (HIP kernels for gfx950 behind the C
+ABI of ``include/dflash.h``); this package only marshals arguments.  Importing
+it does not load the library; the first ``Drafter`` does, and fails loudly if
+the library was not built.
+"""
+from .abi import ContextGap, DFlashError  # noqa: F401
+
+__all__ = ["Drafter", "Session", "propose_batch", "sample", "ContextGap", "DFlashError"]
+
+
+def __getattr__(name):
+    if name in ("Drafter", "Session", "propose_batch", "sample"):
+        from . import drafter
+        return getattr(drafter, name)
+    raise AttributeError(name)

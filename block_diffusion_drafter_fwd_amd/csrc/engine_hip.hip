@@ -1,0 +1,607 @@
+// HIP backend of the drafter: plans and enqueues the kernels of the context
+// pass (taps -> [aux norms] -> fc -> hidden_norm -> [per-layer input norm]
+// -> all layers' K/V in one GEMM -> k-norm + RoPE + slot write), the block
+// pass (embed -> per layer: norm, QKV(+g) GEMM, q/k norm + RoPE + block K/V
+// write, attention, o_proj, norm, gate|up GEMM, SwiGLU, down_proj -> final
+// norm of rows 1..n -> unembedding) and the sampler.  All device memory is
+// the caller's: the per-call tables and every intermediate live in the
+// workspace whose layout is computed here.
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "engine.h"
+#include "kernels.h"
+
+namespace dflash {
+namespace {
+
+using namespace kern;
+
+size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+    size_t desc, rowinfo, rowsrc, srcptr;
+    size_t ctx_stage, ctx_fc, ctx_c, ctx_x, ctx_kv;
+    size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_mlp;
+    size_t attn_o, attn_ml, part, bitmap, stats;
+    size_t total;
+    int32_t r_ctx, r_blk, items_cap, nchunk_max;
+    size_t part_cap;
+};
+
+constexpr int kSampleChunk = 4096;
+constexpr int kAttnTargetWG = 2048;
+constexpr size_t kPartCapFloats = size_t(8) << 20;   // split-K partials: 32 MiB
+
+#define HIP_OK(expr)                                                                    \
+    do {                                                                                \
+        hipError_t e_ = (expr);                                                         \
+        if (e_ != hipSuccess) return fail(DFLASH_E_HIP, std::string(#expr) + ": " +     \
+                                                         hipGetErrorString(e_));        \
+    } while (0)
+
+class HipEngine : public Engine {
+public:
+    HipEngine(const Model& m, int num_cus) : m_(m), cus_(num_cus) {}
+
+    WsLayout layout(int32_t ms) const {
+        const dflash_config& c = m_.cfg;
+        WsLayout w{};
+        const size_t act = m_.elem;
+        w.r_blk = ms * c.block_size;
+        w.r_ctx = std::max(c.flush_rows, w.r_blk);
+        const int32_t rmax = std::max(w.r_ctx, w.r_blk);
+        const int32_t L = c.layers, H = c.hidden, I = c.intermediate;
+        w.items_cap = std::max(1, kAttnTargetWG / c.kv_heads) + ms;
+        w.nchunk_max = (c.vocab + kSampleChunk - 1) / kSampleChunk;
+        w.part_cap = kPartCapFloats;
+        size_t o = 0;
+        auto put = [&](size_t bytes) { size_t at = o; o += al(bytes); return at; };
+        w.desc = put(sizeof(SeqDesc) * (size_t)ms);
+        w.rowinfo = put(sizeof(RowInfo) * (size_t)rmax);
+        w.rowsrc = put(sizeof(int32_t) * (size_t)w.r_blk);
+        w.srcptr = put(sizeof(uint64_t) * (size_t)w.r_ctx);
+        w.ctx_stage = put(act * (size_t)w.r_ctx * m_.fc_in);
+        w.ctx_fc = put(4 * (size_t)w.r_ctx * H);
+        w.ctx_c = put(4 * (size_t)w.r_ctx * H);
+        w.ctx_x = put(act * (size_t)(c.ctx_input_norm ? L : 1) * w.r_ctx * H);
+        w.ctx_kv = put(4 * (size_t)w.r_ctx * L * 2 * m_.kd);
+        w.blk_h = put(4 * (size_t)w.r_blk * H);
+        w.blk_x = put(act * (size_t)w.r_blk * std::max(std::max(H, I), m_.qd));
+        w.blk_qkv = put(4 * (size_t)w.r_blk * qkv_ld());
+        w.blk_q = put(act * (size_t)w.r_blk * m_.qd);
+        w.blk_attn = put(act * (size_t)w.r_blk * m_.qd);
+        w.blk_mlp = put(4 * (size_t)w.r_blk * 2 * I);
+        const bool bf16 = c.dtype == DFLASH_BF16;
+        w.attn_o = put(bf16 ? 4 * (size_t)w.items_cap * c.kv_heads * 64 * c.head_dim : 0);
+        w.attn_ml = put(bf16 ? 4 * (size_t)w.items_cap * c.kv_heads * 64 * 2 : 0);
+        w.part = put(bf16 ? 4 * w.part_cap : 0);
+        w.bitmap = put(4 * (size_t)ms * ((c.vocab + 31) / 32));
+        w.stats = put(16 * (size_t)w.r_blk * w.nchunk_max);
+        w.total = o;
+        return w;
+    }
+
+    int32_t qkv_ld() const { return m_.qd + 2 * m_.kd + (m_.cfg.gate ? m_.cfg.q_heads : 0); }
+
+    size_t workspace_bytes(int32_t ms) const override { return layout(ms).total; }
+
+    int copy_rows(void* dst, const void* src, size_t bytes, void* stream) override {
+        if (!bytes) return 0;
+        HIP_OK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+        return 0;
+    }
+
+    int write_history(const SessView& s, int32_t slot0, const int32_t* tokens, int32_t count,
+                      void* stream) override {
+        HIP_OK(upload(s.hist + slot0, tokens, sizeof(int32_t) * (size_t)count, (hipStream_t)stream));
+        return 0;
+    }
+
+    int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs, void* ws,
+                    int32_t ws_sessions, void* stream) override;
+    int block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs, float* logits,
+                      float* hidden, void* ws, int32_t ws_sessions, void* stream) override;
+    int sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
+               const dflash_sample_params& p, int32_t* ids, float* probs, void* ws, int32_t ws_sessions,
+               void* stream) override;
+
+    int cache_read(const SessView& s, int32_t layer, int32_t pos0, int32_t count, float* k_out, float* v_out,
+                   void* stream) override {
+        const dflash_config& c = m_.cfg;
+        HIP_OK(kern::cache_read(s.cache, s.cap, s.ring, c.kv_heads, c.head_dim, layer, pos0, count,
+                                c.dtype == DFLASH_BF16, k_out, v_out, (hipStream_t)stream));
+        return 0;
+    }
+
+    int profile_begin(const std::string& stage) override {
+        stage_ = stage;
+        ev_used_ = 0;
+        return 0;
+    }
+
+    int profile_end(double* total_ms, int32_t* launches) override {
+        *total_ms = 0.0;
+        *launches = (int32_t)(ev_used_ / 2);
+        stage_.clear();
+        if (ev_used_ >= 2) HIP_OK(hipEventSynchronize(ev_[ev_used_ - 1]));
+        for (size_t i = 0; i + 1 < ev_used_; i += 2) {
+            float ms = 0.f;
+            HIP_OK(hipEventElapsedTime(&ms, ev_[i], ev_[i + 1]));
+            *total_ms += ms;
+        }
+        ev_used_ = 0;
+        return 0;
+    }
+
+    ~HipEngine() override {
+        for (hipEvent_t e : ev_) (void)hipEventDestroy(e);
+    }
+
+private:
+    // Brackets the launches of one stage with events while that stage is profiled.
+    struct Timed {
+        HipEngine* e;
+        hipStream_t st;
+        bool on;
+        Timed(HipEngine* eng, const char* stage, hipStream_t s) : e(eng), st(s), on(eng->stage_ == stage) {
+            if (on) e->record(st);
+        }
+        ~Timed() {
+            if (on) e->record(st);
+        }
+    };
+    void record(hipStream_t st) {
+        if (ev_used_ == ev_.size()) {
+            hipEvent_t ev;
+            if (hipEventCreate(&ev) != hipSuccess) return;
+            ev_.push_back(ev);
+        }
+        (void)hipEventRecord(ev_[ev_used_++], st);
+    }
+
+    bool bf16() const { return m_.cfg.dtype == DFLASH_BF16; }
+
+    NormArgs norm_args(const void* in, int in_bf16, int64_t in_stride, int rows, int width) const {
+        NormArgs n{};
+        n.in = in;
+        n.in_bf16 = in_bf16;
+        n.in_stride = in_stride;
+        n.rows = rows;
+        n.width = width;
+        n.groups = 1;
+        n.eps = m_.cfg.rms_eps;
+        n.gain_bf16 = bf16();
+        n.out_bf16 = bf16();
+        n.out_stride = width;
+        return n;
+    }
+
+    SeqDesc desc_of(const SessView& s) const {
+        SeqDesc d{};
+        d.cache = s.cache;
+        d.hist = s.hist;
+        d.seed = s.seed;
+        d.stream = s.stream_id;
+        d.cap = s.cap;
+        d.ring = s.ring;
+        return d;
+    }
+
+    Model m_;
+    int cus_;
+    std::string stage_;
+    std::vector<hipEvent_t> ev_;
+    size_t ev_used_ = 0;
+};
+
+int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs, void* ws,
+                           int32_t ws_sessions, void* stream) {
+    const dflash_config& c = m_.cfg;
+    const WsLayout w = layout(ws_sessions);
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const int32_t H = c.hidden, L = c.layers, kd = m_.kd;
+    const size_t rb = (size_t)m_.fc_in * m_.elem;
+    size_t si = 0;
+    while (si < segs.size()) {
+        // a group of whole segments with at most r_ctx rows
+        size_t sj = si;
+        int32_t rows = 0;
+        while (sj < segs.size() && rows + segs[sj].nrows <= w.r_ctx) rows += segs[sj++].nrows;
+        if (sj == si) return fail(DFLASH_E_CAPACITY, "context segment larger than the workspace");
+        std::vector<SeqDesc> descs;
+        std::vector<RowInfo> info;
+        std::vector<uint64_t> srcs;
+        std::vector<int32_t> map(sess.size(), -1);
+        for (size_t k = si; k < sj; ++k) {
+            const CtxSeg& g = segs[k];
+            if (map[g.sess] < 0) {
+                map[g.sess] = (int32_t)descs.size();
+                descs.push_back(desc_of(sess[g.sess]));
+            }
+            for (int32_t r = 0; r < g.nrows; ++r) {
+                info.push_back({map[g.sess], g.pos0 + r});
+                srcs.push_back((uint64_t)((const char*)g.rows + (size_t)r * rb));
+            }
+        }
+        HIP_OK(upload(base + w.desc, descs.data(), sizeof(SeqDesc) * descs.size(), st));
+        HIP_OK(upload(base + w.rowinfo, info.data(), sizeof(RowInfo) * info.size(), st));
+        const SeqDesc* d_desc = (const SeqDesc*)(base + w.desc);
+        const RowInfo* d_info = (const RowInfo*)(base + w.rowinfo);
+
+        // A operand of fc: the segment rows themselves, or gathered / aux-normed
+        const void* A = segs[si].rows;
+        if (sj - si > 1) {
+            HIP_OK(upload(base + w.srcptr, srcs.data(), sizeof(uint64_t) * srcs.size(), st));
+            HIP_OK(gather_rows(base + w.ctx_stage, (const uint64_t*)(base + w.srcptr), rows, rb, st));
+            A = base + w.ctx_stage;
+        }
+        if (c.aux_norms) {
+            NormArgs n = norm_args(A, bf16(), m_.fc_in, rows, m_.fc_in);
+            n.groups = c.taps;
+            n.gain_group_stride = c.target_hidden;
+            n.nout = 1;
+            n.gain[0] = m_.aux_norms;
+            n.out[0] = base + w.ctx_stage;
+            n.out_stride = m_.fc_in;
+            HIP_OK(rmsnorm(n, st));
+            A = base + w.ctx_stage;
+        }
+        {
+            GemmArgs g{};
+            g.M = rows;
+            g.K = m_.fc_in;
+            g.C = (float*)(base + w.ctx_fc);
+            g.ldc = H;
+            g.part = (float*)(base + w.part);
+            g.nseg = 1;
+            g.seg[0] = GemmSeg{A, m_.fc, m_.fc_in, m_.fc_in, H, 0, 0, 0};
+            Timed tm(this, "flush_fc", st);
+            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+        }
+        // hidden_norm, then (Laguna) every layer's input_layernorm
+        char* xs = base + w.ctx_x;
+        const size_t xstride = m_.elem * (size_t)w.r_ctx * H;
+        if (c.ctx_input_norm) {
+            NormArgs n = norm_args(base + w.ctx_fc, 0, H, rows, H);
+            n.nout = 1;
+            n.gain[0] = m_.hidden_norm;
+            n.out[0] = base + w.ctx_c;
+            n.out_bf16 = 0;
+            HIP_OK(rmsnorm(n, st));
+            for (int32_t l0 = 0; l0 < L; l0 += kMaxOut) {
+                NormArgs n2 = norm_args(base + w.ctx_c, 0, H, rows, H);
+                n2.nout = std::min(kMaxOut, L - l0);
+                for (int32_t j = 0; j < n2.nout; ++j) {
+                    n2.gain[j] = m_.layer[l0 + j].in_ln;
+                    n2.out[j] = xs + (size_t)(l0 + j) * xstride;
+                }
+                HIP_OK(rmsnorm(n2, st));
+            }
+        } else {
+            NormArgs n = norm_args(base + w.ctx_fc, 0, H, rows, H);
+            n.nout = 1;
+            n.gain[0] = m_.hidden_norm;
+            n.out[0] = xs;
+            HIP_OK(rmsnorm(n, st));
+        }
+        // every layer's K|V in one GEMM (up to 16 layers per launch)
+        const int32_t ldkv = L * 2 * kd;
+        for (int32_t l0 = 0; l0 < L; l0 += kMaxSeg / 2) {
+            const int32_t nl = std::min<int32_t>(kMaxSeg / 2, L - l0);
+            GemmArgs g{};
+            g.M = rows;
+            g.K = H;
+            g.C = (float*)(base + w.ctx_kv);
+            g.ldc = ldkv;
+            g.part = (float*)(base + w.part);
+            g.nseg = 2 * nl;
+            for (int32_t j = 0; j < nl; ++j) {
+                const int32_t l = l0 + j;
+                const void* x = xs + (c.ctx_input_norm ? (size_t)l * xstride : 0);
+                g.seg[2 * j] = GemmSeg{x, m_.layer[l].k, H, H, kd, l * 2 * kd, 0, 0};
+                g.seg[2 * j + 1] = GemmSeg{x, m_.layer[l].v, H, H, kd, l * 2 * kd + kd, 0, 0};
+            }
+            Timed tm(this, "flush_kv", st);
+            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+        }
+        for (int32_t l0 = 0; l0 < L; l0 += kMaxL) {
+            HeadArgs h{};
+            h.src = (const float*)(base + w.ctx_kv);
+            h.rows = d_info;
+            h.seqs = d_desc;
+            h.ld = ldkv;
+            h.nrows = rows;
+            h.D = c.head_dim;
+            h.Hq = c.q_heads;
+            h.Hkv = c.kv_heads;
+            h.L = L;
+            h.q_col = -1;
+            const int nl = std::min(kMaxL, L - l0);
+            for (int j = 0; j < nl; ++j) {
+                h.k_col[j] = (l0 + j) * 2 * kd;
+                h.v_col[j] = (l0 + j) * 2 * kd + kd;
+                h.layer[j] = l0 + j;
+                h.k_norm[j] = m_.layer[l0 + j].k_norm;
+            }
+            h.qk_norm = c.qk_norm;
+            h.w_bf16 = bf16();
+            h.cache_bf16 = bf16();
+            h.eps = c.rms_eps;
+            h.theta = c.rope_theta;
+            HIP_OK(head_finish(h, nl, st));
+        }
+        si = sj;
+    }
+    return 0;
+}
+
+int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs, float* logits,
+                             float* hidden, void* ws, int32_t ws_sessions, void* stream) {
+    const dflash_config& c = m_.cfg;
+    const WsLayout w = layout(ws_sessions);
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const int32_t H = c.hidden, I = c.intermediate, qd = m_.qd, kd = m_.kd;
+    const int32_t G = c.q_heads / c.kv_heads;
+
+    // tables: one SeqDesc per block, one RowInfo per block row, the input row
+    // of every unembedded row, and the attention work split
+    std::vector<SeqDesc> descs;
+    std::vector<RowInfo> info;
+    std::vector<int32_t> rowsrc;
+    int32_t R = 0, Rout = 0;
+    int64_t total_keys = 0;
+    for (const BlockSeq& b : seqs) {
+        SeqDesc d = desc_of(sess[b.sess]);
+        d.F = b.F;
+        d.M = b.M;
+        d.q_row0 = R;
+        d.out_row0 = Rout;
+        d.key_lo = c.window ? std::max(0, b.F - c.window + 1) : 0;
+        d.current = b.current;
+        total_keys += b.F + b.M - d.key_lo;
+        for (int32_t i = 0; i < b.M; ++i) info.push_back({(int32_t)descs.size(), b.F + i});
+        for (int32_t i = 1; i < b.M; ++i) rowsrc.push_back(R + i);
+        R += b.M;
+        Rout += b.M - 1;
+        descs.push_back(d);
+    }
+    if (R > w.r_blk) return fail(DFLASH_E_CAPACITY, "block rows exceed the workspace");
+    const int32_t target_items = std::max(1, kAttnTargetWG / c.kv_heads);
+    int32_t chunk = (int32_t)((total_keys + target_items - 1) / target_items);
+    chunk = std::max(64, (chunk + 63) / 64 * 64);
+    int32_t items = 0;
+    for (SeqDesc& d : descs) {
+        const int32_t nk = d.F + d.M - d.key_lo;
+        d.item0 = items;
+        d.nitems = (nk + chunk - 1) / chunk;
+        items += d.nitems;
+    }
+    if (bf16() && items > w.items_cap) return fail(DFLASH_E_CAPACITY, "attention work exceeds the workspace");
+    HIP_OK(upload(base + w.desc, descs.data(), sizeof(SeqDesc) * descs.size(), st));
+    HIP_OK(upload(base + w.rowinfo, info.data(), sizeof(RowInfo) * info.size(), st));
+    HIP_OK(upload(base + w.rowsrc, rowsrc.data(), sizeof(int32_t) * rowsrc.size(), st));
+    const SeqDesc* d_desc = (const SeqDesc*)(base + w.desc);
+    const RowInfo* d_info = (const RowInfo*)(base + w.rowinfo);
+
+    float* h = (float*)(base + w.blk_h);
+    void* x = base + w.blk_x;
+    float* qkv = (float*)(base + w.blk_qkv);
+    const int32_t ldq = qkv_ld();
+    {
+        EmbedArgs e{m_.embed, h, d_info, d_desc, H, R, c.mask_id, bf16()};
+        HIP_OK(embed(e, st));
+    }
+    for (int32_t l = 0; l < c.layers; ++l) {
+        const LayerW& lw = m_.layer[l];
+        {
+            NormArgs n = norm_args(h, 0, H, R, H);
+            n.nout = 1;
+            n.gain[0] = lw.in_ln;
+            n.out[0] = x;
+            HIP_OK(rmsnorm(n, st));
+        }
+        {
+            GemmArgs g{};
+            g.M = R;
+            g.K = H;
+            g.C = qkv;
+            g.ldc = ldq;
+            g.part = (float*)(base + w.part);
+            g.seg[0] = GemmSeg{x, lw.q, H, H, qd, 0, 0, 0};
+            g.seg[1] = GemmSeg{x, lw.k, H, H, kd, qd, 0, 0};
+            g.seg[2] = GemmSeg{x, lw.v, H, H, kd, qd + kd, 0, 0};
+            g.nseg = 3;
+            if (c.gate) g.seg[g.nseg++] = GemmSeg{x, lw.g, H, H, c.q_heads, qd + 2 * kd, 0, 0};
+            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+        }
+        {
+            HeadArgs hd{};
+            hd.src = qkv;
+            hd.rows = d_info;
+            hd.seqs = d_desc;
+            hd.q_out = base + w.blk_q;
+            hd.q_norm = lw.q_norm;
+            hd.k_norm[0] = lw.k_norm;
+            hd.ld = ldq;
+            hd.nrows = R;
+            hd.D = c.head_dim;
+            hd.Hq = c.q_heads;
+            hd.Hkv = c.kv_heads;
+            hd.L = c.layers;
+            hd.q_col = 0;
+            hd.k_col[0] = qd;
+            hd.v_col[0] = qd + kd;
+            hd.layer[0] = l;
+            hd.qk_norm = c.qk_norm;
+            hd.w_bf16 = bf16();
+            hd.cache_bf16 = bf16();
+            hd.q_bf16 = bf16();
+            hd.eps = c.rms_eps;
+            hd.theta = c.rope_theta;
+            HIP_OK(head_finish(hd, 1, st));
+        }
+        {
+            AttnArgs a{};
+            a.Q = base + w.blk_q;
+            a.seqs = d_desc;
+            a.rows = d_info;
+            a.part_o = (float*)(base + w.attn_o);
+            a.part_ml = (float*)(base + w.attn_ml);
+            a.gate_src = qkv;
+            a.out = base + w.blk_attn;
+            a.nseq = (int32_t)descs.size();
+            a.nrows = R;
+            a.layer = l;
+            a.L = c.layers;
+            a.Hq = c.q_heads;
+            a.Hkv = c.kv_heads;
+            a.D = c.head_dim;
+            a.causal = c.causal;
+            a.window = c.window;
+            a.chunk = chunk;
+            a.total_items = items;
+            a.gate = c.gate;
+            a.gate_ld = ldq;
+            a.gate_col = qd + 2 * kd;
+            a.out_bf16 = bf16();
+            a.scale = 1.f / sqrtf((float)c.head_dim);
+            (void)G;
+            Timed tm(this, "attention", st);
+            HIP_OK(attention(a, bf16(), st));
+        }
+        {
+            GemmArgs g{};
+            g.M = R;
+            g.K = qd;
+            g.C = h;
+            g.ldc = H;
+            g.accumulate = 1;
+            g.part = (float*)(base + w.part);
+            g.seg[0] = GemmSeg{base + w.blk_attn, lw.o, qd, qd, H, 0, 0, 0};
+            g.nseg = 1;
+            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+        }
+        {
+            NormArgs n = norm_args(h, 0, H, R, H);
+            n.nout = 1;
+            n.gain[0] = lw.post_ln;
+            n.out[0] = x;
+            HIP_OK(rmsnorm(n, st));
+        }
+        {
+            GemmArgs g{};
+            g.M = R;
+            g.K = H;
+            g.C = (float*)(base + w.blk_mlp);
+            g.ldc = 2 * I;
+            g.part = (float*)(base + w.part);
+            g.seg[0] = GemmSeg{x, lw.gate, H, H, I, 0, 0, 0};
+            g.seg[1] = GemmSeg{x, lw.up, H, H, I, I, 0, 0};
+            g.nseg = 2;
+            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+        }
+        HIP_OK(silu_mul((const float*)(base + w.blk_mlp), 2 * I, I, x, bf16(), R, st));
+        {
+            GemmArgs g{};
+            g.M = R;
+            g.K = I;
+            g.C = h;
+            g.ldc = H;
+            g.accumulate = 1;
+            g.part = (float*)(base + w.part);
+            g.seg[0] = GemmSeg{x, lw.down, I, I, H, 0, 0, 0};
+            g.nseg = 1;
+            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+        }
+    }
+    if (hidden) HIP_OK(hipMemcpyAsync(hidden, h, sizeof(float) * (size_t)R * H, hipMemcpyDeviceToDevice, st));
+    if (Rout > 0) {
+        NormArgs n = norm_args(h, 0, H, Rout, H);
+        n.row_src = (const int32_t*)(base + w.rowsrc);
+        n.nout = 1;
+        n.gain[0] = m_.norm;
+        n.out[0] = x;
+        HIP_OK(rmsnorm(n, st));
+        GemmArgs g{};
+        g.M = Rout;
+        g.K = H;
+        g.C = logits;
+        g.ldc = c.vocab;
+        g.part = (float*)(base + w.part);
+        g.seg[0] = GemmSeg{x, m_.lm_head, H, H, c.vocab, 0, 0, 0};
+        g.nseg = 1;
+        Timed tm(this, "unembed", st);
+        HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st, 1));
+    }
+    return 0;
+}
+
+int HipEngine::sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
+                      const dflash_sample_params& p, int32_t* ids, float* probs, void* ws, int32_t ws_sessions,
+                      void* stream) {
+    const dflash_config& c = m_.cfg;
+    const WsLayout w = layout(ws_sessions);
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const int32_t count = (int32_t)sess.size();
+    const int32_t R = row_offsets[count];
+    if (R > w.r_blk) return fail(DFLASH_E_CAPACITY, "sampled rows exceed the workspace");
+    std::vector<SeqDesc> descs(count);
+    std::vector<RowInfo> info;
+    bool any_hist = false;
+    for (int32_t k = 0; k < count; ++k) {
+        descs[k] = desc_of(sess[k]);
+        descs[k].hist_n = std::min(std::min(sess[k].hist_count, kHistory), p.history);
+        descs[k].hist_head = sess[k].hist_head;
+        any_hist |= descs[k].hist_n > 0;
+        for (int32_t r = row_offsets[k]; r < row_offsets[k + 1]; ++r) info.push_back({k, r - row_offsets[k]});
+    }
+    HIP_OK(upload(base + w.desc, descs.data(), sizeof(SeqDesc) * descs.size(), st));
+    HIP_OK(upload(base + w.rowinfo, info.data(), sizeof(RowInfo) * info.size(), st));
+    SampleArgs a{};
+    a.logits = logits;
+    a.seqs = (const SeqDesc*)(base + w.desc);
+    a.rows = (const RowInfo*)(base + w.rowinfo);
+    a.bitmap = (uint32_t*)(base + w.bitmap);
+    a.stats = (float*)(base + w.stats);
+    a.ids = ids;
+    a.probs = probs;
+    a.V = c.vocab;
+    a.R = R;
+    a.nseq = count;
+    a.words = (c.vocab + 31) / 32;
+    a.chunk = kSampleChunk;
+    a.nchunk = w.nchunk_max;
+    a.round = p.round;
+    a.use_penalty = (p.rep_penalty != 1.f && any_hist) ? 1 : 0;
+    a.temperature = p.temperature;
+    a.rho = p.rep_penalty;
+    Timed tm(this, "sampler", st);
+    HIP_OK(kern::sample(a, st));
+    return 0;
+}
+
+}  // namespace
+
+Engine* make_engine(const Model& m, std::string* err) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *err = std::string("hipGetDevice: ") + hipGetErrorString(e);
+        return nullptr;
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) {
+        *err = std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e);
+        return nullptr;
+    }
+    return new HipEngine(m, cus);
+}
+
+}  // namespace dflash

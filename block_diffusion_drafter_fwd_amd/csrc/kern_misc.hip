@@ -1,0 +1,432 @@
+// Row-wise kernels of the drafter forward: RMSNorm, the per-head q/k norm +
+// RoPE + slot-indexed K/V cache writer, embedding gather, SwiGLU, descriptor
+// upload, row gather, cache readback, and the batched sampler.
+#include <cmath>
+
+#include "kernels.h"
+
+namespace dflash {
+namespace kern {
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float x) {   // round to nearest, ties to even
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float ld_any(const void* p, size_t i, int bf16) {
+    return bf16 ? bf2f(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+__device__ __forceinline__ void st_any(void* p, size_t i, float v, int bf16) {
+    if (bf16) ((uint16_t*)p)[i] = f2bf(v);
+    else ((float*)p)[i] = v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) sh[w] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += sh[i];
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * gain, per row and per group of
+// width/groups columns; one input, up to kMaxOut (gain, output) pairs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
+    __shared__ float sh[8];
+    const int orow = blockIdx.x, grp = blockIdx.y;
+    const int irow = a.row_src ? a.row_src[orow] : orow;
+    const int W = a.width / a.groups;
+    const size_t ibase = (size_t)irow * a.in_stride + (size_t)grp * W;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < W; i += 256) {
+        const float x = ld_any(a.in, ibase + i, a.in_bf16);
+        ss += x * x;
+    }
+    ss = block_sum(ss, sh);
+    const float rstd = 1.f / sqrtf(ss / (float)W + a.eps);
+    const size_t obase = (size_t)orow * a.out_stride + (size_t)grp * W;
+    const size_t gbase = (size_t)grp * a.gain_group_stride;
+    for (int o = 0; o < a.nout; ++o)
+        for (int i = threadIdx.x; i < W; i += 256) {
+            const float x = ld_any(a.in, ibase + i, a.in_bf16);
+            const float gn = ld_any(a.gain[o], gbase + i, a.gain_bf16);
+            st_any(a.out[o], obase + i, x * rstd * gn, a.out_bf16);
+        }
+}
+
+hipError_t rmsnorm(const NormArgs& a, hipStream_t st) {
+    if (a.rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rmsnorm, dim3(a.rows, a.groups), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-head finish of a projection row: q and k get RMSNorm over the head and
+// rotate-half RoPE at the row's position (angles in fp64, then fp32); q goes
+// to the query buffer, k and v to the session's cache at the row's slot.
+// One workgroup per (row, layer); wave w takes heads w, w+4, ...
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
+    const int row = blockIdx.x, li = blockIdx.y;
+    const RowInfo ri = a.rows[row];
+    const SeqDesc sd = a.seqs[ri.seq];
+    const int pos = ri.pos;
+    const int slot = sd.ring ? pos % sd.cap : pos;
+    const int half = a.D >> 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool act = lane < half;
+    float cs = 1.f, sn = 0.f;
+    if (act) {
+        const double inv = pow((double)a.theta, -2.0 * (double)lane / (double)a.D);
+        const double ang = (double)pos * inv;
+        cs = (float)cos(ang);
+        sn = (float)sin(ang);
+    }
+    const int layer = a.layer[li];
+    const int nq = (a.q_col >= 0) ? a.Hq : 0;
+    const int ntask = nq + 2 * a.Hkv;
+    const float* src = a.src + (size_t)row * a.ld;
+    for (int task = wave; task < ntask; task += 4) {
+        int kind, head, col;   // kind 0 q, 1 k, 2 v
+        if (task < nq) { kind = 0; head = task; col = a.q_col + head * a.D; }
+        else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * a.D; }
+        else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * a.D; }
+        float x1 = act ? src[col + lane] : 0.f;
+        float x2 = act ? src[col + lane + half] : 0.f;
+        if (kind != 2) {
+            if (a.qk_norm) {
+                const float ss = wave_sum(x1 * x1 + x2 * x2);
+                const float rstd = 1.f / sqrtf(ss / (float)a.D + a.eps);
+                const void* gn = kind == 0 ? a.q_norm : a.k_norm[li];
+                if (act) {
+                    x1 = x1 * rstd * ld_any(gn, lane, a.w_bf16);
+                    x2 = x2 * rstd * ld_any(gn, lane + half, a.w_bf16);
+                }
+            }
+            const float y1 = x1 * cs - x2 * sn;
+            const float y2 = x2 * cs + x1 * sn;
+            x1 = y1;
+            x2 = y2;
+        }
+        if (!act) continue;
+        if (kind == 0) {
+            const size_t o = ((size_t)row * a.Hq + head) * a.D;
+            st_any(a.q_out, o + lane, x1, a.q_bf16);
+            st_any(a.q_out, o + lane + half, x2, a.q_bf16);
+        } else {
+            const size_t o = ((((size_t)layer * 2 + (kind - 1)) * a.Hkv + head) * sd.cap + slot) * a.D;
+            st_any(sd.cache, o + lane, x1, a.cache_bf16);
+            st_any(sd.cache, o + lane + half, x2, a.cache_bf16);
+        }
+    }
+}
+
+hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st) {
+    if (a.nrows <= 0 || nlayer <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_head_finish, dim3(a.nrows, nlayer), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block embedding: row i of a sequence's block is the anchor (i = 0) or the
+// mask token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
+    const int row = blockIdx.x;
+    const RowInfo ri = a.rows[row];
+    const SeqDesc sd = a.seqs[ri.seq];
+    const int tok = ri.pos == sd.F ? sd.current : a.mask_id;
+    const size_t src = (size_t)tok * a.H;
+    for (int j = threadIdx.x; j < a.H; j += 256) a.h[(size_t)row * a.H + j] = ld_any(a.table, src + j, a.w_bf16);
+}
+
+hipError_t embed(const EmbedArgs& a, hipStream_t st) {
+    if (a.nrows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_embed, dim3(a.nrows), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU: out = silu(gate) * up, gate and up side by side in one row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_silu_mul(const float* in, int32_t ld, int32_t I, void* out,
+                                                  int32_t out_bf16, int32_t rows) {
+    const size_t total = (size_t)rows * I;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const int r = (int)(i / I), j = (int)(i % I);
+        const float gt = in[(size_t)r * ld + j];
+        const float up = in[(size_t)r * ld + I + j];
+        st_any(out, i, gt / (1.f + expf(-gt)) * up, out_bf16);
+    }
+}
+
+hipError_t silu_mul(const float* in, int32_t ld, int32_t I, void* out, int32_t out_bf16, int32_t rows,
+                    hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    const size_t total = (size_t)rows * I;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 2048);
+    hipLaunchKernelGGL(k_silu_mul, dim3(blocks), dim3(256), 0, st, in, ld, I, out, out_bf16, rows);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Descriptor upload (payload travels in the kernel arguments), row gather,
+// cache readback.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_upload(UploadArgs a) {
+    for (int i = threadIdx.x; i < a.nwords; i += 256) a.dst[i] = a.data[i];
+}
+
+hipError_t upload(void* dst, const void* host, size_t bytes, hipStream_t st) {
+    const uint32_t* src = (const uint32_t*)host;
+    size_t words = (bytes + 3) / 4;
+    UploadArgs a;
+    for (size_t off = 0; off < words; off += kUploadWords) {
+        const int n = (int)std::min<size_t>(kUploadWords, words - off);
+        a.dst = (uint32_t*)dst + off;
+        a.nwords = n;
+        a.pad = 0;
+        for (int i = 0; i < n; ++i) a.data[i] = src[off + i];
+        hipLaunchKernelGGL(k_upload, dim3(1), dim3(256), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+__global__ __launch_bounds__(256) void k_gather_rows(uint4* dst, const uint64_t* src, size_t row_words) {
+    const int row = blockIdx.x;
+    const uint4* s = (const uint4*)src[row];
+    for (size_t i = threadIdx.x; i < row_words; i += 256) dst[(size_t)row * row_words + i] = s[i];
+}
+
+hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gather_rows, dim3(rows), dim3(256), 0, st, (uint4*)dst, src_ptrs, row_bytes / 16);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_cache_read(const void* cache, int32_t cap, int32_t ring, int32_t Hkv,
+                                                    int32_t D, int32_t layer, int32_t pos0, int32_t count,
+                                                    int32_t bf16, float* k_out, float* v_out) {
+    const size_t per = (size_t)Hkv * D;
+    const size_t total = (size_t)count * per;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const int c = (int)(i / per);
+        const int h = (int)((i % per) / D), d = (int)(i % D);
+        const int pos = pos0 + c;
+        const int slot = ring ? pos % cap : pos;
+        const size_t kk = ((((size_t)layer * 2 + 0) * Hkv + h) * cap + slot) * D + d;
+        const size_t vv = ((((size_t)layer * 2 + 1) * Hkv + h) * cap + slot) * D + d;
+        k_out[i] = ld_any(cache, kk, bf16);
+        v_out[i] = ld_any(cache, vv, bf16);
+    }
+}
+
+hipError_t cache_read(const void* cache, int32_t cap, int32_t ring, int32_t Hkv, int32_t D, int32_t layer,
+                      int32_t pos0, int32_t count, int32_t bf16, float* k_out, float* v_out, hipStream_t st) {
+    const size_t total = (size_t)count * Hkv * D;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_cache_read, dim3(blocks), dim3(256), 0, st, cache, cap, ring, Hkv, D, layer, pos0,
+                       count, bf16, k_out, v_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sampler.  Penalties (CTRL repetition penalty over the distinct tokens of the
+// session's committed history) -> temperature -> softmax probabilities and a
+// Gumbel-max draw, u from Philox4x64-10 (Salmon et al., SC'11) at counter
+// (t div 4, row, round, 0) under key (seed, stream), word t mod 4, top 23 bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+        const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+        const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_hist_bitmap(SampleArgs a) {
+    const SeqDesc sd = a.seqs[blockIdx.x];
+    uint32_t* bm = a.bitmap + (size_t)blockIdx.x * a.words;
+    for (int i = threadIdx.x; i < a.words; i += 256) bm[i] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < sd.hist_n; j += 256) {
+        const int tok = sd.hist[(sd.hist_head - sd.hist_n + j + 2 * 512) % 512];
+        if (tok >= 0 && tok < a.V) atomicOr(&bm[tok >> 5], 1u << (tok & 31));
+    }
+}
+
+struct Stat {
+    float m, l, best;
+    int idx;
+};
+
+__device__ __forceinline__ void stat_merge(Stat& a, const Stat& b) {
+    if (b.m > a.m) {
+        a.l = a.l * (a.m == -INFINITY ? 0.f : __expf(a.m - b.m)) + b.l;
+        a.m = b.m;
+    } else if (b.m != -INFINITY) {
+        a.l += b.l * __expf(b.m - a.m);
+    }
+    if (b.best > a.best || (b.best == a.best && b.idx < a.idx)) {
+        a.best = b.best;
+        a.idx = b.idx;
+    }
+}
+
+__device__ __forceinline__ float penalized(const SampleArgs& a, const uint32_t* bm, int r, int t) {
+    float z = a.logits[(size_t)r * a.V + t];
+    if (a.use_penalty && ((bm[t >> 5] >> (t & 31)) & 1u)) z = z > 0.f ? z / a.rho : z * a.rho;
+    return z;
+}
+
+__device__ Stat block_stat(Stat s) {
+    __shared__ float sm[4], sl[4], sb[4];
+    __shared__ int si[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        Stat b{__shfl_xor(s.m, o), __shfl_xor(s.l, o), __shfl_xor(s.best, o), __shfl_xor(s.idx, o)};
+        stat_merge(s, b);
+    }
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) {
+        sm[w] = s.m;
+        sl[w] = s.l;
+        sb[w] = s.best;
+        si[w] = s.idx;
+    }
+    __syncthreads();
+    Stat t{sm[0], sl[0], sb[0], si[0]};
+    for (int i = 1; i < 4; ++i) stat_merge(t, Stat{sm[i], sl[i], sb[i], si[i]});
+    return t;
+}
+
+__global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
+    const int c = blockIdx.x, r = blockIdx.y;
+    const RowInfo ri = a.rows[r];
+    const SeqDesc sd = a.seqs[ri.seq];
+    const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
+    const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
+    Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    const bool greedy = a.temperature == 0.f;
+    for (int qd = (t_lo >> 2) + threadIdx.x; qd * 4 < t_hi; qd += 256) {
+        uint64_t w[4] = {0, 0, 0, 0};
+        if (!greedy) {
+            w[0] = (uint64_t)qd;
+            w[1] = (uint64_t)ri.pos;
+            w[2] = (uint64_t)a.round;
+            w[3] = 0;
+            philox4x64_10(w, sd.seed, sd.stream);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = qd * 4 + j;
+            if (t >= t_hi) break;
+            const float z = penalized(a, bm, r, t);
+            float key;
+            if (greedy) {
+                key = z;
+            } else {
+                const float sv = z / a.temperature;
+                if (sv > s.m) {
+                    s.l = s.l * (s.m == -INFINITY ? 0.f : __expf(s.m - sv)) + 1.f;
+                    s.m = sv;
+                } else {
+                    s.l += __expf(sv - s.m);
+                }
+                const float u = ((float)(w[j] >> 41) + 0.5f) * 0x1p-23f;
+                key = sv - logf(-logf(u));
+            }
+            if (key > s.best || (key == s.best && t < s.idx)) {
+                s.best = key;
+                s.idx = t;
+            }
+        }
+    }
+    s = block_stat(s);
+    if (threadIdx.x == 0) {
+        float* o = a.stats + ((size_t)r * a.nchunk + c) * 4;
+        o[0] = s.m;
+        o[1] = s.l;
+        o[2] = s.best;
+        o[3] = __int_as_float(s.idx);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
+    __shared__ float tot[4];
+    const int c = blockIdx.x, r = blockIdx.y;
+    if (threadIdx.x < 64) {
+        Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+        for (int j = threadIdx.x; j < a.nchunk; j += 64) {
+            const float* o = a.stats + ((size_t)r * a.nchunk + j) * 4;
+            stat_merge(s, Stat{o[0], o[1], o[2], __float_as_int(o[3])});
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            Stat b{__shfl_xor(s.m, o), __shfl_xor(s.l, o), __shfl_xor(s.best, o), __shfl_xor(s.idx, o)};
+            stat_merge(s, b);
+        }
+        if (threadIdx.x == 0) {
+            tot[0] = s.m;
+            tot[1] = s.l;
+            if (c == 0) a.ids[r] = s.idx;
+        }
+    }
+    if (!a.probs || a.temperature == 0.f) return;
+    __syncthreads();
+    const float M = tot[0], Z = tot[1];
+    const RowInfo ri = a.rows[r];
+    const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
+    const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
+    for (int t = t_lo + threadIdx.x; t < t_hi; t += 256) {
+        const float sv = penalized(a, bm, r, t) / a.temperature;
+        a.probs[(size_t)r * a.V + t] = __expf(sv - M) / Z;
+    }
+}
+
+hipError_t sample(const SampleArgs& a, hipStream_t st) {
+    if (a.R <= 0) return hipSuccess;
+    if (a.use_penalty) {
+        hipLaunchKernelGGL(k_hist_bitmap, dim3(a.nseq), dim3(256), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_sample_stats, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const bool probs = a.probs && a.temperature != 0.f;
+    hipLaunchKernelGGL(k_sample_final, dim3(probs ? a.nchunk : 1, a.R), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace kern
+}  // namespace dflash

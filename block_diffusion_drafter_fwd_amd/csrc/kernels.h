@@ -1,0 +1,141 @@
+// Argument blocks and launchers of the gfx950 kernels of the drafter forward.
+// Every kernel takes its arguments by value; per-call tables (sequence and row
+// descriptors) live in the caller's workspace and are written there by the
+// upload kernel, so no launch needs a host round trip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dflash {
+namespace kern {
+
+constexpr int kMaxSeg = 32;        // column segments of one GEMM launch
+constexpr int kMaxOut = 16;        // outputs of one norm launch
+constexpr int kMaxL = 16;          // layers of one head-finish launch
+constexpr int kUploadWords = 480;  // 1920-byte payload of one upload launch
+
+// One sequence (session) of a batched call.
+struct SeqDesc {
+    void* cache;          // arena base, [L][2][Hkv][cap][D] of the config dtype
+    int32_t* hist;        // committed-token ring (sampler)
+    uint64_t seed, stream;
+    int32_t cap, ring;    // slots; ring != 0: slot = position mod cap
+    int32_t F, M;         // block anchor position, block rows
+    int32_t q_row0;       // first block row of this sequence
+    int32_t out_row0;     // first logits row (block rows minus anchors before it)
+    int32_t key_lo;       // first key position visible to the block
+    int32_t item0, nitems;// attention work items
+    int32_t current;      // anchor token
+    int32_t hist_n, hist_head;
+};
+static_assert(sizeof(SeqDesc) == 80, "SeqDesc layout");
+
+struct RowInfo {
+    int32_t seq;          // index into the SeqDesc table
+    int32_t pos;          // absolute position (context/block) or row index (sampler)
+};
+
+// C[:, c_col0 : c_col0+N] (+)= A[M, K] . B[N, K]^T, one entry per segment.
+struct GemmSeg {
+    const void* A;
+    const void* B;
+    int32_t lda, ldb, N, c_col0, tile0, pad;
+};
+
+struct GemmArgs {
+    int32_t M, K, kc, splits;
+    float* C;
+    int32_t ldc, accumulate;
+    float* part;              // split-K partials [splits][M][ldc]
+    int32_t nseg, ntiles;
+    int32_t col_lo, col_hi;   // columns covered by the segments
+    GemmSeg seg[kMaxSeg];
+};
+
+struct NormArgs {
+    const void* in;
+    int64_t in_stride;        // elements between rows
+    const int32_t* row_src;   // optional: input row of each output row
+    int32_t in_bf16, rows, width, groups;
+    float eps;
+    int32_t gain_bf16, nout, out_bf16;
+    int64_t gain_group_stride;
+    int64_t out_stride;
+    const void* gain[kMaxOut];
+    void* out[kMaxOut];
+};
+
+struct HeadArgs {
+    const float* src;         // projection output rows
+    const RowInfo* rows;
+    const SeqDesc* seqs;
+    void* q_out;              // [rows][Hq][D]
+    const void* q_norm;
+    const void* k_norm[kMaxL];
+    int32_t ld, nrows, D, Hq, Hkv, L;
+    int32_t q_col;            // -1: no q heads in this launch
+    int32_t k_col[kMaxL], v_col[kMaxL], layer[kMaxL];
+    int32_t qk_norm, w_bf16, cache_bf16, q_bf16;
+    float eps, theta;
+};
+
+struct EmbedArgs {
+    const void* table;
+    float* h;
+    const RowInfo* rows;
+    const SeqDesc* seqs;
+    int32_t H, nrows, mask_id, w_bf16;
+};
+
+struct AttnArgs {
+    const void* Q;            // [rows][Hq][D]
+    const SeqDesc* seqs;
+    const RowInfo* rows;
+    float* part_o;            // [items][Hkv][64][D]
+    float* part_ml;           // [items][Hkv][64][2]
+    const float* gate_src;    // projection rows holding the g columns
+    void* out;                // [rows][Hq*D]
+    int32_t nseq, nrows, layer, L, Hq, Hkv, D, causal, window, chunk, total_items;
+    int32_t gate, gate_ld, gate_col, out_bf16;
+    float scale;
+};
+
+struct SampleArgs {
+    const float* logits;
+    const SeqDesc* seqs;
+    const RowInfo* rows;      // seq, row within the session's block
+    uint32_t* bitmap;         // [nseq][words]
+    float* stats;             // [R][nchunk][4]
+    int32_t* ids;
+    float* probs;
+    int32_t V, R, nseq, words, chunk, nchunk, round, use_penalty;
+    float temperature, rho;
+};
+
+struct UploadArgs {
+    uint32_t* dst;
+    int32_t nwords, pad;
+    uint32_t data[kUploadWords];
+};
+
+// launchers (return hipError_t of the launch)
+// tag 1 launches a separate instantiation (the unembedding) so that profilers
+// can tell it apart from the per-layer GEMMs
+hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag = 0);
+hipError_t rmsnorm(const NormArgs& a, hipStream_t st);
+hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st);
+hipError_t embed(const EmbedArgs& a, hipStream_t st);
+hipError_t silu_mul(const float* in, int32_t ld, int32_t I, void* out, int32_t out_bf16, int32_t rows,
+                    hipStream_t st);
+hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st);
+hipError_t sample(const SampleArgs& a, hipStream_t st);
+hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st);
+hipError_t upload(void* dst, const void* host, size_t bytes, hipStream_t st);
+hipError_t cache_read(const void* cache, int32_t cap, int32_t ring, int32_t Hkv, int32_t D, int32_t layer,
+                      int32_t pos0, int32_t count, int32_t bf16, float* k_out, float* v_out, hipStream_t st);
+
+}  // namespace kern
+}  // namespace dflash

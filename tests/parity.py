@@ -1,0 +1,219 @@
+"""Lock-step parity driver: the HIP library (through its C ABI) against the
+float64 oracle, on identical seeded inputs from ``synth``.
+
+Compared after every call: the session state (ctxOffset, pending, cache
+length, outstanding block, rows projected) bit-exactly; logits, the block
+hidden state, probabilities and cache K/V within the relative tolerance
+(max |gpu - ref| / max |ref|: 2e-2 bf16, 1e-4 fp32); token ids exactly
+wherever the oracle's top-1/top-2 score gap exceeds the tie margin (one bf16
+ulp of the top score for bf16, 1e-4 of it for fp32; divided by the
+temperature when sampling).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import synth
+from oracle.model import DraftModel
+from oracle.sampler import sample_row, top2_gap
+from oracle.session import ContextGap as OracleGap, OracleSession
+from tests.helpers import rel_err
+
+
+def tol(cfg) -> float:
+    return 2e-2 if cfg.dtype == "bf16" else 1e-4
+
+
+def probs_tol(z_gpu, z_ref, temperature: float) -> float:
+    """Bound on max|p_gpu - p_ref| / max p_ref implied by the logit deviation.
+
+    softmax(z/T) moves by at most a factor exp(2 max|dz| / T) when the logits
+    move by dz, so probabilities are held to that (plus float32 rounding of
+    the exponentials); the logit deviation itself is held to the logits
+    tolerance separately.
+    """
+    dz = float(np.max(np.abs(np.asarray(z_gpu, dtype=np.float64) - np.asarray(z_ref, dtype=np.float64))))
+    return math.expm1(2.0 * dz / temperature) + 1e-4
+
+
+def margin(cfg, top: float, temperature: float = 0.0) -> float:
+    top = abs(top)
+    if cfg.dtype == "bf16":
+        m = 2.0 ** (math.floor(math.log2(top)) - 7) if top > 0 else 0.0
+    else:
+        m = 1e-4 * top
+    return m / temperature if temperature > 0 else m
+
+
+def device_tensors(cfg, arrays: dict, device="cuda") -> dict:
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(device=device).to(dt) for k, v in arrays.items()}
+
+
+def feats_dev(cfg, f: np.ndarray, device="cuda") -> torch.Tensor:
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    return torch.from_numpy(np.ascontiguousarray(f)).to(device=device).to(dt)
+
+
+@dataclass
+class Report:
+    worst: dict = field(default_factory=dict)
+    ids_compared: int = 0
+    ids_skipped: int = 0
+    rounds: int = 0
+
+    def note(self, key, value):
+        self.worst[key] = max(self.worst.get(key, 0.0), value)
+
+
+class Pair:
+    """One GPU session and its two oracle twins (exact and bf16-emulating)."""
+
+    def __init__(self, drafter, cfg, weights_np, capacity, seed=0, sid=0, restored=0):
+        self.cfg = cfg
+        self.g = drafter.session(capacity, seed=seed, stream_id=sid, restored_offset=restored)
+        self.o = [OracleSession(DraftModel(cfg, weights_np, emulate_bf16=e), restored)
+                  for e in ((False, True) if cfg.dtype == "bf16" else (False,))]
+        self.seed, self.sid = seed, sid
+
+    def check_state(self, where=""):
+        gs = self.g.state()
+        for o in self.o:
+            assert tuple(gs) == tuple(o.state()), f"{where}: gpu {gs} oracle {o.state()}"
+        assert self.g.rows_written == self.o[0].rows_written, where
+
+    def committed(self, tokens, feats, position):
+        err = None
+        for o in self.o:
+            try:
+                o.committed(tokens, feats, position)
+            except OracleGap as e:
+                err = e
+        try:
+            self.g.committed(tokens, feats_dev(self.cfg, feats), position)
+            assert err is None, "oracle refused a run the library accepted"
+        except Exception as e:  # noqa: BLE001
+            if err is None:
+                raise
+            assert "gap" in str(e), e
+
+    def flush(self):
+        for o in self.o:
+            o.flush()
+        self.g.flush()
+
+    def commit_block(self):
+        for o in self.o:
+            o.commit_block()
+        self.g.commit_block()
+
+    def propose(self, current, max_tokens, rep: Report, hidden=True):
+        outs = [o.propose(current, max_tokens) for o in self.o]
+        n, logits, hid = self.g.propose(current, max_tokens, hidden=hidden)
+        if outs[0] is None:
+            assert n == 0
+            return None
+        assert n == outs[0]["n"]
+        z = logits.double().cpu().numpy()
+        for k, out in enumerate(outs):
+            e = rel_err(z, out["logits"])
+            rep.note(f"logits[{k}]", e)
+            assert e < tol(self.cfg), f"logits rel err {e} (oracle mode {k})"
+            if hid is not None:
+                e = rel_err(hid.double().cpu().numpy(), out["hidden"])
+                rep.note(f"hidden[{k}]", e)
+                assert e < tol(self.cfg), f"hidden rel err {e}"
+        return n, logits, outs[-1]
+
+    def check_cache(self, rep: Report, positions=None):
+        ctx_offset, _, cache_len, _ = self.g.state()
+        lo = 0
+        if self.cfg.window:
+            lo = max(0, ctx_offset - (self.cfg.window - 1))
+        if positions is None:
+            positions = np.arange(lo, cache_len)
+        positions = np.asarray(positions)
+        if positions.size == 0:
+            return
+        for l in range(self.cfg.layers):
+            p0, p1 = int(positions.min()), int(positions.max()) + 1
+            k, v = self.g.cache_read(l, p0, p1 - p0)
+            k = k.double().cpu().numpy()[positions - p0]
+            v = v.double().cpu().numpy()[positions - p0]
+            for j, o in enumerate(self.o):
+                K, V = o.cache_kv(l, positions)
+                ek, ev = rel_err(k, K), rel_err(v, V)
+                rep.note(f"cache[{j}]", max(ek, ev))
+                assert ek < tol(self.cfg) and ev < tol(self.cfg), (l, ek, ev)
+
+
+def check_ids(gpu_ids, ref_rows, rep: Report):
+    """ref_rows: (oracle id, oracle scores, tie margin) per row."""
+    for gid, (oid, scores, tau) in zip(gpu_ids, ref_rows):
+        if top2_gap(scores) > tau:
+            rep.ids_compared += 1
+            assert int(gid) == int(oid), f"id {gid} != oracle {oid} (gap {top2_gap(scores)}, margin {tau})"
+        else:
+            rep.ids_skipped += 1
+
+
+def run_session_script(drafter, cfg, wl: synth.Workload, weights_np, capacity, rounds=None, seed=0, sid=0,
+                       sample=True, check_cache_every=0) -> Report:
+    """The synthetic round driver (prompt in commit_rows pieces, then rounds
+    of propose -> sample -> accept -> rewind -> commit) on GPU and oracle."""
+    from block_diffusion_drafter_fwd_amd import sample as gpu_sample
+    rep = Report()
+    fs = synth.FeatureSource(cfg, seed, sid)
+    rs = synth.RoundScript(cfg, wl, seed, sid)
+    pr = Pair(drafter, cfg, weights_np, capacity, seed, sid)
+    ctx_len = wl.context
+    for p in range(0, ctx_len, wl.commit_rows):
+        T = min(wl.commit_rows, ctx_len - p)
+        pr.committed(fs.tokens(p, T), fs.features(p, T), p)
+        pr.check_state(f"prompt commit at {p}")
+    pr.check_cache(rep)
+    current = rs.first_anchor()
+    for r in range(wl.rounds if rounds is None else rounds):
+        if rs.flush_before:
+            pr.flush()
+        res = pr.propose(current, rs.max_tokens, rep)
+        pr.check_state(f"round {r} propose")
+        if res is not None and sample:
+            n, logits, out = res
+            ids, probs = gpu_sample([pr.g], [0, n], logits, wl.temperature, wl.rep_penalty, wl.history, r,
+                                    probs=wl.probs)
+            ids = ids.cpu().numpy()
+            o = pr.o[-1]
+            ref = []
+            for i in range(n):
+                oid, oprob, score = sample_row(out["logits"][i], o.history[-wl.history:] if wl.history else [],
+                                               wl.temperature, wl.rep_penalty, pr.seed, pr.sid, r, i)
+                zmax = float(np.max(np.abs(out["logits"][i])))
+                ref.append((oid, score, margin(cfg, zmax, wl.temperature)))
+                if probs is not None:
+                    e = rel_err(probs[i].double().cpu().numpy(), oprob)
+                    pt = probs_tol(logits[i].double().cpu().numpy(), out["logits"][i], wl.temperature)
+                    rep.note("probs", e)
+                    rep.note("probs/bound", e / pt)
+                    assert e < pt, f"probs rel err {e} above the bound {pt} implied by the logits"
+            check_ids(ids, ref, rep)
+        n = res[0] if res is not None else 0
+        a = rs.accept(n)
+        pr.commit_block()
+        F = pr.o[0].ctx_offset + pr.o[0].pending_count
+        toks = np.concatenate([[current], fs.tokens(F + 1, a)]).astype(np.int32)
+        pr.committed(toks, fs.features(F, a + 1), F)
+        pr.check_state(f"round {r} commit")
+        current = rs.bonus()
+        rep.rounds += 1
+        if check_cache_every and (r + 1) % check_cache_every == 0:
+            pr.check_cache(rep)
+    pr.flush()
+    pr.check_state("final flush")
+    pr.check_cache(rep)
+    return rep

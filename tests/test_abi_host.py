@@ -1,0 +1,320 @@
+"""C ABI tests that need no GPU.
+
+* libdflash.so loads and exports every function include/dflash.h declares
+  (nothing is called: there is no device here).
+* The session state machine, through the same C ABI built over the trace
+  backend (libdflash_host.so), follows the golden scripts hand-derived from
+  Ollama mlxrunner/dflash.go, rejects gaps and bad configs with the documented
+  codes and unchanged state, and plans the expected context passes (chunking
+  by flush_rows, Laguna drop-before-fc).
+"""
+import ctypes
+import os
+import re
+from ctypes import byref, c_int32, c_int64, c_void_p
+
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_fwd_amd import abi
+from tests.helpers import load_golden, run_script
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported_by_hip_library():
+    if not os.path.exists(abi.LIB_HIP):
+        pytest.skip("libdflash.so not built")
+    lib = ctypes.CDLL(abi.LIB_HIP)
+    names = _header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(abi.SYMBOLS), "binding and header disagree"
+
+
+# --------------------------------------------------------------------------
+# host (trace) build
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def host():
+    from block_diffusion_drafter_fwd_amd import build
+    build.build_host()
+    lib = abi.load("host")
+    lib.dflash_trace_count.restype = ctypes.c_int
+    lib.dflash_trace_line.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_int]
+    return lib
+
+
+def _trace(lib):
+    out = []
+    buf = ctypes.create_string_buffer(4096)
+    for i in range(lib.dflash_trace_count()):
+        lib.dflash_trace_line(i, buf, 4096)
+        out.append(buf.value.decode())
+    lib.dflash_trace_clear()
+    return out
+
+
+class FakeModel:
+    """dflash_config + dflash_weights whose pointers are host buffers: the
+    trace backend checks shapes and never dereferences data."""
+
+    def __init__(self, lib, **kw):
+        base = dict(dtype=abi.FP32, hidden=64, layers=2, q_heads=4, kv_heads=4, head_dim=16, taps=5,
+                    target_hidden=64, vocab=32, block_size=8, mask_id=31, window=0, intermediate=192,
+                    causal=1, qk_norm=1, gate=0, aux_norms=0, ctx_input_norm=0, fused_qkv=0,
+                    attention_bias=0, flush_rows=16)
+        base.update(kw)
+        self.c = abi.Config()
+        for k, v in base.items():
+            setattr(self.c, k, v)
+        self.c.rope_theta = 10000.0
+        self.c.rms_eps = 1e-6
+        self.buf = np.zeros(64, dtype=np.uint8)
+        self.lib = lib
+        self.W = self.weights()
+
+    def t(self, *shape):
+        x = abi.Tensor()
+        x.data = self.buf.ctypes.data
+        x.ndim = len(shape)
+        for i, s in enumerate(shape):
+            x.shape[i] = s
+        return x
+
+    def weights(self, **override):
+        c = self.c
+        H, V, I, D = c.hidden, c.vocab, c.intermediate, c.head_dim
+        qd, kd = c.q_heads * D, c.kv_heads * D
+        W = abi.Weights()
+        W.embed, W.lm_head, W.fc = self.t(V, H), self.t(V, H), self.t(H, c.taps * c.target_hidden)
+        W.hidden_norm, W.norm = self.t(H), self.t(H)
+        W.aux_norms = self.t(c.taps, c.target_hidden)
+        self.layers = (abi.LayerWeights * c.layers)()
+        for l in range(c.layers):
+            L = self.layers[l]
+            L.input_layernorm = L.post_attention_layernorm = self.t(H)
+            L.q_proj, L.k_proj, L.v_proj = self.t(qd, H), self.t(kd, H), self.t(kd, H)
+            L.qkv_proj = self.t(qd + 2 * kd, H)
+            L.q_norm = L.k_norm = self.t(D)
+            L.g_proj = self.t(c.q_heads, H)
+            L.o_proj = self.t(H, qd)
+            L.gate_proj = L.up_proj = self.t(I, H)
+            L.down_proj = self.t(H, I)
+            for k, v in override.items():
+                setattr(L, k, v)
+        W.layers = ctypes.cast(self.layers, ctypes.POINTER(abi.LayerWeights))
+        return W
+
+    def create(self):
+        ctx = c_void_p()
+        rc = self.lib.dflash_create(byref(self.c), byref(self.W), byref(ctx))
+        return rc, ctx
+
+
+class HostSession:
+    def __init__(self, lib, ctx, capacity=4096, restored=0, max_sessions=1):
+        self.lib = lib
+        n = lib.dflash_session_bytes(ctx, capacity)
+        self.arena = np.zeros(n, dtype=np.uint8)
+        ws = lib.dflash_workspace_bytes(ctx, max_sessions)
+        self.ws = np.zeros(ws, dtype=np.uint8)
+        self.h = c_void_p()
+        abi.check(lib, lib.dflash_session_open(ctx, self.arena.ctypes.data, n, capacity, self.ws.ctypes.data,
+                                               ws, max_sessions, restored, 1, 2, None, byref(self.h)))
+        self.feat = np.zeros(1 << 16, dtype=np.uint8)
+
+    def committed(self, tokens, feats, position):
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        abi.check(self.lib, self.lib.dflash_committed(self.h, t.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                                      self.feat.ctypes.data, len(t), position))
+
+    def flush(self):
+        abi.check(self.lib, self.lib.dflash_flush(self.h))
+
+    def commit_block(self):
+        abi.check(self.lib, self.lib.dflash_commit_block(self.h))
+
+    def propose(self, current, max_tokens):
+        n = c_int32()
+        logits = np.zeros(16, dtype=np.float32)
+        abi.check(self.lib, self.lib.dflash_propose(self.h, current, max_tokens, logits.ctypes.data, None,
+                                                    byref(n)))
+        return n.value
+
+    def state(self):
+        a, b, c, d, e = c_int32(), c_int32(), c_int32(), c_int32(), c_int64()
+        abi.check(self.lib, self.lib.dflash_session_state(self.h, byref(a), byref(b), byref(c), byref(d),
+                                                          byref(e)))
+        self._rw = e.value
+        return a.value, b.value, c.value, d.value
+
+    @property
+    def rows_written(self):
+        self.state()
+        return self._rw
+
+
+@pytest.mark.parametrize("fixture", ["session_script.json", "window_drop_script.json"])
+def test_golden_scripts_through_c_abi(host, fixture):
+    g = load_golden(fixture)
+    c = g["config"]
+    fm = FakeModel(host, block_size=c["block_size"], flush_rows=c["flush_rows"], window=c["window"],
+                   causal=int(c["window"] == 0))
+    rc, ctx = fm.create()
+    assert rc == 0, host.dflash_last_error()
+    _trace(host)
+    run_script(g, lambda off: HostSession(host, ctx, capacity=64, restored=off),
+               lambda pos, cnt: None, abi.ContextGap)
+    host.dflash_destroy(ctx)
+
+
+def test_chunked_flush_plan(host):
+    fm = FakeModel(host, flush_rows=16)
+    rc, ctx = fm.create()
+    assert rc == 0
+    s = HostSession(host, ctx)
+    _trace(host)
+    s.committed(np.arange(5), None, 0)
+    s.committed(np.arange(5, 45), None, 5)          # 45 rows >= 16: flush everything
+    tr = [l for l in _trace(host) if l.startswith("ctx")]
+    assert tr == ["ctx sess=0 pos0=0 rows=16", "ctx sess=0 pos0=16 rows=16", "ctx sess=0 pos0=32 rows=13"]
+    assert s.state() == (45, 0, 45, 0) and s.rows_written == 45
+
+
+def test_window_drop_plan_skips_old_chunks(host):
+    fm = FakeModel(host, flush_rows=16, window=6, causal=0)
+    rc, ctx = fm.create()
+    assert rc == 0
+    s = HostSession(host, ctx, capacity=64)
+    _trace(host)
+    s.committed(np.arange(100), None, 0)            # frontier 100: keep slots >= 95
+    tr = [l for l in _trace(host) if l.startswith("ctx")]
+    assert tr == ["ctx sess=0 pos0=95 rows=1", "ctx sess=0 pos0=96 rows=4"]
+    assert s.state() == (100, 0, 100, 0) and s.rows_written == 5
+
+
+def test_history_ring_and_sample_plan(host):
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    s = HostSession(host, ctx)
+    _trace(host)
+    s.committed(np.arange(600), None, 0)
+    hist = [l for l in _trace(host) if l.startswith("hist")]
+    toks = [int(x) for l in hist for x in l.split("tokens=")[1].split(",")]
+    assert toks == list(range(88, 600))             # only the last 512 are kept
+    n = s.propose(3, 7)
+    logits = np.zeros(16, dtype=np.float32)
+    ids = np.zeros(16, dtype=np.int32)
+    offs = (c_int32 * 2)(0, n)
+    hs = (c_void_p * 1)(s.h)
+    p = abi.SampleParams(0.7, 1.1, 512, 4)
+    abi.check(host, host.dflash_sample(hs, 1, offs, logits.ctypes.data, byref(p), ids.ctypes.data, None))
+    tr = [l for l in _trace(host) if l.startswith("sample")]
+    assert tr == ["sample rows=7 round=4 hist=600@0"]        # ring of 512 written from slot 0
+
+
+@pytest.mark.parametrize("field,value", [("block_size", 1), ("block_size", 513), ("window", 1),
+                                         ("window", (1 << 20) + 1), ("attention_bias", 1), ("kv_heads", 3),
+                                         ("dtype", 5), ("layers", 17)])
+def test_config_bounds(host, field, value):
+    fm = FakeModel(host, **{field: value})
+    rc, ctx = fm.create()
+    assert rc == abi.E_CONFIG, (field, value, rc)
+
+
+def test_bf16_shape_rules(host):
+    fm = FakeModel(host, dtype=abi.BF16)                 # head_dim 16 not allowed on the bf16 path
+    assert fm.create()[0] == abi.E_CONFIG
+
+
+def test_weight_shape_checks(host):
+    fm = FakeModel(host)
+    fm.W = fm.weights(q_proj=fm.t(60, 64))               # wrong q_proj rows
+    rc, _ = fm.create()
+    assert rc == abi.E_SHAPE and b"q_proj" in host.dflash_last_error()
+    fm = FakeModel(host, fused_qkv=1)
+    fm.W = fm.weights(qkv_proj=fm.t(64 + 64 + 63, 64))
+    assert fm.create()[0] == abi.E_SHAPE
+    fm = FakeModel(host, gate=1)
+    fm.W = fm.weights(g_proj=fm.t(4, 63))                # input width
+    assert fm.create()[0] == abi.E_SHAPE
+    fm = FakeModel(host)
+    fm.W = fm.weights(k_norm=fm.t(15))                   # per-head norm length
+    assert fm.create()[0] == abi.E_SHAPE
+
+
+def test_gap_and_capacity_errors_leave_state(host):
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    s = HostSession(host, ctx, capacity=32)
+    s.committed(np.arange(10), None, 0)
+    with pytest.raises(abi.ContextGap):
+        s.committed(np.arange(3), None, 11)
+    assert s.state() == (0, 10, 0, 0)
+    with pytest.raises(abi.DFlashError) as e:
+        s.committed(np.arange(20), None, 10)             # 30 + block 8 > 32
+    assert e.value.code == abi.E_CAPACITY
+    assert s.state() == (0, 10, 0, 0)
+
+
+def test_windowed_capacity_rule(host):
+    fm = FakeModel(host, window=6, causal=0)
+    rc, ctx = fm.create()
+    n = host.dflash_session_bytes(ctx, 12)
+    arena = np.zeros(n, dtype=np.uint8)
+    ws = np.zeros(host.dflash_workspace_bytes(ctx, 1), dtype=np.uint8)
+    h = c_void_p()
+    rc = host.dflash_session_open(ctx, arena.ctypes.data, n, 12, ws.ctypes.data, ws.size, 1, 0, 0, 0, None,
+                                  byref(h))
+    assert rc == abi.E_CAPACITY                          # needs >= 6 + 8 - 1 = 13
+    HostSession(host, ctx, capacity=13)
+
+
+def test_batch_rules(host):
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    a = HostSession(host, ctx, max_sessions=4)
+    b = HostSession(host, ctx, max_sessions=4)
+    b.ws, b.h2 = a.ws, None
+    # sessions with different workspaces cannot be batched
+    logits = np.zeros(64, dtype=np.float32)
+    offs = (c_int32 * 3)()
+    hs = (c_void_p * 2)(a.h, b.h)
+    cur = (c_int32 * 2)(1, 2)
+    mt = (c_int32 * 2)(3, 3)
+    a.committed(np.arange(4), None, 0)
+    rc = host.dflash_propose_batch(hs, 2, cur, mt, logits.ctypes.data, offs)
+    assert rc == abi.E_ARG
+    # a batch over one workspace; a session with no context contributes no rows
+    ws = np.zeros(host.dflash_workspace_bytes(ctx, 4), dtype=np.uint8)
+    sess = []
+    for k in range(3):
+        n = host.dflash_session_bytes(ctx, 64)
+        arena = np.zeros(n, dtype=np.uint8)
+        h = c_void_p()
+        abi.check(host, host.dflash_session_open(ctx, arena.ctypes.data, n, 64, ws.ctypes.data, ws.size, 4,
+                                                 0, 0, k, None, byref(h)))
+        sess.append((h, arena))
+    feat = np.zeros(1 << 14, dtype=np.uint8)
+    for k, (h, _) in enumerate(sess[:2]):
+        t = np.arange(3 + k, dtype=np.int32)
+        abi.check(host, host.dflash_committed(h, t.ctypes.data_as(ctypes.POINTER(c_int32)), feat.ctypes.data,
+                                              len(t), 0))
+    _trace(host)
+    hs = (c_void_p * 3)(*[h for h, _ in sess])
+    cur = (c_int32 * 3)(5, 6, 7)
+    mt = (c_int32 * 3)(2, 9, 4)
+    offs = (c_int32 * 4)()
+    abi.check(host, host.dflash_propose_batch(hs, 3, cur, mt, logits.ctypes.data, offs))
+    assert list(offs) == [0, 2, 9, 9]
+    tr = _trace(host)
+    assert tr == ["ctx sess=0 pos0=0 rows=3", "ctx sess=1 pos0=0 rows=4",
+                  "block sess=0 F=3 M=3 cur=5", "block sess=1 F=4 M=8 cur=6"]

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle.
+
+Sizes keep the model dimensions of each configuration family (so every
+kernel runs its real tiling: 256-row flushes through the tiled MFMA GEMM,
+16-row blocks through the skinny one, the 64-query-row attention tile) while
+cutting layers, vocabulary (ragged: not a multiple of any tile) and context
+(ragged flush tails), so that the oracle finishes in seconds.  Probabilities
+are held to the bound their own logit deviation implies (see
+tests/parity.py: probs_tol); the logits are held to 2e-2 (bf16) / 1e-4 (fp32).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.parity import (Pair, Report, check_ids, device_tensors, feats_dev, margin, probs_tol, rel_err,
+                          run_session_script, tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_fwd_amd import abi
+    abi.load("hip")
+    return True
+
+
+def _drafter(cfg, w, max_sessions=1):
+    from block_diffusion_drafter_fwd_amd import Drafter
+    return Drafter(cfg, device_tensors(cfg, w), max_sessions=max_sessions)
+
+
+W = synth.Workload
+CASES = {
+    # name: (config, workload, capacity)
+    "tiny": (synth.config("tiny"), synth.WORKLOADS["tiny"], 48 + 8 * 20 + 16),
+    "tiny_w": (synth.config("tiny_w"), synth.WORKLOADS["tiny_w"], 6 + 8 - 1),
+    "tiny_sampling": (synth.config("tiny", causal=False),
+                      W("ts", "tiny", context=37, commit_rows=5, rounds=12, temperature=0.7, rep_penalty=1.1,
+                        history=24, probs=True, max_tokens=-1, flush_fraction=1.0), 400),
+    "qwen_small": (synth.config("qwen", layers=2, vocab=5003),
+                   W("qs", "qwen", context=300, commit_rows=256, rounds=5), 512),
+    "laguna_small": (synth.config("laguna", layers=2, vocab=4099),
+                     W("ls", "laguna", context=1100, commit_rows=300, rounds=5), 512 + 8 - 1),
+    "long_small": (synth.config("long", layers=1, vocab=3001),
+                   W("lo", "long", context=270, commit_rows=256, rounds=4, max_tokens=7, temperature=1.0,
+                     probs=True), 400),
+    "batched_shape_sampling": (synth.config("qwen", layers=1, vocab=3001),
+                               W("bs", "qwen", context=130, commit_rows=40, rounds=5, max_tokens=-1,
+                                 temperature=0.7, rep_penalty=1.1, history=512, probs=True), 300),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_round_script_parity(cuda, name):
+    cfg, wl, cap = CASES[name]
+    say(f"[parity] {name}: weights")
+    w = synth.make_weights(cfg, seed=1, gains="random")
+    d = _drafter(cfg, w)
+    say(f"[parity] {name}: running {wl.rounds} rounds, context {wl.context}")
+    rep = run_session_script(d, cfg, wl, w, cap, seed=1, sid=3)
+    say(f"[parity] {name}: worst {rep.worst} ids compared {rep.ids_compared} skipped {rep.ids_skipped}")
+    assert rep.ids_compared > 0
+    assert rep.ids_skipped <= max(2, rep.ids_compared // 10)
+
+
+def test_restored_offset_and_gap(cuda):
+    """open() at a restored offset skips the held prefix; a run past the
+    frontier is refused with the state unchanged (dflash.go committed)."""
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg, seed=2)
+    d = _drafter(cfg, w)
+    fs = synth.FeatureSource(cfg, 2)
+    s = d.session(128)
+    s.committed(fs.tokens(0, 20), feats_dev(cfg, fs.features(0, 20)), 0)
+    st = s.state()
+    from block_diffusion_drafter_fwd_amd import ContextGap
+    with pytest.raises(ContextGap):
+        s.committed([1, 2], torch.zeros((2, cfg.fc_in), device="cuda"), 25)
+    assert s.state() == st
+
+
+def test_batched_propose_matches_oracle(cuda):
+    """dflash_propose_batch over sessions of ragged context (one with none)
+    equals each session's own oracle propose; one batched sample call draws
+    every row with per-session penalties."""
+    from block_diffusion_drafter_fwd_amd import propose_batch, sample
+    from oracle.sampler import sample_row
+    cfg = synth.config("qwen", layers=2, vocab=4099)
+    w = synth.make_weights(cfg, seed=4, gains="random")
+    d = _drafter(cfg, w, max_sessions=5)
+    lens = [260, 300, 17, 0, 45]
+    mts = [15, 3, 7, 5, 1]
+    pairs = [Pair(d, cfg, w, 512, seed=4, sid=k) for k in range(len(lens))]
+    srcs = [synth.FeatureSource(cfg, 4, k) for k in range(len(lens))]
+    for k, (pr, L) in enumerate(zip(pairs, lens)):
+        for p in range(0, L, 100):
+            T = min(100, L - p)
+            pr.committed(srcs[k].tokens(p, T), srcs[k].features(p, T), p)
+    rep = Report()
+    rng = np.random.default_rng(0)
+    for r in range(3):
+        say(f"[parity] batched round {r}")
+        cur = [int(x) for x in rng.integers(0, cfg.vocab - 1, len(lens))]
+        outs = [[o.propose(c, m) for o in pr.o] for pr, c, m in zip(pairs, cur, mts)]
+        offs, logits = propose_batch([pr.g for pr in pairs], cur, mts)
+        for k, pr in enumerate(pairs):
+            pr.check_state(f"batched round {r} session {k}")
+            rows = logits[offs[k]:offs[k + 1]].double().cpu().numpy()
+            if outs[k][0] is None:
+                assert offs[k + 1] == offs[k]
+                continue
+            for j, out in enumerate(outs[k]):
+                e = rel_err(rows, out["logits"])
+                rep.note(f"logits[{j}]", e)
+                assert e < tol(cfg), (k, j, e)
+        ids, probs = sample([pr.g for pr in pairs], offs, logits, 0.7, 1.1, 512, r, probs=True)
+        ids = ids.cpu().numpy()
+        ref = []
+        for k, pr in enumerate(pairs):
+            if outs[k][0] is None:
+                continue
+            o = pr.o[-1]
+            for i in range(outs[k][-1]["n"]):
+                z = outs[k][-1]["logits"][i]
+                oid, op, sc = sample_row(z, o.history[-512:], 0.7, 1.1, 4, k, r, i)
+                ref.append((oid, sc, margin(cfg, float(np.max(np.abs(z))), 0.7)))
+                e = rel_err(probs[offs[k] + i].double().cpu().numpy(), op)
+                pt = probs_tol(logits[offs[k] + i].double().cpu().numpy(), z, 0.7)
+                rep.note("probs", e)
+                rep.note("probs/bound", e / pt)
+                assert e < pt, (k, i, e, pt)
+        check_ids(ids, ref, rep)
+        for k, pr in enumerate(pairs):
+            pr.commit_block()
+            F = pr.o[0].ctx_offset + pr.o[0].pending_count
+            if F:
+                toks = np.array([cur[k], 7], dtype=np.int32)
+                pr.committed(toks, srcs[k].features(F, 2), F)
+    say(f"[parity] batched worst {rep.worst} ids {rep.ids_compared}/{rep.ids_skipped}")
+    for pr in pairs:
+        pr.flush()
+        pr.check_state("final")
+        pr.check_cache(rep)
+    assert rep.ids_compared > 0
