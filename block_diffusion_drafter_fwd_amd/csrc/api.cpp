@@ -89,6 +89,7 @@ static int check_config(const dflash_config& c) {
         c.taps <= 0 || c.target_hidden <= 0 || c.vocab <= 1 || c.intermediate <= 0)
         return bad("sizes must be positive");
     if (c.layers > kMaxLayers) return bad("at most 16 layers");
+    if (c.hidden > 8192 || c.target_hidden > 8192) return bad("hidden and target_hidden must be at most 8192");
     if (c.block_size < 2 || c.block_size > 512) return bad("block_size must lie in 2..512");
     if (c.window != 0 && (c.window < 2 || c.window > (1 << 20)))
         return bad("window must be 0 or lie in 2..2^20");

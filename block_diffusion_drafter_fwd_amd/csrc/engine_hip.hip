@@ -1,12 +1,23 @@
 // HIP backend of the drafter: plans and enqueues the kernels of the context
-// pass (taps -> [aux norms] -> fc -> hidden_norm -> [per-layer input norm]
-// -> all layers' K/V in one GEMM -> k-norm + RoPE + slot write), the block
-// pass (embed -> per layer: norm, QKV(+g) GEMM, q/k norm + RoPE + block K/V
-// write, attention, o_proj, norm, gate|up GEMM, SwiGLU, down_proj -> final
-// norm of rows 1..n -> unembedding) and the sampler.  All device memory is
-// the caller's: the per-call tables and every intermediate live in the
-// workspace whose layout is computed here.
+// pass, the block pass and the sampler.  All device memory is the caller's:
+// the per-call tables and every intermediate live in the workspace whose
+// layout is computed here.
+//
+// Context pass (rows of one or more sessions):
+//   [aux tap norms] -> fc GEMM (K slices) -> hidden_norm (sums the slices)
+//   -> [per-layer input_layernorm] -> every layer's k|v in one GEMM (K slices)
+//   -> head_finish (sums slices; k-norm, RoPE, slot write of K and V)
+// Block pass (anchor + n mask rows per sequence):
+//   embed -> norm -> per layer: QKV(+g) GEMM (slices) -> head_finish (q to the
+//   query buffer, block K/V to the cache) -> attention partials -> combine
+//   (+ gate) -> o_proj (slices) -> residual add + post norm -> gate|up GEMM
+//   with SwiGLU epilogue -> down_proj (slices) -> residual add + next norm
+//   (the final norm after the last layer) -> unembedding of rows 1..n.
+// Splitting K over workgroups lets the small-N weight-streaming GEMMs use all
+// CUs; the slices are added by whichever kernel reads the result next, so no
+// reduction pass is launched.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -21,19 +32,20 @@ using namespace kern;
 
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
+constexpr int kSampleChunk = 4096;
+constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
+constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 32 MiB
+constexpr int kMaxSlicesFc = 8;                      // K slices of the fc GEMM
+constexpr int kMaxSlicesKv = 2;                      // K slices of the context k|v GEMM
+
 struct WsLayout {
-    size_t desc, rowinfo, rowsrc, srcptr;
+    size_t tables;
     size_t ctx_stage, ctx_fc, ctx_c, ctx_x, ctx_kv;
-    size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_mlp;
+    size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_part, blk_mlp, blk_act;
     size_t attn_o, attn_ml, part, bitmap, stats;
     size_t total;
-    int32_t r_ctx, r_blk, items_cap, nchunk_max;
-    size_t part_cap;
+    int32_t r_ctx, r_blk, items_cap, nchunk_max, blk_slices;
 };
-
-constexpr int kSampleChunk = 4096;
-constexpr int kAttnTargetWG = 2048;
-constexpr size_t kPartCapFloats = size_t(8) << 20;   // split-K partials: 32 MiB
 
 #define HIP_OK(expr)                                                                    \
     do {                                                                                \
@@ -52,37 +64,40 @@ public:
         const size_t act = m_.elem;
         w.r_blk = ms * c.block_size;
         w.r_ctx = std::max(c.flush_rows, w.r_blk);
+        w.blk_slices = std::max(1, std::min(8, 4096 / w.r_blk));
         const int32_t rmax = std::max(w.r_ctx, w.r_blk);
         const int32_t L = c.layers, H = c.hidden, I = c.intermediate;
-        w.items_cap = std::max(1, kAttnTargetWG / c.kv_heads) + ms;
+        w.items_cap = std::max(1, attn_target_wg() / c.kv_heads) + ms;
         w.nchunk_max = (c.vocab + kSampleChunk - 1) / kSampleChunk;
-        w.part_cap = kPartCapFloats;
         size_t o = 0;
         auto put = [&](size_t bytes) { size_t at = o; o += al(bytes); return at; };
-        w.desc = put(sizeof(SeqDesc) * (size_t)ms);
-        w.rowinfo = put(sizeof(RowInfo) * (size_t)rmax);
-        w.rowsrc = put(sizeof(int32_t) * (size_t)w.r_blk);
-        w.srcptr = put(sizeof(uint64_t) * (size_t)w.r_ctx);
+        w.tables = put(sizeof(SeqDesc) * (size_t)ms + sizeof(RowInfo) * (size_t)rmax +
+                       sizeof(int32_t) * (size_t)w.r_blk + sizeof(uint64_t) * (size_t)w.r_ctx + 64);
         w.ctx_stage = put(act * (size_t)w.r_ctx * m_.fc_in);
-        w.ctx_fc = put(4 * (size_t)w.r_ctx * H);
+        w.ctx_fc = put(4 * (size_t)kMaxSlicesFc * w.r_ctx * H);
         w.ctx_c = put(4 * (size_t)w.r_ctx * H);
         w.ctx_x = put(act * (size_t)(c.ctx_input_norm ? L : 1) * w.r_ctx * H);
-        w.ctx_kv = put(4 * (size_t)w.r_ctx * L * 2 * m_.kd);
+        w.ctx_kv = put(4 * (size_t)kMaxSlicesKv * w.r_ctx * L * 2 * m_.kd);
         w.blk_h = put(4 * (size_t)w.r_blk * H);
-        w.blk_x = put(act * (size_t)w.r_blk * std::max(std::max(H, I), m_.qd));
-        w.blk_qkv = put(4 * (size_t)w.r_blk * qkv_ld());
+        w.blk_x = put(act * (size_t)w.r_blk * H);
+        w.blk_qkv = put(4 * (size_t)w.blk_slices * w.r_blk * qkv_ld());
         w.blk_q = put(act * (size_t)w.r_blk * m_.qd);
         w.blk_attn = put(act * (size_t)w.r_blk * m_.qd);
+        w.blk_part = put(4 * (size_t)w.blk_slices * w.r_blk * H);
         w.blk_mlp = put(4 * (size_t)w.r_blk * 2 * I);
+        w.blk_act = put(act * (size_t)w.r_blk * I);
         const bool bf16 = c.dtype == DFLASH_BF16;
         w.attn_o = put(bf16 ? 4 * (size_t)w.items_cap * c.kv_heads * 64 * c.head_dim : 0);
         w.attn_ml = put(bf16 ? 4 * (size_t)w.items_cap * c.kv_heads * 64 * 2 : 0);
-        w.part = put(bf16 ? 4 * w.part_cap : 0);
+        w.part = put(bf16 ? 4 * kPartCapFloats : 0);
         w.bitmap = put(4 * (size_t)ms * ((c.vocab + 31) / 32));
         w.stats = put(16 * (size_t)w.r_blk * w.nchunk_max);
         w.total = o;
         return w;
     }
+
+    // attention work items per call: about four workgroups per CU over all kv heads
+    int32_t attn_target_wg() const { return 4 * cus_; }
 
     int32_t qkv_ld() const { return m_.qd + 2 * m_.kd + (m_.cfg.gate ? m_.cfg.q_heads : 0); }
 
@@ -179,6 +194,36 @@ private:
         return n;
     }
 
+    GemmArgs gemm_args(int32_t M, int32_t K, float* C, int32_t ldc, GemmMode mode, float* part,
+                       int32_t max_slices) const {
+        GemmArgs g{};
+        g.M = M;
+        g.K = K;
+        g.C = C;
+        g.ldc = ldc;
+        g.mode = mode;
+        g.part = part;
+        g.max_splits = max_slices;
+        return g;
+    }
+
+    // Per-call tables, packed and written by one upload (a few for long tables).
+    struct Tables {
+        std::vector<uint8_t> blob;
+        size_t add(const void* p, size_t n) {
+            const size_t off = (blob.size() + 15) & ~size_t(15);
+            blob.resize(off + n);
+            if (n) std::memcpy(blob.data() + off, p, n);
+            return off;
+        }
+    };
+
+    void fill_inv_freq(HeadArgs& h) const {
+        const dflash_config& c = m_.cfg;
+        for (int d = 0; d < c.head_dim / 2 && d < 64; ++d)
+            h.inv_freq[d] = std::pow((double)c.rope_theta, -2.0 * d / (double)c.head_dim);
+    }
+
     SeqDesc desc_of(const SessView& s) const {
         SeqDesc d{};
         d.cache = s.cache;
@@ -205,6 +250,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
     char* base = (char*)ws;
     const int32_t H = c.hidden, L = c.layers, kd = m_.kd;
     const size_t rb = (size_t)m_.fc_in * m_.elem;
+    float* part = (float*)(base + w.part);
     size_t si = 0;
     while (si < segs.size()) {
         // a group of whole segments with at most r_ctx rows
@@ -227,16 +273,19 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
                 srcs.push_back((uint64_t)((const char*)g.rows + (size_t)r * rb));
             }
         }
-        HIP_OK(upload(base + w.desc, descs.data(), sizeof(SeqDesc) * descs.size(), st));
-        HIP_OK(upload(base + w.rowinfo, info.data(), sizeof(RowInfo) * info.size(), st));
-        const SeqDesc* d_desc = (const SeqDesc*)(base + w.desc);
-        const RowInfo* d_info = (const RowInfo*)(base + w.rowinfo);
+        Tables tb;
+        const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+        const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+        const size_t o_src = sj - si > 1 ? tb.add(srcs.data(), sizeof(uint64_t) * srcs.size()) : 0;
+        char* tab = base + w.tables;
+        HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+        const SeqDesc* d_desc = (const SeqDesc*)(tab + o_desc);
+        const RowInfo* d_info = (const RowInfo*)(tab + o_info);
 
         // A operand of fc: the segment rows themselves, or gathered / aux-normed
         const void* A = segs[si].rows;
         if (sj - si > 1) {
-            HIP_OK(upload(base + w.srcptr, srcs.data(), sizeof(uint64_t) * srcs.size(), st));
-            HIP_OK(gather_rows(base + w.ctx_stage, (const uint64_t*)(base + w.srcptr), rows, rb, st));
+            HIP_OK(gather_rows(base + w.ctx_stage, (const uint64_t*)(tab + o_src), rows, rb, st));
             A = base + w.ctx_stage;
         }
         if (c.aux_norms) {
@@ -250,28 +299,34 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             HIP_OK(rmsnorm(n, st));
             A = base + w.ctx_stage;
         }
+        float* fc_out = (float*)(base + w.ctx_fc);
+        int fc_slices = 1;
         {
-            GemmArgs g{};
-            g.M = rows;
-            g.K = m_.fc_in;
-            g.C = (float*)(base + w.ctx_fc);
-            g.ldc = H;
-            g.part = (float*)(base + w.part);
+            GemmArgs g = gemm_args(rows, m_.fc_in, fc_out, H, kPartial, part, kMaxSlicesFc);
             g.nseg = 1;
             g.seg[0] = GemmSeg{A, m_.fc, m_.fc_in, m_.fc_in, H, 0, 0, 0};
             Timed tm(this, "flush_fc", st);
-            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+            HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &fc_slices));
         }
-        // hidden_norm, then (Laguna) every layer's input_layernorm
+        // hidden_norm over the summed slices, then (Laguna) every layer's input_layernorm
         char* xs = base + w.ctx_x;
         const size_t xstride = m_.elem * (size_t)w.r_ctx * H;
-        if (c.ctx_input_norm) {
-            NormArgs n = norm_args(base + w.ctx_fc, 0, H, rows, H);
+        {
+            NormArgs n = norm_args(nullptr, 0, H, rows, H);
+            n.part = fc_out;
+            n.nsplit = fc_slices;
+            n.part_stride = (int64_t)rows * H;
             n.nout = 1;
             n.gain[0] = m_.hidden_norm;
-            n.out[0] = base + w.ctx_c;
-            n.out_bf16 = 0;
+            if (c.ctx_input_norm) {
+                n.out[0] = base + w.ctx_c;
+                n.out_bf16 = 0;
+            } else {
+                n.out[0] = xs;
+            }
             HIP_OK(rmsnorm(n, st));
+        }
+        if (c.ctx_input_norm) {
             for (int32_t l0 = 0; l0 < L; l0 += kMaxOut) {
                 NormArgs n2 = norm_args(base + w.ctx_c, 0, H, rows, H);
                 n2.nout = std::min(kMaxOut, L - l0);
@@ -281,23 +336,13 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
                 }
                 HIP_OK(rmsnorm(n2, st));
             }
-        } else {
-            NormArgs n = norm_args(base + w.ctx_fc, 0, H, rows, H);
-            n.nout = 1;
-            n.gain[0] = m_.hidden_norm;
-            n.out[0] = xs;
-            HIP_OK(rmsnorm(n, st));
         }
         // every layer's K|V in one GEMM (up to 16 layers per launch)
         const int32_t ldkv = L * 2 * kd;
+        float* kv_out = (float*)(base + w.ctx_kv);
         for (int32_t l0 = 0; l0 < L; l0 += kMaxSeg / 2) {
             const int32_t nl = std::min<int32_t>(kMaxSeg / 2, L - l0);
-            GemmArgs g{};
-            g.M = rows;
-            g.K = H;
-            g.C = (float*)(base + w.ctx_kv);
-            g.ldc = ldkv;
-            g.part = (float*)(base + w.part);
+            GemmArgs g = gemm_args(rows, H, kv_out, ldkv, kPartial, part, kMaxSlicesKv);
             g.nseg = 2 * nl;
             for (int32_t j = 0; j < nl; ++j) {
                 const int32_t l = l0 + j;
@@ -305,12 +350,15 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
                 g.seg[2 * j] = GemmSeg{x, m_.layer[l].k, H, H, kd, l * 2 * kd, 0, 0};
                 g.seg[2 * j + 1] = GemmSeg{x, m_.layer[l].v, H, H, kd, l * 2 * kd + kd, 0, 0};
             }
-            Timed tm(this, "flush_kv", st);
-            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
-        }
-        for (int32_t l0 = 0; l0 < L; l0 += kMaxL) {
+            int kv_slices = 1;
+            {
+                Timed tm(this, "flush_kv", st);
+                HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &kv_slices));
+            }
             HeadArgs h{};
-            h.src = (const float*)(base + w.ctx_kv);
+            h.src = kv_out;
+            h.nsplit = kv_slices;
+            h.src_stride = (int64_t)rows * ldkv;
             h.rows = d_info;
             h.seqs = d_desc;
             h.ld = ldkv;
@@ -320,7 +368,6 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             h.Hkv = c.kv_heads;
             h.L = L;
             h.q_col = -1;
-            const int nl = std::min(kMaxL, L - l0);
             for (int j = 0; j < nl; ++j) {
                 h.k_col[j] = (l0 + j) * 2 * kd;
                 h.v_col[j] = (l0 + j) * 2 * kd + kd;
@@ -331,7 +378,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             h.w_bf16 = bf16();
             h.cache_bf16 = bf16();
             h.eps = c.rms_eps;
-            h.theta = c.rope_theta;
+            fill_inv_freq(h);
             HIP_OK(head_finish(h, nl, st));
         }
         si = sj;
@@ -346,10 +393,9 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
     const int32_t H = c.hidden, I = c.intermediate, qd = m_.qd, kd = m_.kd;
-    const int32_t G = c.q_heads / c.kv_heads;
 
-    // tables: one SeqDesc per block, one RowInfo per block row, the input row
-    // of every unembedded row, and the attention work split
+    // tables: one SeqDesc per block, one RowInfo per block row, the row of
+    // every unembedded row (rows 1..n of each block), the attention work split
     std::vector<SeqDesc> descs;
     std::vector<RowInfo> info;
     std::vector<int32_t> rowsrc;
@@ -371,9 +417,9 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         descs.push_back(d);
     }
     if (R > w.r_blk) return fail(DFLASH_E_CAPACITY, "block rows exceed the workspace");
-    const int32_t target_items = std::max(1, kAttnTargetWG / c.kv_heads);
+    const int32_t target_items = std::max(1, attn_target_wg() / c.kv_heads);
     int32_t chunk = (int32_t)((total_keys + target_items - 1) / target_items);
-    chunk = std::max(64, (chunk + 63) / 64 * 64);
+    chunk = std::max(kAttnMinChunk, (chunk + 63) / 64 * 64);
     int32_t items = 0;
     for (SeqDesc& d : descs) {
         const int32_t nk = d.F + d.M - d.key_lo;
@@ -382,46 +428,48 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         items += d.nitems;
     }
     if (bf16() && items > w.items_cap) return fail(DFLASH_E_CAPACITY, "attention work exceeds the workspace");
-    HIP_OK(upload(base + w.desc, descs.data(), sizeof(SeqDesc) * descs.size(), st));
-    HIP_OK(upload(base + w.rowinfo, info.data(), sizeof(RowInfo) * info.size(), st));
-    HIP_OK(upload(base + w.rowsrc, rowsrc.data(), sizeof(int32_t) * rowsrc.size(), st));
-    const SeqDesc* d_desc = (const SeqDesc*)(base + w.desc);
-    const RowInfo* d_info = (const RowInfo*)(base + w.rowinfo);
+    Tables tb;
+    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+    const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+    const size_t o_src = tb.add(rowsrc.data(), sizeof(int32_t) * rowsrc.size());
+    char* tab = base + w.tables;
+    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+    const SeqDesc* d_desc = (const SeqDesc*)(tab + o_desc);
+    const RowInfo* d_info = (const RowInfo*)(tab + o_info);
+    const int32_t* d_rowsrc = (const int32_t*)(tab + o_src);
 
     float* h = (float*)(base + w.blk_h);
     void* x = base + w.blk_x;
     float* qkv = (float*)(base + w.blk_qkv);
+    float* hpart = (float*)(base + w.blk_part);
+    float* part = (float*)(base + w.part);
     const int32_t ldq = qkv_ld();
     {
         EmbedArgs e{m_.embed, h, d_info, d_desc, H, R, c.mask_id, bf16()};
         HIP_OK(embed(e, st));
+        NormArgs n = norm_args(h, 0, H, R, H);
+        n.nout = 1;
+        n.gain[0] = m_.layer[0].in_ln;
+        n.out[0] = x;
+        HIP_OK(rmsnorm(n, st));
     }
     for (int32_t l = 0; l < c.layers; ++l) {
         const LayerW& lw = m_.layer[l];
+        int qkv_slices = 1;
         {
-            NormArgs n = norm_args(h, 0, H, R, H);
-            n.nout = 1;
-            n.gain[0] = lw.in_ln;
-            n.out[0] = x;
-            HIP_OK(rmsnorm(n, st));
-        }
-        {
-            GemmArgs g{};
-            g.M = R;
-            g.K = H;
-            g.C = qkv;
-            g.ldc = ldq;
-            g.part = (float*)(base + w.part);
+            GemmArgs g = gemm_args(R, H, qkv, ldq, kPartial, part, w.blk_slices);
             g.seg[0] = GemmSeg{x, lw.q, H, H, qd, 0, 0, 0};
             g.seg[1] = GemmSeg{x, lw.k, H, H, kd, qd, 0, 0};
             g.seg[2] = GemmSeg{x, lw.v, H, H, kd, qd + kd, 0, 0};
             g.nseg = 3;
             if (c.gate) g.seg[g.nseg++] = GemmSeg{x, lw.g, H, H, c.q_heads, qd + 2 * kd, 0, 0};
-            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+            HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &qkv_slices));
         }
         {
             HeadArgs hd{};
             hd.src = qkv;
+            hd.nsplit = qkv_slices;
+            hd.src_stride = (int64_t)R * ldq;
             hd.rows = d_info;
             hd.seqs = d_desc;
             hd.q_out = base + w.blk_q;
@@ -442,7 +490,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             hd.cache_bf16 = bf16();
             hd.q_bf16 = bf16();
             hd.eps = c.rms_eps;
-            hd.theta = c.rope_theta;
+            fill_inv_freq(hd);
             HIP_OK(head_finish(hd, 1, st));
         }
         {
@@ -453,6 +501,8 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             a.part_o = (float*)(base + w.attn_o);
             a.part_ml = (float*)(base + w.attn_ml);
             a.gate_src = qkv;
+            a.gate_nsplit = qkv_slices;
+            a.gate_stride = (int64_t)R * ldq;
             a.out = base + w.blk_attn;
             a.nseq = (int32_t)descs.size();
             a.nrows = R;
@@ -470,73 +520,64 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             a.gate_col = qd + 2 * kd;
             a.out_bf16 = bf16();
             a.scale = 1.f / sqrtf((float)c.head_dim);
-            (void)G;
             Timed tm(this, "attention", st);
             HIP_OK(attention(a, bf16(), st));
         }
+        int o_slices = 1;
         {
-            GemmArgs g{};
-            g.M = R;
-            g.K = qd;
-            g.C = h;
-            g.ldc = H;
-            g.accumulate = 1;
-            g.part = (float*)(base + w.part);
+            GemmArgs g = gemm_args(R, qd, hpart, H, kPartial, part, w.blk_slices);
             g.seg[0] = GemmSeg{base + w.blk_attn, lw.o, qd, qd, H, 0, 0, 0};
             g.nseg = 1;
-            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+            HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &o_slices));
         }
-        {
+        {   // h += attention output; x = post-attention norm of h
             NormArgs n = norm_args(h, 0, H, R, H);
+            n.part = hpart;
+            n.nsplit = o_slices;
+            n.part_stride = (int64_t)R * H;
+            n.writeback = h;
             n.nout = 1;
             n.gain[0] = lw.post_ln;
             n.out[0] = x;
             HIP_OK(rmsnorm(n, st));
         }
         {
-            GemmArgs g{};
-            g.M = R;
-            g.K = H;
-            g.C = (float*)(base + w.blk_mlp);
-            g.ldc = 2 * I;
-            g.part = (float*)(base + w.part);
+            GemmArgs g = gemm_args(R, H, (float*)(base + w.blk_mlp), 2 * I, kSwiGLU, part, 1);
             g.seg[0] = GemmSeg{x, lw.gate, H, H, I, 0, 0, 0};
             g.seg[1] = GemmSeg{x, lw.up, H, H, I, I, 0, 0};
             g.nseg = 2;
-            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+            g.out = base + w.blk_act;        // act = silu(x W_gate^T) * (x W_up^T)
+            g.ldo = I;
+            g.out_bf16 = bf16();
+            HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st));
         }
-        HIP_OK(silu_mul((const float*)(base + w.blk_mlp), 2 * I, I, x, bf16(), R, st));
+        int d_slices = 1;
         {
-            GemmArgs g{};
-            g.M = R;
-            g.K = I;
-            g.C = h;
-            g.ldc = H;
-            g.accumulate = 1;
-            g.part = (float*)(base + w.part);
-            g.seg[0] = GemmSeg{x, lw.down, I, I, H, 0, 0, 0};
+            GemmArgs g = gemm_args(R, I, hpart, H, kPartial, part, w.blk_slices);
+            g.seg[0] = GemmSeg{base + w.blk_act, lw.down, I, I, H, 0, 0, 0};
             g.nseg = 1;
-            HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st));
+            HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &d_slices));
+        }
+        {   // h += MLP output; x = next layer's input norm (the final norm after the last)
+            NormArgs n = norm_args(h, 0, H, R, H);
+            n.part = hpart;
+            n.nsplit = d_slices;
+            n.part_stride = (int64_t)R * H;
+            n.writeback = h;
+            n.nout = 1;
+            n.gain[0] = l + 1 < c.layers ? m_.layer[l + 1].in_ln : m_.norm;
+            n.out[0] = x;
+            HIP_OK(rmsnorm(n, st));
         }
     }
     if (hidden) HIP_OK(hipMemcpyAsync(hidden, h, sizeof(float) * (size_t)R * H, hipMemcpyDeviceToDevice, st));
     if (Rout > 0) {
-        NormArgs n = norm_args(h, 0, H, Rout, H);
-        n.row_src = (const int32_t*)(base + w.rowsrc);
-        n.nout = 1;
-        n.gain[0] = m_.norm;
-        n.out[0] = x;
-        HIP_OK(rmsnorm(n, st));
-        GemmArgs g{};
-        g.M = Rout;
-        g.K = H;
-        g.C = logits;
-        g.ldc = c.vocab;
-        g.part = (float*)(base + w.part);
+        GemmArgs g = gemm_args(Rout, H, logits, c.vocab, kStore, part, 1);
+        g.a_rows = d_rowsrc;                 // rows 1..n of every block
         g.seg[0] = GemmSeg{x, m_.lm_head, H, H, c.vocab, 0, 0, 0};
         g.nseg = 1;
         Timed tm(this, "unembed", st);
-        HIP_OK(gemm(g, bf16(), w.part_cap, cus_, st, 1));
+        HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 1));
     }
     return 0;
 }
@@ -561,12 +602,15 @@ int HipEngine::sample(const std::vector<SessView>& sess, const int32_t* row_offs
         any_hist |= descs[k].hist_n > 0;
         for (int32_t r = row_offsets[k]; r < row_offsets[k + 1]; ++r) info.push_back({k, r - row_offsets[k]});
     }
-    HIP_OK(upload(base + w.desc, descs.data(), sizeof(SeqDesc) * descs.size(), st));
-    HIP_OK(upload(base + w.rowinfo, info.data(), sizeof(RowInfo) * info.size(), st));
+    Tables tb;
+    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+    const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+    char* tab = base + w.tables;
+    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
     SampleArgs a{};
     a.logits = logits;
-    a.seqs = (const SeqDesc*)(base + w.desc);
-    a.rows = (const RowInfo*)(base + w.rowinfo);
+    a.seqs = (const SeqDesc*)(tab + o_desc);
+    a.rows = (const RowInfo*)(tab + o_info);
     a.bitmap = (uint32_t*)(base + w.bitmap);
     a.stats = (float*)(base + w.stats);
     a.ids = ids;

@@ -2,15 +2,16 @@
 // and B = a weight [N, K] (row-major, out x in), several weights per launch
 // as column segments (q|k|v|g, gate|up, every layer's k|v).
 //
-//  * k_gemm_skinny   M <= 16 (block path).  Each wave owns 16 output columns
-//    and streams its weight rows straight from HBM into MFMA operands
-//    (v_mfma_f32_16x16x32_bf16); weights are read exactly once, so the kernel
-//    is HBM-bound and split-K supplies enough waves to fill 256 CUs.
+//  * k_gemm_skinny   M <= 16 (block path).  A workgroup owns 16 output
+//    columns and streams their weight rows straight from HBM into MFMA
+//    operands (v_mfma_f32_16x16x32_bf16), its 8 waves splitting K; weights
+//    are read exactly once, so the kernel is HBM-bound.
 //  * k_gemm_tiled    M > 16 (256-row flushes, batched blocks).  64|128 x 128
 //    tiles, 4 waves as 2x2, A and B staged through LDS with double buffering.
 //  * k_gemm_f32      the fp32 configuration (tiny shapes), plain FMA.
 //
-// Split-K partials go to a workspace slice and a reduce kernel writes C.
+// Split-K partials of the tiled kernel go to a workspace slice and a reduce
+// kernel writes C; the skinny kernel reduces inside the workgroup.
 #include "kernels.h"
 
 namespace dflash {
@@ -42,68 +43,243 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int split, int m, i
 }
 
 // ---------------------------------------------------------------------------
-// skinny: M <= 16, 64 columns per workgroup (16 per wave)
+// skinny: M <= 16.  A 512-thread workgroup owns TPW 16-column tiles (two
+// tiles: the same A fragments feed both, halving activation traffic per
+// weight byte; paired mode puts the gate tile and the up tile of the same
+// columns side by side and the epilogue writes silu(gate) * up).  Its 8 waves
+// take interleaved 64-wide k steps of the workgroup's K slice (kPartial mode
+// splits K over gridDim.y workgroups), read the weight rows straight from HBM
+// into MFMA operands, and reduce through LDS in a fixed order.
 // ---------------------------------------------------------------------------
-template <int TAG>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmArgs a) {
-    const int tile = blockIdx.x, split = blockIdx.y;
-    const GemmSeg g = a.seg[find_seg(a, tile)];
+constexpr int kSkWaves = 8;
+
+template <int TPW, int TAG>
+__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
+    constexpr int BATCH = TPW == 1 ? 4 : 2;    // k steps per wave between waits
+    __shared__ float red[kSkWaves][TPW][256];
+    const int b = blockIdx.x, split = blockIdx.y, S = gridDim.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (tile - g.tile0) * 64 + wave * 16;
-    if (n0 >= g.N) return;
     const int r = lane & 15, q = lane >> 4;
-    const bool bval = n0 + r < g.N, aval = r < a.M;
-    const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
-    // lane (r, q) reads 32 contiguous bytes of row r at k + 16q: both MFMAs of
-    // a 64-wide k step see the same k assignment for A and B
-    const uint16_t* Bp = (const uint16_t*)g.B + (size_t)(bval ? n0 + r : 0) * g.ldb + q * 16;
-    const uint16_t* Ap = (const uint16_t*)g.A + (size_t)(aval ? r : 0) * g.lda + q * 16;
+    const bool pair = a.mode == kSwiGLU;
+    const bool aval = r < a.M;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    int k = kb;
-    for (; k + 256 <= ke; k += 256) {
-        u32x4_t bv[8], av[8];
+    const uint16_t* Bp[TPW];
+    bool bval[TPW];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            bv[2 * u] = *(const u32x4_t*)(Bp + k + 64 * u);
-            bv[2 * u + 1] = *(const u32x4_t*)(Bp + k + 64 * u + 8);
+    for (int j = 0; j < TPW; ++j) {
+        int n0;
+        const GemmSeg* g;
+        bool valid = true;
+        if (pair) {
+            g = &a.seg[j];
+            n0 = b * 16;
+        } else {
+            const int tile = b * TPW + j;
+            valid = tile < a.ntiles;
+            g = &a.seg[find_seg(a, valid ? tile : a.ntiles - 1)];
+            n0 = ((valid ? tile : a.ntiles - 1) - g->tile0) * 16;
+        }
+        bval[j] = valid && n0 + r < g->N;
+        Bp[j] = (const uint16_t*)g->B + (size_t)(bval[j] ? n0 + r : 0) * g->ldb + q * 16;
+    }
+    // every tile of a workgroup reads the same A (the launcher guarantees it)
+    const GemmSeg& g0 = a.seg[pair ? 0 : find_seg(a, min(b * TPW, a.ntiles - 1))];
+    const int arow = aval ? (a.a_rows ? a.a_rows[r] : r) : 0;
+    const uint16_t* Ap = (const uint16_t*)g0.A + (size_t)arow * g0.lda + q * 16;
+    f32x4_t acc0[TPW], acc1[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc0[j] = acc1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // this split's 64-wide k steps, interleaved over the waves
+    const int nsteps_all = a.K >> 6;
+    const int per = (nsteps_all + S - 1) / S;
+    const int s_lo = split * per, s_hi = min(nsteps_all, s_lo + per);
+    int st = s_lo + wave;
+    for (; st + (BATCH - 1) * kSkWaves < s_hi; st += BATCH * kSkWaves) {
+        u32x4_t bv[TPW][2 * BATCH], av[2 * BATCH];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int k = (st + u * kSkWaves) << 6;
+                bv[j][2 * u] = *(const u32x4_t*)(Bp[j] + k);
+                bv[j][2 * u + 1] = *(const u32x4_t*)(Bp[j] + k + 8);
+            }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = (st + u * kSkWaves) << 6;
+            av[2 * u] = *(const u32x4_t*)(Ap + k);
+            av[2 * u + 1] = *(const u32x4_t*)(Ap + k + 8);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            av[2 * u] = *(const u32x4_t*)(Ap + k + 64 * u);
-            av[2 * u + 1] = *(const u32x4_t*)(Ap + k + 64 * u + 8);
+        for (int u = 0; u < 2 * BATCH; ++u) {
+            av[u] = aval ? av[u] : zero;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) bv[j][u] = bval[j] ? bv[j][u] : zero;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (!bval) bv[u] = zero;
-            if (!aval) av[u] = zero;
+        for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                if (u & 1) {
+                    acc1[j] = mfma32(av[2 * u], bv[j][2 * u], acc1[j]);
+                    acc1[j] = mfma32(av[2 * u + 1], bv[j][2 * u + 1], acc1[j]);
+                } else {
+                    acc0[j] = mfma32(av[2 * u], bv[j][2 * u], acc0[j]);
+                    acc0[j] = mfma32(av[2 * u + 1], bv[j][2 * u + 1], acc0[j]);
+                }
+            }
+    }
+    for (; st < s_hi; st += kSkWaves) {
+        const int k = st << 6;
+        u32x4_t a0 = *(const u32x4_t*)(Ap + k), a1 = *(const u32x4_t*)(Ap + k + 8);
+        a0 = aval ? a0 : zero;
+        a1 = aval ? a1 : zero;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            u32x4_t b0 = *(const u32x4_t*)(Bp[j] + k), b1 = *(const u32x4_t*)(Bp[j] + k + 8);
+            b0 = bval[j] ? b0 : zero;
+            b1 = bval[j] ? b1 : zero;
+            acc0[j] = mfma32(a0, b0, acc0[j]);
+            acc0[j] = mfma32(a1, b1, acc0[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const f32x4_t acc = acc0[j] + acc1[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][j][lane * 4 + e] = acc[e];
+    }
+    __syncthreads();
+    // output (m, nn) of a tile lives at lane nn + 16 (m / 4), element m % 4
+    const int t = threadIdx.x;
+    const int j = t >> 8;              // tile of this thread (TPW == 2: threads 256..511 take tile 1)
+    const int m = (t & 255) >> 4, nn = t & 15;
+    if (j >= TPW || m >= a.M) return;
+    const int idx = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+    if (pair) {
+        if (j != 0 || b * 16 + nn >= a.seg[0].N) return;
+        float gt = 0.f, up = 0.f;
+        for (int w = 0; w < kSkWaves; ++w) {
+            gt += red[w][0][idx];
+            up += red[w][TPW - 1][idx];
+        }
+        const float v = gt / (1.f + __expf(-gt)) * up;
+        const size_t o = (size_t)m * a.ldo + b * 16 + nn;
+        if (a.out_bf16) {
+            uint32_t u = __float_as_uint(v);
+            u += 0x7FFFu + ((u >> 16) & 1u);
+            ((uint16_t*)a.out)[o] = (uint16_t)(u >> 16);
+        } else {
+            ((float*)a.out)[o] = v;
+        }
+        return;
+    }
+    const int tile = b * TPW + j;
+    if (tile >= a.ntiles) return;
+    const GemmSeg& g = a.seg[find_seg(a, tile)];
+    const int n = (tile - g.tile0) * 16 + nn;
+    if (n >= g.N) return;
+    float s0 = 0.f;
+    for (int w = 0; w < kSkWaves; ++w) s0 += red[w][j][idx];
+    if (a.mode == kPartial) {
+        // this split's share; the consumer of C sums the splits
+        a.C[((size_t)split * a.M + m) * a.ldc + g.c_col0 + n] = s0;
+        return;
+    }
+    float* p = a.C + (size_t)m * a.ldc + g.c_col0 + n;
+    *p = a.mode == kAccumulate ? *p + s0 : s0;
+}
+
+// ---------------------------------------------------------------------------
+// skinny, persistent: the same work split, but each workgroup keeps its waves'
+// A fragments in registers (STEPS 64-wide k steps per wave) and walks column
+// tiles blockIdx.x, blockIdx.x + gridDim.x, ...  The activations are then read
+// once per workgroup instead of once per 16 columns, which is what limits the
+// per-tile kernel when N is large (the unembedding reads 622 MB of weights
+// against 64 KB of activations).
+// ---------------------------------------------------------------------------
+template <int STEPS, int TAG>
+__global__ __launch_bounds__(512) void k_gemm_skinny_p(GemmArgs a) {
+    __shared__ float red[kSkWaves][64 * 4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool pair = a.mode == kSwiGLU;
+    const int nw = pair ? kSkWaves / 2 : kSkWaves;
+    const int wv = pair ? (wave & (kSkWaves / 2 - 1)) : wave;
+    const int r = lane & 15, q = lane >> 4;
+    const bool aval = r < a.M;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    // this wave's k steps are wv, wv + nw, ... (STEPS of them: K = 64 * nw * STEPS)
+    u32x4_t av[2 * STEPS];
+    {
+        const int arow = aval ? (a.a_rows ? a.a_rows[r] : r) : 0;
+        const uint16_t* Ap = (const uint16_t*)a.seg[0].A + (size_t)arow * a.seg[0].lda + q * 16;
+#pragma unroll
+        for (int j = 0; j < STEPS; ++j) {
+            const int k = (wv + j * nw) << 6;
+            av[2 * j] = *(const u32x4_t*)(Ap + k);
+            av[2 * j + 1] = *(const u32x4_t*)(Ap + k + 8);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (u & 1) {
-                acc1 = mfma32(av[2 * u], bv[2 * u], acc1);
-                acc1 = mfma32(av[2 * u + 1], bv[2 * u + 1], acc1);
-            } else {
-                acc0 = mfma32(av[2 * u], bv[2 * u], acc0);
-                acc0 = mfma32(av[2 * u + 1], bv[2 * u + 1], acc0);
+        for (int j = 0; j < 2 * STEPS; ++j) av[j] = aval ? av[j] : zero;
+    }
+    const int t = threadIdx.x;
+    for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        const GemmSeg g = pair ? a.seg[wave / (kSkWaves / 2)] : a.seg[find_seg(a, tile)];
+        const int n0 = (tile - g.tile0) * 16;
+        const bool bval = n0 + r < g.N;
+        const uint16_t* Bp = (const uint16_t*)g.B + (size_t)(bval ? n0 + r : 0) * g.ldb + q * 16;
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int j0 = 0; j0 < STEPS; j0 += 4) {
+            u32x4_t bv[8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = (wv + (j0 + u) * nw) << 6;
+                bv[2 * u] = *(const u32x4_t*)(Bp + k);
+                bv[2 * u + 1] = *(const u32x4_t*)(Bp + k + 8);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) bv[u] = bval ? bv[u] : zero;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (u & 1) {
+                    acc1 = mfma32(av[2 * (j0 + u)], bv[2 * u], acc1);
+                    acc1 = mfma32(av[2 * (j0 + u) + 1], bv[2 * u + 1], acc1);
+                } else {
+                    acc0 = mfma32(av[2 * (j0 + u)], bv[2 * u], acc0);
+                    acc0 = mfma32(av[2 * (j0 + u) + 1], bv[2 * u + 1], acc0);
+                }
             }
         }
-    }
-    for (; k < ke; k += 64) {
-        u32x4_t b0 = *(const u32x4_t*)(Bp + k), b1 = *(const u32x4_t*)(Bp + k + 8);
-        u32x4_t a0 = *(const u32x4_t*)(Ap + k), a1 = *(const u32x4_t*)(Ap + k + 8);
-        if (!bval) b0 = b1 = zero;
-        if (!aval) a0 = a1 = zero;
-        acc0 = mfma32(a0, b0, acc0);
-        acc0 = mfma32(a1, b1, acc0);
-    }
-    const f32x4_t acc = acc0 + acc1;
-    if (!bval) return;
-    const int col = g.c_col0 + n0 + r;
+        const f32x4_t acc = acc0 + acc1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int m = 4 * q + e;
-        if (m < a.M) store_out(a, split, m, col, acc[e]);
+        for (int e = 0; e < 4; ++e) red[wave][lane * 4 + e] = acc[e];
+        __syncthreads();
+        const int m = t >> 4, nn = t & 15;
+        if (t < 256 && m < a.M) {
+            const int idx = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+            float s0 = 0.f;
+            for (int w = 0; w < nw; ++w) s0 += red[w][idx];
+            if (pair) {
+                if (n0 + nn < a.seg[0].N) {
+                    float s1 = 0.f;
+                    for (int w = nw; w < kSkWaves; ++w) s1 += red[w][idx];
+                    const float v = s0 / (1.f + __expf(-s0)) * s1;
+                    const size_t o = (size_t)m * a.ldo + n0 + nn;
+                    if (a.out_bf16) {
+                        uint32_t u = __float_as_uint(v);
+                        u += 0x7FFFu + ((u >> 16) & 1u);
+                        ((uint16_t*)a.out)[o] = (uint16_t)(u >> 16);
+                    } else {
+                        ((float*)a.out)[o] = v;
+                    }
+                }
+            } else if (n0 + nn < g.N) {
+                float* p = a.C + (size_t)m * a.ldc + g.c_col0 + n0 + nn;   // kPartial: split 0 of 1
+                *p = a.mode == kAccumulate ? *p + s0 : s0;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -134,7 +310,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
     do {                                                                                        \
         _Pragma("unroll") for (int i = 0; i < AL; ++i) {                                        \
             const int row_ = m0 + lrow + 32 * i;                                                \
-            const u32x4_t v_ = *(const u32x4_t*)(Ag + (size_t)min(row_, a.M - 1) * g.lda + (k) + lcol); \
+            const int ar_ = min(row_, a.M - 1);                                                 \
+            const u32x4_t v_ = *(const u32x4_t*)(Ag + (size_t)(a.a_rows ? a.a_rows[ar_] : ar_) * g.lda + (k) + lcol); \
             ra[i] = row_ < a.M ? v_ : zero;                                                     \
         }                                                                                       \
         _Pragma("unroll") for (int i = 0; i < BL; ++i) {                                        \
@@ -212,7 +389,7 @@ __global__ __launch_bounds__(64) void k_gemm_f32(GemmArgs a) {
     const GemmSeg g = a.seg[s];
     const int n = col - g.c_col0;
     if (n < 0 || n >= g.N) return;
-    const float* A = (const float*)g.A + (size_t)m * g.lda;
+    const float* A = (const float*)g.A + (size_t)(a.a_rows ? a.a_rows[m] : m) * g.lda;
     const float* B = (const float*)g.B + (size_t)n * g.ldb;
     float acc = 0.f;
     for (int k = 0; k < a.K; ++k) acc = fmaf(A[k], B[k], acc);
@@ -235,53 +412,147 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // launcher: tiles, split-K choice, reduce
 // ---------------------------------------------------------------------------
-hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag) {
+__global__ __launch_bounds__(256) void k_swiglu(const float* in, int32_t ld, int32_t I, void* out, int32_t ldo,
+                                                int32_t out_bf16, int32_t rows) {
+    const size_t total = (size_t)rows * I;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const int r = (int)(i / I), j = (int)(i % I);
+        const float gt = in[(size_t)r * ld + j];
+        const float up = in[(size_t)r * ld + I + j];
+        const float v = gt / (1.f + __expf(-gt)) * up;
+        const size_t o = (size_t)r * ldo + j;
+        if (out_bf16) {
+            uint32_t u = __float_as_uint(v);
+            u += 0x7FFFu + ((u >> 16) & 1u);
+            ((uint16_t*)out)[o] = (uint16_t)(u >> 16);
+        } else {
+            ((float*)out)[o] = v;
+        }
+    }
+}
+
+hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag,
+                int* splits_out) {
     if (a.M <= 0 || a.nseg <= 0) return hipSuccess;
+    a.accumulate = a.mode == kAccumulate;
     a.col_lo = a.seg[0].c_col0;
     a.col_hi = a.seg[a.nseg - 1].c_col0 + a.seg[a.nseg - 1].N;
+    const bool swiglu = a.mode == kSwiGLU;
+    const bool skinny = bf16 && a.M <= 16;
+    if (skinny) {
+        int ntiles = 0;
+        if (swiglu) {
+            ntiles = (a.seg[0].N + 15) / 16;
+            a.seg[0].tile0 = a.seg[1].tile0 = 0;
+        } else {
+            for (int s = 0; s < a.nseg; ++s) {
+                a.seg[s].tile0 = ntiles;
+                ntiles += (a.seg[s].N + 15) / 16;
+            }
+        }
+        a.ntiles = ntiles;
+        a.splits = 1;
+        a.kc = a.K;
+        // persistent form when every segment shares one A and each wave's k
+        // share fits in registers (4 or 8 steps of 64)
+        bool shared_a = true;
+        for (int s = 1; s < a.nseg; ++s) shared_a &= a.seg[s].A == a.seg[0].A && a.seg[s].lda == a.seg[0].lda;
+        const int nw = swiglu ? kSkWaves / 2 : kSkWaves;
+        const int steps = (a.K % (64 * nw)) ? 0 : a.K / (64 * nw);
+        const int grid = std::min(ntiles, 2 * num_cus);   // persistent grid
+        // (only when every workgroup gets at least two tiles; otherwise the
+        // per-tile kernel, with more workgroups in flight, is faster)
+        if (shared_a && (steps == 4 || steps == 8) && ntiles >= 2 * grid) {
+            if (splits_out) *splits_out = 1;
+            if (steps == 4) {
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1>), dim3(grid), dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0>), dim3(grid), dim3(512), 0, st, a);
+            } else {
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<8, 1>), dim3(grid), dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<8, 0>), dim3(grid), dim3(512), 0, st, a);
+            }
+            return hipGetLastError();
+        }
+        // two tiles per workgroup (shared A) when there are enough columns;
+        // kPartial: split K over workgroups until about two workgroups per CU,
+        // keeping at least two 64-wide k steps per wave
+        const int tpw = swiglu ? 2 : ((shared_a && ntiles >= num_cus) ? 2 : 1);
+        const int nwg = swiglu ? ntiles : (ntiles + tpw - 1) / tpw;
+        int splits = 1;
+        const int nsteps = a.K / 64;
+        while (a.mode == kPartial && nwg * splits * 2 <= 2 * num_cus && nsteps / (splits * 2 * kSkWaves) >= 2 &&
+               splits * 2 <= a.max_splits)
+            splits *= 2;
+        a.splits = splits;
+        if (splits_out) *splits_out = splits;
+        const dim3 grid2(nwg, splits);
+        if (tpw == 2) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<2, 1>), grid2, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_skinny<2, 0>), grid2, dim3(512), 0, st, a);
+        } else {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<1, 1>), grid2, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_skinny<1, 0>), grid2, dim3(512), 0, st, a);
+        }
+        return hipGetLastError();
+    }
+    // larger M (or fp32): plain GEMM into C, then the SwiGLU pass if asked;
+    // kPartial leaves the split partials [splits][M][ldc] in C
+    if (swiglu) a.accumulate = 0;
+    if (splits_out) *splits_out = 1;
+    hipError_t e = hipSuccess;
     if (!bf16) {
         a.splits = 1;
         a.kc = a.K;
+        a.accumulate = a.mode == kAccumulate;
         dim3 grid((a.col_hi - a.col_lo + 63) / 64, a.M);
         hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, st, a);
-        return hipGetLastError();
-    }
-    const bool skinny = a.M <= 16;
-    const int NT = skinny ? 64 : 128;
-    const int MT = skinny ? 16 : (a.M <= 64 ? 64 : 128);
-    int ntiles = 0;
-    for (int s = 0; s < a.nseg; ++s) {
-        a.seg[s].tile0 = ntiles;
-        ntiles += (a.seg[s].N + NT - 1) / NT;
-    }
-    a.ntiles = ntiles;
-    const int mtiles = (a.M + MT - 1) / MT;
-    const int base = ntiles * mtiles;
-    // enough workgroups for ~2 per CU; keep a split at >= 512 k-values
-    int splits = 1;
-    const int target = 2 * num_cus;
-    while (base * splits < target && a.K / (splits * 2) >= 512) splits *= 2;
-    while (splits > 1 && (size_t)splits * a.M * a.ldc > part_cap_floats) splits /= 2;
-    int kc = ((a.K + splits - 1) / splits + 63) / 64 * 64;
-    splits = (a.K + kc - 1) / kc;
-    a.splits = splits;
-    a.kc = kc;
-    const dim3 blk(256);
-    if (skinny) {
-        if (tag == 1) hipLaunchKernelGGL(k_gemm_skinny<1>, dim3(ntiles, splits), blk, 0, st, a);
-        else hipLaunchKernelGGL(k_gemm_skinny<0>, dim3(ntiles, splits), blk, 0, st, a);
-    } else if (MT == 64) {
-        if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
-        else hipLaunchKernelGGL((k_gemm_tiled<64, 0>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+        e = hipGetLastError();
     } else {
-        if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<128, 1>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
-        else hipLaunchKernelGGL((k_gemm_tiled<128, 0>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+        const int NT = 128;
+        const int MT = a.M <= 64 ? 64 : 128;
+        int ntiles = 0;
+        for (int s = 0; s < a.nseg; ++s) {
+            a.seg[s].tile0 = ntiles;
+            ntiles += (a.seg[s].N + NT - 1) / NT;
+        }
+        a.ntiles = ntiles;
+        const int mtiles = (a.M + MT - 1) / MT;
+        const int base = ntiles * mtiles;
+        // about one 256-thread tile per CU; keep a split at >= 512 k-values
+        int splits = 1;
+        while (base * splits < num_cus && a.K / (splits * 2) >= 512) splits *= 2;
+        const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
+        while (splits > 1 && ((size_t)splits * a.M * a.ldc > cap || splits > (a.mode == kPartial ? a.max_splits : 1 << 30)))
+            splits /= 2;
+        int kc = ((a.K + splits - 1) / splits + 63) / 64 * 64;
+        splits = (a.K + kc - 1) / kc;
+        a.splits = splits;
+        a.kc = kc;
+        if (a.mode == kPartial) {
+            a.part = a.C;            // the partial slices are the output
+            if (splits_out) *splits_out = splits;
+        }
+        const dim3 blk(256);
+        if (MT == 64) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_tiled<64, 0>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+        } else {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<128, 1>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_tiled<128, 0>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+        }
+        e = hipGetLastError();
+        if (e == hipSuccess && splits > 1 && a.mode != kPartial) {
+            const size_t total = (size_t)a.M * (a.col_hi - a.col_lo);
+            const int blocks = (int)std::min<size_t>((total + 255) / 256, (size_t)num_cus * 8);
+            hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, st, a);
+            e = hipGetLastError();
+        }
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    const size_t total = (size_t)a.M * (a.col_hi - a.col_lo);
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, (size_t)num_cus * 8);
-    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, st, a);
+    if (e != hipSuccess || !swiglu) return e;
+    const int I = a.seg[0].N;
+    const size_t total = (size_t)a.M * I;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_swiglu, dim3(blocks), dim3(256), 0, st, a.C, a.ldc, I, a.out, a.ldo, a.out_bf16, a.M);
     return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // Row-wise kernels of the drafter forward: RMSNorm, the per-head q/k norm +
-// RoPE + slot-indexed K/V cache writer, embedding gather, SwiGLU, descriptor
-// upload, row gather, cache readback, and the batched sampler.
+// RoPE + slot-indexed K/V cache writer, embedding gather, descriptor upload,
+// row gather, cache readback, and the batched sampler.
 #include <cmath>
 
 #include "kernels.h"
@@ -44,101 +44,112 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 
 // ---------------------------------------------------------------------------
 // RMSNorm: y = x / sqrt(mean(x^2) + eps) * gain, per row and per group of
-// width/groups columns; one input, up to kMaxOut (gain, output) pairs.
+// width/groups columns; one input, up to kMaxOut (gain, output) pairs.  x may
+// be the sum of a residual row and K-slices of a GEMM (then written back).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
+__global__ __launch_bounds__(512) void k_rmsnorm(NormArgs a) {
     __shared__ float sh[8];
+    __shared__ float xs[kNormMaxW];
     const int orow = blockIdx.x, grp = blockIdx.y;
     const int irow = a.row_src ? a.row_src[orow] : orow;
     const int W = a.width / a.groups;
     const size_t ibase = (size_t)irow * a.in_stride + (size_t)grp * W;
+    // gather x (residual + slices) into LDS: every load is independent of the
+    // stores, which come after the reduction
     float ss = 0.f;
-    for (int i = threadIdx.x; i < W; i += 256) {
-        const float x = ld_any(a.in, ibase + i, a.in_bf16);
+    for (int i = threadIdx.x; i < W; i += 512) {
+        float x = a.in ? ld_any(a.in, ibase + i, a.in_bf16) : 0.f;
+        const float* __restrict__ p = a.part + ibase + i;
+        for (int sp = 0; sp < a.nsplit; ++sp) x += p[(size_t)sp * a.part_stride];
+        xs[i] = x;
         ss += x * x;
     }
     ss = block_sum(ss, sh);
     const float rstd = 1.f / sqrtf(ss / (float)W + a.eps);
+    if (a.writeback)
+        for (int i = threadIdx.x; i < W; i += 512) a.writeback[ibase + i] = xs[i];
     const size_t obase = (size_t)orow * a.out_stride + (size_t)grp * W;
     const size_t gbase = (size_t)grp * a.gain_group_stride;
     for (int o = 0; o < a.nout; ++o)
-        for (int i = threadIdx.x; i < W; i += 256) {
-            const float x = ld_any(a.in, ibase + i, a.in_bf16);
+        for (int i = threadIdx.x; i < W; i += 512) {
             const float gn = ld_any(a.gain[o], gbase + i, a.gain_bf16);
-            st_any(a.out[o], obase + i, x * rstd * gn, a.out_bf16);
+            st_any(a.out[o], obase + i, xs[i] * rstd * gn, a.out_bf16);
         }
 }
 
 hipError_t rmsnorm(const NormArgs& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_rmsnorm, dim3(a.rows, a.groups), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_rmsnorm, dim3(a.rows, a.groups), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Per-head finish of a projection row: q and k get RMSNorm over the head and
-// rotate-half RoPE at the row's position (angles in fp64, then fp32); q goes
-// to the query buffer, k and v to the session's cache at the row's slot.
-// One workgroup per (row, layer); wave w takes heads w, w+4, ...
+// rotate-half RoPE at the row's position (angle pos * theta^(-2d/D) in fp64,
+// cos/sin rounded to fp32); q goes to the query buffer, k and v to the
+// session's cache at the row's slot.  Grid (row, task group, layer); each
+// wave finishes one head (tasks: q heads, then k heads, then v heads).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
-    const int row = blockIdx.x, li = blockIdx.y;
+    const int row = blockIdx.x, li = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nq = (a.q_col >= 0) ? a.Hq : 0;
+    const int task = blockIdx.y * 4 + wave;
+    if (task >= nq + 2 * a.Hkv) return;
     const RowInfo ri = a.rows[row];
     const SeqDesc sd = a.seqs[ri.seq];
     const int pos = ri.pos;
     const int slot = sd.ring ? pos % sd.cap : pos;
     const int half = a.D >> 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool act = lane < half;
-    float cs = 1.f, sn = 0.f;
-    if (act) {
-        const double inv = pow((double)a.theta, -2.0 * (double)lane / (double)a.D);
-        const double ang = (double)pos * inv;
-        cs = (float)cos(ang);
-        sn = (float)sin(ang);
-    }
     const int layer = a.layer[li];
-    const int nq = (a.q_col >= 0) ? a.Hq : 0;
-    const int ntask = nq + 2 * a.Hkv;
+    int kind, head, col;   // kind 0 q, 1 k, 2 v
+    if (task < nq) { kind = 0; head = task; col = a.q_col + head * a.D; }
+    else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * a.D; }
+    else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * a.D; }
     const float* src = a.src + (size_t)row * a.ld;
-    for (int task = wave; task < ntask; task += 4) {
-        int kind, head, col;   // kind 0 q, 1 k, 2 v
-        if (task < nq) { kind = 0; head = task; col = a.q_col + head * a.D; }
-        else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * a.D; }
-        else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * a.D; }
-        float x1 = act ? src[col + lane] : 0.f;
-        float x2 = act ? src[col + lane + half] : 0.f;
-        if (kind != 2) {
-            if (a.qk_norm) {
-                const float ss = wave_sum(x1 * x1 + x2 * x2);
-                const float rstd = 1.f / sqrtf(ss / (float)a.D + a.eps);
-                const void* gn = kind == 0 ? a.q_norm : a.k_norm[li];
-                if (act) {
-                    x1 = x1 * rstd * ld_any(gn, lane, a.w_bf16);
-                    x2 = x2 * rstd * ld_any(gn, lane + half, a.w_bf16);
-                }
+    float x1 = 0.f, x2 = 0.f;
+    if (act)
+        for (int sp = 0; sp < a.nsplit; ++sp) {
+            x1 += src[(size_t)sp * a.src_stride + col + lane];
+            x2 += src[(size_t)sp * a.src_stride + col + lane + half];
+        }
+    if (kind != 2) {
+        if (a.qk_norm) {
+            const float ss = wave_sum(x1 * x1 + x2 * x2);
+            const float rstd = 1.f / sqrtf(ss / (float)a.D + a.eps);
+            const void* gn = kind == 0 ? a.q_norm : a.k_norm[li];
+            if (act) {
+                x1 = x1 * rstd * ld_any(gn, lane, a.w_bf16);
+                x2 = x2 * rstd * ld_any(gn, lane + half, a.w_bf16);
             }
+        }
+        if (act) {
+            double sd_, cd_;
+            sincos((double)pos * a.inv_freq[lane], &sd_, &cd_);
+            const float cs = (float)cd_, sn = (float)sd_;
             const float y1 = x1 * cs - x2 * sn;
             const float y2 = x2 * cs + x1 * sn;
             x1 = y1;
             x2 = y2;
         }
-        if (!act) continue;
-        if (kind == 0) {
-            const size_t o = ((size_t)row * a.Hq + head) * a.D;
-            st_any(a.q_out, o + lane, x1, a.q_bf16);
-            st_any(a.q_out, o + lane + half, x2, a.q_bf16);
-        } else {
-            const size_t o = ((((size_t)layer * 2 + (kind - 1)) * a.Hkv + head) * sd.cap + slot) * a.D;
-            st_any(sd.cache, o + lane, x1, a.cache_bf16);
-            st_any(sd.cache, o + lane + half, x2, a.cache_bf16);
-        }
+    }
+    if (!act) return;
+    if (kind == 0) {
+        const size_t o = ((size_t)row * a.Hq + head) * a.D;
+        st_any(a.q_out, o + lane, x1, a.q_bf16);
+        st_any(a.q_out, o + lane + half, x2, a.q_bf16);
+    } else {
+        const size_t o = ((((size_t)layer * 2 + (kind - 1)) * a.Hkv + head) * sd.cap + slot) * a.D;
+        st_any(sd.cache, o + lane, x1, a.cache_bf16);
+        st_any(sd.cache, o + lane + half, x2, a.cache_bf16);
     }
 }
 
 hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st) {
     if (a.nrows <= 0 || nlayer <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_head_finish, dim3(a.nrows, nlayer), dim3(256), 0, st, a);
+    const int ntask = (a.q_col >= 0 ? a.Hq : 0) + 2 * a.Hkv;
+    hipLaunchKernelGGL(k_head_finish, dim3(a.nrows, (ntask + 3) / 4, nlayer), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -158,29 +169,6 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
 hipError_t embed(const EmbedArgs& a, hipStream_t st) {
     if (a.nrows <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_embed, dim3(a.nrows), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// SwiGLU: out = silu(gate) * up, gate and up side by side in one row.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_silu_mul(const float* in, int32_t ld, int32_t I, void* out,
-                                                  int32_t out_bf16, int32_t rows) {
-    const size_t total = (size_t)rows * I;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
-        const int r = (int)(i / I), j = (int)(i % I);
-        const float gt = in[(size_t)r * ld + j];
-        const float up = in[(size_t)r * ld + I + j];
-        st_any(out, i, gt / (1.f + expf(-gt)) * up, out_bf16);
-    }
-}
-
-hipError_t silu_mul(const float* in, int32_t ld, int32_t I, void* out, int32_t out_bf16, int32_t rows,
-                    hipStream_t st) {
-    if (rows <= 0) return hipSuccess;
-    const size_t total = (size_t)rows * I;
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, 2048);
-    hipLaunchKernelGGL(k_silu_mul, dim3(blocks), dim3(256), 0, st, in, ld, I, out, out_bf16, rows);
     return hipGetLastError();
 }
 

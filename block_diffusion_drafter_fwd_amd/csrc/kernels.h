@@ -45,20 +45,38 @@ struct GemmSeg {
     int32_t lda, ldb, N, c_col0, tile0, pad;
 };
 
+// epilogues: C = acc, C += acc, out = silu(acc of segment 0) * (acc of
+// segment 1) for the paired gate|up projection, or kPartial: K is split over
+// workgroups and split s writes its share to C + s * M * ldc (at most
+// max_splits slices); the consumer of C adds the slices
+enum GemmMode { kStore = 0, kAccumulate = 1, kSwiGLU = 2, kPartial = 3 };
+
 struct GemmArgs {
     int32_t M, K, kc, splits;
     float* C;
     int32_t ldc, accumulate;
+    int32_t mode, ldo;
+    void* out;                // kSwiGLU output [M, ldo]
+    int32_t out_bf16, max_splits;
+    const int32_t* a_rows;    // optional: A row of output row m (all segments)
     float* part;              // split-K partials [splits][M][ldc]
     int32_t nseg, ntiles;
     int32_t col_lo, col_hi;   // columns covered by the segments
     GemmSeg seg[kMaxSeg];
 };
 
+// y = RMSNorm(x) * gain with x = in[row] (optional) + sum of nsplit fp32
+// slices part[s * part_stride + row * in_stride]; x is written back to
+// `writeback` when given (fused residual add).  Rows are at most kNormMaxW wide.
+constexpr int kNormMaxW = 8192;
 struct NormArgs {
     const void* in;
-    int64_t in_stride;        // elements between rows
+    int64_t in_stride;        // elements between rows (of in, part and writeback)
     const int32_t* row_src;   // optional: input row of each output row
+    const float* part;
+    int64_t part_stride;
+    float* writeback;
+    int32_t nsplit, pad;
     int32_t in_bf16, rows, width, groups;
     float eps;
     int32_t gain_bf16, nout, out_bf16;
@@ -69,7 +87,7 @@ struct NormArgs {
 };
 
 struct HeadArgs {
-    const float* src;         // projection output rows
+    const float* src;         // projection output rows: nsplit slices of src_stride floats, summed
     const RowInfo* rows;
     const SeqDesc* seqs;
     void* q_out;              // [rows][Hq][D]
@@ -79,7 +97,10 @@ struct HeadArgs {
     int32_t q_col;            // -1: no q heads in this launch
     int32_t k_col[kMaxL], v_col[kMaxL], layer[kMaxL];
     int32_t qk_norm, w_bf16, cache_bf16, q_bf16;
-    float eps, theta;
+    int32_t nsplit, pad;
+    int64_t src_stride;
+    float eps;
+    double inv_freq[64];      // theta^(-2d/D), d < D/2, computed on the host in fp64
 };
 
 struct EmbedArgs {
@@ -96,10 +117,12 @@ struct AttnArgs {
     const RowInfo* rows;
     float* part_o;            // [items][Hkv][64][D]
     float* part_ml;           // [items][Hkv][64][2]
-    const float* gate_src;    // projection rows holding the g columns
+    const float* gate_src;    // projection rows holding the g columns (gate_nsplit slices, summed)
     void* out;                // [rows][Hq*D]
     int32_t nseq, nrows, layer, L, Hq, Hkv, D, causal, window, chunk, total_items;
     int32_t gate, gate_ld, gate_col, out_bf16;
+    int32_t gate_nsplit, pad;
+    int64_t gate_stride;
     float scale;
 };
 
@@ -124,12 +147,12 @@ struct UploadArgs {
 // launchers (return hipError_t of the launch)
 // tag 1 launches a separate instantiation (the unembedding) so that profilers
 // can tell it apart from the per-layer GEMMs
-hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag = 0);
+// splits_out (optional) receives the number of K slices written in kPartial mode
+hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag = 0,
+                int* splits_out = nullptr);
 hipError_t rmsnorm(const NormArgs& a, hipStream_t st);
 hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st);
 hipError_t embed(const EmbedArgs& a, hipStream_t st);
-hipError_t silu_mul(const float* in, int32_t ld, int32_t I, void* out, int32_t out_bf16, int32_t rows,
-                    hipStream_t st);
 hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st);
 hipError_t sample(const SampleArgs& a, hipStream_t st);
 hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st);

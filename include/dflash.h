@@ -66,7 +66,8 @@ typedef struct dflash_session dflash_session;
  * the sliding window (0 = dense context); flush_rows is the pending bound
  * (256 in dflash.go).  Bounds checked by dflash_create (E_CONFIG):
  * block_size in [2, 512]; window 0 or in [2, 2^20]; attention_bias must be 0;
- * q_heads a multiple of kv_heads; bf16 needs head_dim 128 and hidden,
+ * q_heads a multiple of kv_heads; hidden, target_hidden <= 8192; at most 16
+ * layers; (q_heads/kv_heads) * block_size <= 64; bf16 needs head_dim 128 and hidden,
  * intermediate, target_hidden, q_heads*head_dim multiples of 64; fp32 needs
  * head_dim <= 64 and even. */
 typedef struct {
