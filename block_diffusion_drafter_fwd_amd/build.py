@@ -25,6 +25,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators in ordinary VGPRs: no copies through AGPRs
+             # where an accumulator is rescaled between products
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 

@@ -96,8 +96,10 @@ public:
         return w;
     }
 
-    // attention work items per call: about four workgroups per CU over all kv heads
-    int32_t attn_target_wg() const { return 4 * cus_; }
+    // attention work items per call: two workgroups per CU over all kv heads,
+    // the number that are resident together (64 KiB of LDS each), so the
+    // whole split runs as one round
+    int32_t attn_target_wg() const { return 2 * cus_; }
 
     int32_t qkv_ld() const { return m_.qd + 2 * m_.kd + (m_.cfg.gate ? m_.cfg.q_heads : 0); }
 

@@ -7,14 +7,19 @@
 // h / (Hq / Hkv).
 //
 // bf16 path (flash-decoding split over the context):
-//   k_attn_partial  one workgroup per (context chunk, kv head).  The G q heads
-//                   of that kv head times M block rows form up to 64 query rows
-//                   (4 waves x 16).  Per 64-key tile: K and V^T staged in LDS,
-//                   S^T = K . Q^T with v_mfma_f32_16x16x32_bf16 (its output
-//                   layout holds, per lane, the 4 keys the next product's B
-//                   operand needs; two key tiles fill one k = 32 step),
-//                   online softmax in fp32, O^T += V^T . P^T.
-//                   Writes unnormalised O with its running max and sum.
+//   k_attn_partial  one workgroup (4 waves) per (context chunk, kv head).  The
+//                   G q heads of that kv head times M block rows form up to 64
+//                   query rows, 16 per wave.  64-key tiles of K and V are
+//                   copied from the cache straight into LDS (global_load_lds,
+//                   double-buffered one tile ahead) with their 16-byte pieces
+//                   XOR-permuted per key; S^T = K . Q^T with
+//                   v_mfma_f32_16x16x32_bf16 (its output layout holds, per
+//                   lane, the 4 keys the next product's B operand needs; two
+//                   key tiles fill one k = 32 step); online softmax in fp32 on
+//                   the base-2 exponential; O^T += V^T . P^T with the V^T
+//                   operand read from the row-major tile by the transposing
+//                   LDS read (ds_read_b64_tr_b16).  Writes unnormalised O with
+//                   its running max and sum.
 //   k_attn_combine  merges the chunks of each (row, q head) with weights
 //                   staged in LDS, applies the per-head sigmoid gate.
 // fp32 path (tiny configurations): k_attn_f32, one workgroup per (row, head).
@@ -33,6 +38,14 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// two floats to packed bf16 (round to nearest even, one conversion instruction)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ int find_item_seq(const SeqDesc* seqs, int nseq, int item) {
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {                       // last seq with item0 <= item
@@ -42,14 +55,13 @@ __device__ __forceinline__ int find_item_seq(const SeqDesc* seqs, int nseq, int 
     return lo;
 }
 
+// (bitwise, not short-circuit: keeps the masking branch-free)
 __device__ __forceinline__ bool visible(int s, int p, int kend, int causal, int window) {
-    return s < kend && (!causal || s <= p) && (!window || p - s < window);
+    return (s < kend) & ((causal == 0) | (s <= p)) & ((window == 0) | (p - s < window));
 }
 
 constexpr int kKT = 64;                 // keys per tile
 constexpr int kD = 128;                 // head dim of the bf16 path
-constexpr int kKLD = kD + 8;            // LDS row stride of K (elements)
-constexpr int kVLD = kKT + 8;           // LDS row stride of V^T
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
@@ -59,14 +71,33 @@ __device__ __forceinline__ f32x4_t mfma32(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    c, 0, 0, 0);
 }
 
-// V^T is stored with its 4-key groups XOR-swizzled by the row's 8-row band,
-// which makes the transposing stores conflict-free and keeps every 4-key group
-// contiguous (8-byte aligned) for the fragment reads.
-__device__ __forceinline__ int vt_index(int d, int key) { return d * kVLD + (key ^ (((d >> 3) & 15) << 2)); }
+constexpr int kAttnWaves = 4;               // waves per workgroup
+constexpr int kRG = 4 / kAttnWaves;         // 16-row groups per wave (64 query rows per workgroup)
+constexpr int kAttnThreads = 64 * kAttnWaves;
 
-__global__ __launch_bounds__(256) void k_attn_partial(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * kKLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * kVLD];
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+// K and V tiles sit in LDS row-major (64 keys x 256 bytes), with the 16-byte
+// pieces of each row XOR-permuted by the key so that the fragment reads hit
+// distinct banks: K reads take 16 keys of one piece, V reads (transposing,
+// ds_read_b64_tr_b16) take 8 keys of two adjacent pieces.
+__device__ __forceinline__ int k_piece(int key, int c) { return key * 16 + (c ^ (key & 15)); }
+__device__ __forceinline__ int v_piece(int key, int c) { return key * 16 + (c ^ ((key & 7) << 1)); }
+
+// The waves share each 64-key tile; each owns kRG 16-row groups of the 64
+// query rows (every K and V fragment read from LDS feeds kRG MFMAs).  Tiles
+// are copied from the cache straight into LDS (global_load_lds, no registers)
+// one tile ahead, into a second buffer; V^T fragments come from the
+// row-major V tile through the transposing LDS read.
+__global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
+    // two buffers per operand, as separate objects: the copy into one must be
+    // seen by the compiler as independent of the reads from the other, or it
+    // waits for the copy before every read
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[kKT * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[kKT * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[kKT * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[kKT * kD];
 
     const int item = blockIdx.x, g = blockIdx.y;
     const SeqDesc sd = a.seqs[find_item_seq(a.seqs, a.nseq, item)];
@@ -76,134 +107,183 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnArgs a) {
     const int ke = min(kend, kb + a.chunk);
     const int G = a.Hq / a.Hkv;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 15, q = lane >> 4;
-    const int row = wave * 16 + r;
-    const bool rvalid = row < sd.M * G;
-    const int qi = rvalid ? row / G : 0;
-    const int hq = g * G + (rvalid ? row % G : 0);
-    const int p = sd.F + qi;
     const int p_last = sd.F + sd.M - 1;
 
-    // Q^T as the B operand of S^T = K Q^T: lane (r, q) holds Q[row r][32 j + 8 q .. +8]
-    u32x4_t qf[4];
-    {
+    // per row group: query row, validity, position; Q^T as the B operand of
+    // S^T = K Q^T: lane (r, q) holds Q[row][32 j + 8 q .. +8]
+    int row[kRG], pos[kRG];
+    bool rvalid[kRG];
+    u32x4_t qf[kRG][4];
+#pragma unroll
+    for (int gi = 0; gi < kRG; ++gi) {
+        row[gi] = (wave * kRG + gi) * 16 + r;
+        rvalid[gi] = row[gi] < sd.M * G;
+        const int qi = rvalid[gi] ? row[gi] / G : 0;
+        const int hq = g * G + (rvalid[gi] ? row[gi] % G : 0);
+        pos[gi] = sd.F + qi;
         const uint16_t* Qp = (const uint16_t*)a.Q + ((size_t)(sd.q_row0 + qi) * a.Hq + hq) * kD;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            qf[j] = rvalid ? *(const u32x4_t*)(Qp + j * 32 + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int j = 0; j < 4; ++j) {
+            const u32x4_t v = *(const u32x4_t*)(Qp + j * 32 + 8 * q);   // row qi is in range either way
+            qf[gi][j] = rvalid[gi] ? v : u32x4_t{0u, 0u, 0u, 0u};
+        }
     }
     const size_t headsz = (size_t)sd.cap * kD;
     const uint16_t* Kc = (const uint16_t*)sd.cache + ((size_t)(a.layer * 2 + 0) * a.Hkv + g) * headsz;
     const uint16_t* Vc = (const uint16_t*)sd.cache + ((size_t)(a.layer * 2 + 1) * a.Hkv + g) * headsz;
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4_t o[8];
+    float m_run[kRG], l_run[kRG];   // raw-score max, running sum
 #pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // 64-key tiles: the next tile's K and V are loaded into registers while
-    // the current one is multiplied out of LDS
-    uint4 kreg[4], vreg[4];
-#define DF_ATTN_LOAD(T0)                                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                             \
-        const int idx_ = t + 256 * i;                                           \
-        const int kp_ = (T0) + (idx_ >> 4), dc_ = (idx_ & 15) * 8;               \
-        kreg[i] = uint4{0u, 0u, 0u, 0u};                                        \
-        vreg[i] = uint4{0u, 0u, 0u, 0u};                                        \
-        if (kp_ < ke) {                                                         \
-            const int slot_ = sd.ring ? kp_ % sd.cap : kp_;                     \
-            kreg[i] = *(const uint4*)(Kc + (size_t)slot_ * kD + dc_);           \
-            vreg[i] = *(const uint4*)(Vc + (size_t)slot_ * kD + dc_);           \
-        }                                                                       \
+    for (int gi = 0; gi < kRG; ++gi) {
+        m_run[gi] = -INFINITY;
+        l_run[gi] = 0.f;
     }
-    DF_ATTN_LOAD(kb)
-    for (int t0 = kb; t0 < ke; t0 += kKT) {
+    const float c2 = a.scale * 1.4426950408889634f;
+    f32x4_t o[kRG][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = t + 256 * i;
-            const int key = idx >> 4, dc = (idx & 15) * 8;
-            *(uint4*)&sK[key * kKLD + dc] = kreg[i];
-            const uint16_t* ve = (const uint16_t*)&vreg[i];
+    for (int gi = 0; gi < kRG; ++gi)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sVt[vt_index(dc + e, key)] = ve[e];
-        }
-        __syncthreads();
-        if (t0 + kKT < ke) {
-            DF_ATTN_LOAD(t0 + kKT)
-        }
+        for (int d = 0; d < 8; ++d) o[gi][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // S^T[key][row] for 4 key tiles of 16 (4 MFMAs of k = 32 over D)
-        f32x4_t s[4];
+    // tile copy: instruction i of this wave fills LDS pieces (8 wave + i) * 64
+    // + lane, i.e. key 4 (8 wave + i) + lane / 16, position lane % 16, with the
+    // piece the XOR permutation puts there.  Keys past the chunk end copy the
+    // chunk's last key (masked below, probability zero).
+    auto load_tile = [&](int t0, uint16_t* dK, uint16_t* dV) {
+#pragma unroll
+        for (int i = 0; i < 16 / kAttnWaves; ++i) {
+            const int b = wave * (16 / kAttnWaves) + i;
+            const int key = 4 * b + (lane >> 4), cpos = lane & 15;
+            const int kk = min(t0 + key, ke - 1);
+            const int slot = sd.ring ? kk % sd.cap : kk;
+            const uint16_t* krow = Kc + (size_t)slot * kD;
+            const uint16_t* vrow = Vc + (size_t)slot * kD;
+            __builtin_amdgcn_global_load_lds(krow + 8 * (cpos ^ (key & 15)), (lds_void_t*)&dK[b * 512], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vrow + 8 * (cpos ^ ((key & 7) << 1)), (lds_void_t*)&dV[b * 512], 16, 0, 0);
+        }
+    };
+    auto tile = [&](int t0, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's copies of the tile landed
+        __syncthreads();                                    // everyone's have; the other buffer is free
+        if (t0 + kKT < ke) load_tile(t0 + kKT, nK, nV);
+
+        // S^T[key][row] for 4 key tiles of 16 (4 MFMAs of k = 32 over D) per row group
+        f32x4_t s[kRG][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int gi = 0; gi < kRG; ++gi) s[gi][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const u32x4_t kf = *(const u32x4_t*)&sK[(kt * 16 + r) * kKLD + j * 32 + 8 * q];
-                s[kt] = mfma32(kf, qf[j], s[kt]);
+                const u32x4_t kf = *(const u32x4_t*)&tK[8 * k_piece(kt * 16 + r, 4 * j + q)];
+#pragma unroll
+                for (int gi = 0; gi < kRG; ++gi) s[gi][kt] = mfma32(kf, qf[gi][j], s[gi][kt]);
             }
         }
-        // scale and mask; a tile every row sees whole (all context, inside
-        // every row's window) skips the per-element test
+        // mask; a tile every row sees whole (all context, inside every row's
+        // window) skips the per-element test (the branch is uniform)
         const bool full = t0 + kKT <= ke && t0 + kKT <= sd.F && (!a.window || p_last - t0 < a.window);
-        float mx = -INFINITY;
+        if (!full) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+            for (int gi = 0; gi < kRG; ++gi)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kp = t0 + kt * 16 + 4 * q + e;
-                const bool ok = full || (rvalid && visible(kp, p, ke, a.causal, a.window));
-                s[kt][e] = ok ? s[kt][e] * a.scale : -INFINITY;
-                mx = fmaxf(mx, s[kt][e]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
-        float sum = 0.f;
-        uint2 pf[4];
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            float pe[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pe[e] = s[kt][e] == -INFINITY ? 0.f : __expf(s[kt][e] - m_new);
-                sum += pe[e];
-            }
-            pf[kt].x = (uint32_t)f2bf(pe[0]) | ((uint32_t)f2bf(pe[1]) << 16);
-            pf[kt].y = (uint32_t)f2bf(pe[2]) | ((uint32_t)f2bf(pe[3]) << 16);
+                    for (int e = 0; e < 4; ++e) {
+                        const int kp = t0 + kt * 16 + 4 * q + e;
+                        s[gi][kt][e] = (rvalid[gi] & visible(kp, pos[gi], ke, a.causal, a.window)) ? s[gi][kt][e]
+                                                                                                   : -INFINITY;
+                    }
         }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        l_run = l_run * alpha + sum;
-        m_run = m_new;
-        // O^T[d][row] = alpha * O^T + V^T . P^T, k = 32 per MFMA: element e of
-        // lane q stands for key 4q + e of tile 2h (e < 4) or tile 2h + 1 (e >= 4),
-        // for both operands
+        // online softmax on the raw scores in base 2: p = 2^(c s - c m) with
+        // c = scale * log2(e), i.e. exp(scale s - scale m)
+        uint2 pf[kRG][4];
+        float alpha[kRG];
+        bool rescale = false;
+#pragma unroll
+        for (int gi = 0; gi < kRG; ++gi) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                mx = fmaxf(fmaxf(mx, fmaxf(s[gi][kt][0], s[gi][kt][1])), fmaxf(s[gi][kt][2], s[gi][kt][3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[gi], mx);
+            alpha[gi] = m_run[gi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[gi] - m_new) * c2);
+            const float mc = m_new == -INFINITY ? 0.f : m_new * c2;   // a row with nothing visible yet: p = 0
+            float sum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                float pe[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pe[e] = __builtin_amdgcn_exp2f(fmaf(s[gi][kt][e], c2, -mc));   // masked (-inf) scores give 0
+                    sum += pe[e];
+                }
+                pf[gi][kt].x = pack_bf16(pe[0], pe[1]);
+                pf[gi][kt].y = pack_bf16(pe[2], pe[3]);
+            }
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            l_run[gi] = l_run[gi] * alpha[gi] + sum;
+            m_run[gi] = m_new;
+            rescale |= alpha[gi] != 1.f;
+        }
+        // the accumulators are still zero on the chunk's first tile, and a
+        // wave whose rows all kept their maximum needs no rescale
+        if (t0 != kb && __any(rescale)) {
+#pragma unroll
+            for (int gi = 0; gi < kRG; ++gi)
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[gi][dt] *= alpha[gi];
+        }
+        // O^T[d][row] += V^T . P^T, k = 32 per MFMA: element e of lane q
+        // stands for key 4q + e of tile 2h (e < 4) or tile 2h + 1 (e >= 4),
+        // for both operands.  Transposing read: lane r of group q points at
+        // 4 dims (4 (r % 4) ..) of key 4q + r / 4 and receives the 4 keys of
+        // dim r.
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            o[dt] *= alpha;
-            const int d = dt * 16 + r;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                const uint2 v0 = *(const uint2*)&sVt[vt_index(d, (2 * h2) * 16 + 4 * q)];
-                const uint2 v1 = *(const uint2*)&sVt[vt_index(d, (2 * h2 + 1) * 16 + 4 * q)];
-                const u32x4_t vf = {v0.x, v0.y, v1.x, v1.y};
-                const u32x4_t pp = {pf[2 * h2].x, pf[2 * h2].y, pf[2 * h2 + 1].x, pf[2 * h2 + 1].y};
-                o[dt] = mfma32(vf, pp, o[dt]);
+                u32x4_t vf;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int key = (2 * h2 + hh) * 16 + 4 * q + (r >> 2);
+                    const int d = dt * 16 + 4 * (r & 3);
+                    const uint16_t* src = &tV[8 * v_piece(key, d >> 3) + (d & 7)];
+                    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(src));
+                    const uint2 u = __builtin_bit_cast(uint2, v);
+                    vf[2 * hh] = u.x;
+                    vf[2 * hh + 1] = u.y;
+                }
+#pragma unroll
+                for (int gi = 0; gi < kRG; ++gi) {
+                    const u32x4_t pp = {pf[gi][2 * h2].x, pf[gi][2 * h2].y, pf[gi][2 * h2 + 1].x,
+                                        pf[gi][2 * h2 + 1].y};
+                    o[gi][dt] = mfma32(vf, pp, o[gi][dt]);
+                }
             }
         }
-        __syncthreads();
+    };
+    load_tile(kb, sK0, sV0);
+    for (int t0 = kb; t0 < ke; t0 += 2 * kKT) {
+        tile(t0, sK0, sV0, sK1, sV1);
+        if (t0 + kKT < ke) tile(t0 + kKT, sK1, sV1, sK0, sV0);
     }
-#undef DF_ATTN_LOAD
-    if (!rvalid) return;
-    const size_t base = ((size_t)item * a.Hkv + g) * 64 + row;
-    float* po = a.part_o + base * kD;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-        *(float4*)(po + dt * 16 + 4 * q) = float4{o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
-    if (q == 0) {
-        a.part_ml[base * 2] = m_run;
-        a.part_ml[base * 2 + 1] = l_run;
+    for (int gi = 0; gi < kRG; ++gi) {
+        if (!rvalid[gi]) continue;
+        const size_t base = ((size_t)item * a.Hkv + g) * 64 + row[gi];
+        float* po = a.part_o + base * kD;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            *(float4*)(po + dt * 16 + 4 * q) = float4{o[gi][dt][0], o[gi][dt][1], o[gi][dt][2], o[gi][dt][3]};
+        if (q == 0) {
+            a.part_ml[base * 2] = m_run[gi] * a.scale;   // the combine works in natural-log units
+            a.part_ml[base * 2 + 1] = l_run[gi];
+        }
     }
 }
 
@@ -333,7 +413,7 @@ hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st) {
         hipLaunchKernelGGL(k_attn_f32, dim3(a.nrows, a.Hq), dim3(64), 0, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items, a.Hkv), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items, a.Hkv), dim3(kAttnThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, a.Hq), dim3(kD), 0, st, a);
