@@ -1,26 +1,37 @@
 """Throughput of the DFlash drafter forward on one MI355X.
 
-Workload (default): the Qwen3.5-style bf16 drafter (hidden 2048, 5 layers,
-32 q / 8 kv heads x 128, fc 10240 -> 2048, vocab 151936, blockSize 16), seeded
-N(0, 0.02) weights with unit norm gains, N(0, 1) tap features, a 4096-slot
-context written by 256-row flushes, then drafting rounds at n = 15.
+Workload (default, ``--config qwen``): the Qwen3.5-style bf16 drafter (hidden
+2048, 5 layers, 32 q / 8 kv heads x 128, fc 10240 -> 2048, vocab 151936,
+blockSize 16), seeded N(0, 0.02) weights with unit norm gains, N(0, 1) tap
+features, a 4096-slot context written by 256-row flushes, then drafting
+rounds at n = 15.
 
 A step is one round of the whole hot path: rewind the outstanding block,
-commit the accepted run (anchor + a drafted rows, a ~ U{0..15}; its feature
+commit the accepted run (anchor + a drafted rows, a ~ U{0..n}; its feature
 rows ride in the next propose's context pass), propose (pending rows ->
-context K/V; anchor + 15 mask rows through every layer; rows 1..15
-unembedded) and greedily sample the 15 rows.  value = drafted blocks/s.
-The prompt phase is timed separately and reported as flushed context rows/s.
-All inputs (weights, every feature row of the run, tokens, accept lengths)
-are resident on the device or host before the timed region.
+context K/V; anchor + n mask rows through every layer; rows 1..n
+unembedded) and sample the rows.  value = drafted blocks/s (for the batched
+workload one block per session per batched call).  The prompt phase is timed
+separately and reported as flushed context rows/s.  All inputs (weights,
+feature rows, tokens, accept lengths) are resident on the device or host
+before the timed region.
 
-The JSON line also carries the roofline of the dominant kernel (the lm_head
-GEMM, timed with HIP events on its stream inside the timed region) and the CPU
-oracle's rate on a bounded sample of the same workload.
+Other workloads (``--config``): laguna (windowed, fused QKV, gate; 32768-slot
+prompt of which 511 stay), long (hidden 4096, vocab 262144, 131072-slot
+context, T = 1 with probabilities returned), batched (64 sessions with
+log-uniform 1k..16k contexts, U{1..15} rows each, T = 0.7, repetition
+penalty 1.1).  Their feature rows repeat with a period of 4096 slots (values
+do not change the work).
+
+The JSON line carries the roofline of the dominant kernel, timed with HIP
+events on its stream inside the timed region, per-stage rooflines from the
+same hooks (``kernels``), and the CPU oracle's rate on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -31,7 +42,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
 PMC_FILE = os.path.join(ROOT, "profiles", "unembed_qwen_pmc.json")
+POOL_ROWS = 4096
 
 
 def kernel_source_hash() -> str:
@@ -42,15 +55,48 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None, help="timed rounds (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="qwen", choices=["qwen", "laguna", "long", "tiny"])
+    ap.add_argument("--config", default="qwen", choices=["qwen", "laguna", "long", "batched", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512, help="context rows of the oracle sample")
-    ap.add_argument("--stages", action="store_true", help="also time every profiled stage (extra passes)")
+    ap.add_argument("--stages", action="store_true", help="also time the attention, sampler and flush stages")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (PMC byte-counter calibration)")
     return ap.parse_args()
+
+
+class Stage:
+    """Events-based timing of one engine stage (dflash_profile_begin/end)."""
+
+    def __init__(self, lib, ctx):
+        self.lib, self.ctx = lib, ctx
+
+    def begin(self, name):
+        from block_diffusion_drafter_fwd_amd.abi import check
+        check(self.lib, self.lib.dflash_profile_begin(self.ctx, name.encode()))
+
+    def end(self):
+        from block_diffusion_drafter_fwd_amd.abi import check
+        ms, launches = ctypes.c_double(), ctypes.c_int32()
+        check(self.lib, self.lib.dflash_profile_end(self.ctx, ctypes.byref(ms), ctypes.byref(launches)))
+        return ms.value, launches.value
+
+
+def hbm_line(alg_bytes, avg_s, **extra):
+    achieved = alg_bytes / avg_s / 1e9
+    d = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    d.update(extra)
+    return d
+
+
+def mfma_line(flops, avg_s, **extra):
+    achieved = flops / avg_s / 1e12
+    d = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+         "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
+    d.update(extra)
+    return d
 
 
 def main():
@@ -59,12 +105,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not an implemented path", "n_gpus": args.gpus}))
         sys.exit(2)
-    import numpy as np
     import torch
 
     import synth
-    from block_diffusion_drafter_fwd_amd import Drafter, sample
-    from block_diffusion_drafter_fwd_amd.abi import check
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -77,32 +120,70 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    cfg = synth.config(args.config)
     wl = synth.WORKLOADS[args.config]
+    cfg = synth.config(wl.config)
+    steps = args.steps if args.steps is not None else min(wl.rounds, 200)
     bf16 = cfg.dtype == "bf16"
     dt = torch.bfloat16 if bf16 else torch.float32
     t0 = time.time()
     w_np = synth.make_weights(cfg, seed=0, gains="unit")
-    w_dev = {k: torch.from_numpy(v).to(dev).to(dt) for k, v in w_np.items()}
-    if args.no_cpu_baseline:
-        del w_np
+    w_dev = {}
+    for k in list(w_np):
+        w_dev[k] = torch.from_numpy(w_np[k]).to(dev).to(dt)
+        if args.no_cpu_baseline or args.config != "qwen":
+            del w_np[k]
+    torch.cuda.synchronize()
     gen_s = time.time() - t0
-    d = Drafter(cfg, w_dev)
 
+    if wl.sessions > 1:
+        out = bench_batched(args, cfg, wl, w_dev, steps, torch, synth)
+    else:
+        out = bench_single(args, cfg, wl, w_dev, steps, torch, synth)
+    if not args.no_cpu_baseline and args.config == "qwen":
+        out["cpu_baseline"] = cpu_baseline(cfg, wl, w_np, args.cpu_rows)
+    else:
+        out.setdefault("cpu_baseline", None)
+    out["setup_s"] = round(gen_s, 1)
+    print(json.dumps(out), flush=True)
+
+
+class FeaturePool:
+    """Feature rows and tokens on the device: every row of the run when it is
+    small (qwen), else a POOL_ROWS-row block that positions index modulo
+    POOL_ROWS (chunks never straddle its end)."""
+
+    def __init__(self, cfg, total_rows, dev, dt, torch, synth, full):
+        fs = synth.FeatureSource(cfg, 0, 0)
+        self.full = full
+        rows = total_rows if full else POOL_ROWS + 64
+        self.feats = torch.from_numpy(fs.features(0, rows)).to(dev).to(dt)
+        self.toks = fs.tokens(0, rows)
+
+    def at(self, p, T):
+        o = p if self.full else p % POOL_ROWS
+        return self.toks[o:o + T], self.feats[o:o + T]
+
+
+def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
+    import numpy as np
+
+    from block_diffusion_drafter_fwd_amd import Drafter, sample
+
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    d = Drafter(cfg, w_dev)
+    st = Stage(d.lib, d.ctx)
     B = cfg.block_size
-    n_rounds = args.warmup + args.steps
-    capacity = wl.context + (n_rounds + 2) * B + 64
+    n_rounds = args.warmup + steps
+    extra = 20                                   # rounds run after the timed ones (stage passes)
+    capacity = wl.context + (n_rounds + extra) * B + 64
     if cfg.window:
         capacity = cfg.window + B - 1
-    fs = synth.FeatureSource(cfg, 0, 0)
     rs = synth.RoundScript(cfg, wl, 0, 0)
-    total_rows = wl.context + (n_rounds + 1) * B
-    feats = torch.from_numpy(fs.features(0, total_rows)).to(dev).to(dt)
-    toks = fs.tokens(0, total_rows)
-    plan = []
-    for r in range(n_rounds):
-        n = min(rs.max_tokens, B - 1)
-        plan.append((rs.accept(n), rs.bonus()))
+    total_rows = wl.context + (n_rounds + extra) * B
+    pool = FeaturePool(cfg, total_rows, dev, dt, torch, synth, full=args.config == "qwen")
+    n = min(rs.max_tokens, B - 1)
+    plan = [(rs.accept(n), rs.bonus()) for _ in range(n_rounds + extra)]
     current0 = rs.first_anchor()
     logits = torch.empty((B - 1, cfg.vocab), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -111,103 +192,242 @@ def main():
     def prompt(session):
         for p in range(0, wl.context, wl.commit_rows):
             T = min(wl.commit_rows, wl.context - p)
-            session.committed(toks[p:p + T], feats[p:p + T], p)
+            tk, ft = pool.at(p, T)
+            session.committed(tk, ft, p)
+        session.flush()
 
     warm = d.session(capacity)
     prompt(warm)
     warm.close()
     s = d.session(capacity)
     torch.cuda.synchronize()
+    if args.stages:
+        st.begin("flush_fc")
     t = time.perf_counter()
     prompt(s)
     torch.cuda.synchronize()
     flush_s = time.perf_counter() - t
+    fc_stage = st.end() if args.stages else None
     flush_rows_per_s = wl.context / flush_s
 
     # ---- round phase
-    state = {"current": current0}
+    state = {"current": current0, "r": 0}
+    F_seen = []
 
-    def step(r):
-        n, lg, _ = s.propose(state["current"], rs.max_tokens, logits=logits)
-        sample([s], [0, n], lg, wl.temperature, wl.rep_penalty, wl.history, r, probs=wl.probs)
+    def step():
+        r = state["r"]
+        n_, lg, _ = s.propose(state["current"], rs.max_tokens, logits=logits)
+        sample([s], [0, n_], lg, wl.temperature, wl.rep_penalty, wl.history, r, probs=wl.probs)
         a, bonus = plan[r]
         s.commit_block()
         F = s.state()[0]
-        run = np.concatenate([[state["current"]], toks[F + 1:F + 1 + a]]).astype(np.int32)
-        s.committed(run, feats[F:F + a + 1], F)
+        F_seen.append(F)
+        tk, ft = pool.at(F, a + 1)
+        run = np.concatenate([[state["current"]], tk[1:a + 1]]).astype(np.int32)
+        s.committed(run, ft, F)
         state["current"] = bonus
+        state["r"] = r + 1
 
-    for r in range(args.warmup):
-        step(r)
-    lib = d.lib
-    check(lib, lib.dflash_profile_begin(d.ctx, b"unembed"))
+    for _ in range(args.warmup):
+        step()
+    F_seen.clear()
+    st.begin("unembed")
     torch.cuda.synchronize()
     t = time.perf_counter()
-    for r in range(args.warmup, n_rounds):
-        step(r)
+    for _ in range(steps):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t
-    import ctypes
-    ms, launches = ctypes.c_double(), ctypes.c_int32()
-    check(lib, lib.dflash_profile_end(d.ctx, ctypes.byref(ms), ctypes.byref(launches)))
-    blocks_per_s = args.steps / elapsed
+    ms, launches = st.end()
+    blocks_per_s = steps / elapsed
 
-    # roofline of the unembedding GEMM: algorithmic bytes per launch
-    n = min(rs.max_tokens, B - 1)
-    elem = 2 if bf16 else 4
+    elem = 2 if cfg.dtype == "bf16" else 4
     alg_bytes = cfg.vocab * cfg.hidden * elem + n * cfg.hidden * elem + n * cfg.vocab * 4
-    avg_s = ms.value / 1e3 / max(1, launches.value)
-    achieved = alg_bytes / avg_s / 1e9
+    avg_s = ms / 1e3 / max(1, launches)
     traffic = None
     if os.path.exists(PMC_FILE) and args.config == "qwen":
         pmc = json.load(open(PMC_FILE))
         if pmc.get("kernel_source_sha256_16") == kernel_source_hash():
             traffic = pmc.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemm_skinny<1> (lm_head)", "alg_bytes_per_launch": alg_bytes,
-                "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches.value}
+    roofline = hbm_line(alg_bytes, avg_s, traffic=traffic, kernel="k_gemm_skinny_p<4,1> (lm_head)",
+                        alg_bytes_per_launch=alg_bytes, avg_launch_us=round(avg_s * 1e6, 2), launches=launches)
+    kernels = {"unembed": roofline}
 
-    stages = None
     if args.stages:
-        stages = {}
-        for st in ("attention", "sampler"):
-            check(lib, lib.dflash_profile_begin(d.ctx, st.encode()))
-            base = n_rounds
-            for r in range(8):
-                step(min(base - 1, args.warmup + r))
-            check(lib, lib.dflash_profile_end(d.ctx, ctypes.byref(ms), ctypes.byref(launches)))
-            stages[st] = {"avg_us": round(ms.value * 1e3 / max(1, launches.value), 2), "launches": launches.value}
+        # attention: one launch pair per layer; its KV bytes over the visible keys
+        F_mean = float(np.mean(F_seen)) if F_seen else float(wl.context)
+        vis = min(F_mean, cfg.window - 1) + n + 1 if cfg.window else F_mean + n + 1
+        kv_bytes = 2 * cfg.kv_heads * vis * cfg.head_dim * elem
+        for name in ("attention", "sampler"):
+            st.begin(name)
+            for _ in range(8):
+                step()
+            ms_s, l_s = st.end()
+            avg = ms_s / 1e3 / max(1, l_s)
+            if name == "attention":
+                kernels[name] = hbm_line(kv_bytes, avg, alg_bytes_per_launch=int(kv_bytes),
+                                         avg_launch_us=round(avg * 1e6, 2), launches=l_s)
+            else:
+                sb = n * cfg.vocab * 4 * (2 if wl.probs and wl.temperature > 0 else 1)
+                kernels[name] = hbm_line(sb, avg, alg_bytes_per_launch=sb, avg_launch_us=round(avg * 1e6, 2),
+                                         launches=l_s)
+        if fc_stage and fc_stage[1]:
+            avg = fc_stage[0] / 1e3 / fc_stage[1]
+            rows = wl.commit_rows
+            kernels["flush_fc"] = mfma_line(2.0 * rows * cfg.fc_in * cfg.hidden, avg, rows=rows,
+                                            avg_launch_us=round(avg * 1e6, 2), launches=fc_stage[1])
+        s2 = d.session(capacity)
+        st.begin("flush_kv")
+        prompt(s2)
+        torch.cuda.synchronize()
+        ms_k, l_k = st.end()
+        s2.close()
+        if l_k:
+            avg = ms_k / 1e3 / l_k
+            kvn = cfg.layers * 2 * cfg.kv_heads * cfg.head_dim
+            kernels["flush_kv"] = mfma_line(2.0 * wl.commit_rows * cfg.hidden * kvn, avg, rows=wl.commit_rows,
+                                            avg_launch_us=round(avg * 1e6, 2), launches=l_k)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, wl, w_np, args.cpu_rows)
-
-    out = {
+    return {
         "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
         "value": round(blocks_per_s, 2),
         "unit": "blocks/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "fp32",
+        "dtype": "bf16" if cfg.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tap features; no checkpoint)",
-        "config": {"workload": f"{cfg.name}: {wl.context}-slot context in {wl.commit_rows}-row flushes, "
-                               f"then rounds at n={min(rs.max_tokens, B - 1)}",
-                   "hidden": cfg.hidden, "layers": cfg.layers, "heads": f"{cfg.q_heads}/{cfg.kv_heads}x{cfg.head_dim}",
-                   "vocab": cfg.vocab, "block_size": B, "context": wl.context, "temperature": wl.temperature},
+        "config": {"workload": f"{wl.name}: {wl.context}-slot context in {wl.commit_rows}-row flushes, "
+                               f"then rounds at n={n}" + (f", window {cfg.window}" if cfg.window else ""),
+                   "hidden": cfg.hidden, "layers": cfg.layers,
+                   "heads": f"{cfg.q_heads}/{cfg.kv_heads}x{cfg.head_dim}", "vocab": cfg.vocab,
+                   "block_size": B, "context": wl.context, "temperature": wl.temperature},
         "flushed_ctx_rows_per_s": round(flush_rows_per_s, 1),
         "roofline": roofline,
-        "cpu_baseline": cpu,
+        "kernels": kernels,
     }
-    if stages:
-        out["stages"] = stages
-    out["setup_s"] = round(gen_s, 1)
-    print(json.dumps(out), flush=True)
+
+
+def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
+    """64 sessions, one batched propose + one batched sample per round."""
+    import numpy as np
+
+    from block_diffusion_drafter_fwd_amd import Drafter, propose_batch, sample
+
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    S = wl.sessions
+    B = cfg.block_size
+    lens = synth.session_lengths(wl, 0)
+    n_rounds = args.warmup + steps
+    d = Drafter(cfg, w_dev, max_sessions=S)
+    st = Stage(d.lib, d.ctx)
+    pool = FeaturePool(cfg, POOL_ROWS, dev, dt, torch, synth, full=False)
+    scripts = [synth.RoundScript(cfg, wl, 0, k) for k in range(S)]
+    caps = [L + (n_rounds + 12) * B + 64 for L in lens]
+    logits = torch.empty((S * (B - 1), cfg.vocab), dtype=torch.float32, device=dev)
+
+    def prompt(sessions):
+        for k, sess in enumerate(sessions):
+            for p in range(0, lens[k], wl.commit_rows):
+                T = min(wl.commit_rows, lens[k] - p)
+                tk, ft = pool.at(p, T)
+                sess.committed(tk, ft, p)
+            sess.flush()
+
+    sess = [d.session(caps[k], seed=0, stream_id=k) for k in range(S)]
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    prompt(sess)
+    torch.cuda.synchronize()
+    flush_s = time.perf_counter() - t
+    flush_rows_per_s = sum(lens) / flush_s
+
+    cur = [sc.first_anchor() for sc in scripts]
+    mts = [sc.max_tokens for sc in scripts]
+    state = {"r": 0, "rows": []}
+
+    def step():
+        r = state["r"]
+        for k, sc in enumerate(scripts):
+            if sc.flush_before:
+                sess[k].flush()
+        offs, lg = propose_batch(sess, cur, mts, logits=logits)
+        sample(sess, offs, lg, wl.temperature, wl.rep_penalty, wl.history, r, probs=wl.probs)
+        state["rows"].append(offs[S])
+        for k, sc in enumerate(scripts):
+            nk = offs[k + 1] - offs[k]
+            a = sc.accept(nk)
+            bonus = sc.bonus()
+            sess[k].commit_block()
+            F = sess[k].state()[0]
+            tk, ft = pool.at(F, a + 1)
+            run = np.concatenate([[cur[k]], tk[1:a + 1]]).astype(np.int32)
+            sess[k].committed(run, ft, F)
+            cur[k] = bonus
+        state["r"] = r + 1
+
+    for _ in range(args.warmup):
+        step()
+    state["rows"].clear()
+    st.begin("attention")
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t
+    ms_a, l_a = st.end()
+    blocks_per_s = steps * S / elapsed
+    R = float(np.mean(state["rows"]))
+    elem = 2
+    ctx_now = [sess[k].state()[0] for k in range(S)]
+    kv_bytes_layer = sum(2 * cfg.kv_heads * (c + B) * cfg.head_dim * elem for c in ctx_now)
+    avg_a = ms_a / 1e3 / max(1, l_a)
+    attn = hbm_line(kv_bytes_layer, avg_a, kernel="k_attn_partial + k_attn_combine (all sessions, one layer)",
+                    alg_bytes_per_launch=int(kv_bytes_layer), avg_launch_us=round(avg_a * 1e6, 2), launches=l_a)
+    kernels = {"attention": attn}
+    for name in ("unembed", "sampler"):
+        st.begin(name)
+        for _ in range(4):
+            step()
+        ms_s, l_s = st.end()
+        avg = ms_s / 1e3 / max(1, l_s)
+        if name == "unembed":
+            kernels[name] = mfma_line(2.0 * R * cfg.hidden * cfg.vocab, avg, rows=round(R, 1),
+                                      avg_launch_us=round(avg * 1e6, 2), launches=l_s)
+        else:
+            sb = R * cfg.vocab * 4
+            kernels[name] = hbm_line(sb, avg, alg_bytes_per_launch=int(sb), avg_launch_us=round(avg * 1e6, 2),
+                                     launches=l_s)
+    for x in sess:
+        x.close()
+    return {
+        "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
+        "value": round(blocks_per_s, 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tap features repeating every 4096 slots)",
+        "config": {"workload": f"batched: {S} sessions, contexts log-uniform {wl.context_lo}..{wl.context_hi} "
+                               f"(sum {sum(lens)}), U{{1..{B - 1}}} rows each, T={wl.temperature}, "
+                               f"penalty {wl.rep_penalty}",
+                   "hidden": cfg.hidden, "layers": cfg.layers, "vocab": cfg.vocab, "block_size": B,
+                   "sessions": S, "rows_per_round": round(R, 1)},
+        "flushed_ctx_rows_per_s": round(flush_rows_per_s, 1),
+        "roofline": attn,
+        "kernels": kernels,
+    }
 
 
 def cpu_baseline(cfg, wl, w_np, rows):

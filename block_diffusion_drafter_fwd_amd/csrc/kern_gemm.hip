@@ -26,14 +26,16 @@ __device__ __forceinline__ f32x4_t mfma32(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int find_seg(const GemmArgs& a, int tile) {
+template <class GA>
+__device__ __forceinline__ int find_seg(const GA& a, int tile) {
     int s = 0;
     for (int j = 1; j < a.nseg; ++j)
         if (tile >= a.seg[j].tile0) s = j;
     return s;
 }
 
-__device__ __forceinline__ void store_out(const GemmArgs& a, int split, int m, int col, float v) {
+template <class GA>
+__device__ __forceinline__ void store_out(const GA& a, int split, int m, int col, float v) {
     if (a.splits == 1) {
         float* p = a.C + (size_t)m * a.ldc + col;
         *p = a.accumulate ? *p + v : v;
@@ -53,8 +55,8 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int split, int m, i
 // ---------------------------------------------------------------------------
 constexpr int kSkWaves = 8;
 
-template <int TPW, int TAG>
-__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
+template <int TPW, int TAG, class GA>
+__global__ __launch_bounds__(512) void k_gemm_skinny(GA a) {
     constexpr int BATCH = TPW == 1 ? 4 : 2;    // k steps per wave between waits
     __shared__ float red[kSkWaves][TPW][256];
     const int b = blockIdx.x, split = blockIdx.y, S = gridDim.y;
@@ -198,8 +200,8 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
 // per-tile kernel when N is large (the unembedding reads 622 MB of weights
 // against 64 KB of activations).
 // ---------------------------------------------------------------------------
-template <int STEPS, int TAG>
-__global__ __launch_bounds__(512) void k_gemm_skinny_p(GemmArgs a) {
+template <int STEPS, int TAG, class GA>
+__global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
     __shared__ float red[kSkWaves][64 * 4];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const bool pair = a.mode == kSwiGLU;
@@ -286,8 +288,8 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // tiled: MT x 128 tiles, KT = 64, LDS double buffer
 // ---------------------------------------------------------------------------
-template <int MT, int TAG>
-__global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
+template <int MT, int TAG, class GA>
+__global__ __launch_bounds__(256) void k_gemm_tiled(GA a) {
     constexpr int NT = 128, KT = 64, LDS_LD = KT + 8;
     constexpr int AL = MT / 32, BL = NT / 32;      // 16-byte loads per thread
     constexpr int TM = MT / 32, TN = 4;            // 16x16 tiles per wave
@@ -379,7 +381,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // fp32: one thread per output element
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_gemm_f32(GemmArgs a) {
+template <class GA>
+__global__ __launch_bounds__(64) void k_gemm_f32(GA a) {
     const int col = a.col_lo + blockIdx.x * 64 + threadIdx.x;
     const int m = blockIdx.y;
     if (col >= a.col_hi) return;
@@ -397,7 +400,8 @@ __global__ __launch_bounds__(64) void k_gemm_f32(GemmArgs a) {
     *p = a.accumulate ? *p + acc : acc;
 }
 
-__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs a) {
+template <class GA>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GA a) {
     const int width = a.col_hi - a.col_lo;
     const size_t total = (size_t)a.M * width;
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
@@ -431,8 +435,9 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* in, int32_t ld, int
     }
 }
 
-hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag,
-                int* splits_out) {
+template <class GA>
+static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag,
+                            int* splits_out) {
     if (a.M <= 0 || a.nseg <= 0) return hipSuccess;
     a.accumulate = a.mode == kAccumulate;
     a.col_lo = a.seg[0].c_col0;
@@ -465,11 +470,11 @@ hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipS
         if (shared_a && (steps == 4 || steps == 8) && ntiles >= 2 * grid) {
             if (splits_out) *splits_out = 1;
             if (steps == 4) {
-                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1>), dim3(grid), dim3(512), 0, st, a);
-                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0>), dim3(grid), dim3(512), 0, st, a);
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1, GA>), dim3(grid), dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA>), dim3(grid), dim3(512), 0, st, a);
             } else {
-                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<8, 1>), dim3(grid), dim3(512), 0, st, a);
-                else hipLaunchKernelGGL((k_gemm_skinny_p<8, 0>), dim3(grid), dim3(512), 0, st, a);
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<8, 1, GA>), dim3(grid), dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<8, 0, GA>), dim3(grid), dim3(512), 0, st, a);
             }
             return hipGetLastError();
         }
@@ -487,11 +492,11 @@ hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipS
         if (splits_out) *splits_out = splits;
         const dim3 grid2(nwg, splits);
         if (tpw == 2) {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<2, 1>), grid2, dim3(512), 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_skinny<2, 0>), grid2, dim3(512), 0, st, a);
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<2, 1, GA>), grid2, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_skinny<2, 0, GA>), grid2, dim3(512), 0, st, a);
         } else {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<1, 1>), grid2, dim3(512), 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_skinny<1, 0>), grid2, dim3(512), 0, st, a);
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<1, 1, GA>), grid2, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_skinny<1, 0, GA>), grid2, dim3(512), 0, st, a);
         }
         return hipGetLastError();
     }
@@ -505,7 +510,7 @@ hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipS
         a.kc = a.K;
         a.accumulate = a.mode == kAccumulate;
         dim3 grid((a.col_hi - a.col_lo + 63) / 64, a.M);
-        hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL(k_gemm_f32<GA>, grid, dim3(64), 0, st, a);
         e = hipGetLastError();
     } else {
         const int NT = 128;
@@ -534,17 +539,17 @@ hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipS
         }
         const dim3 blk(256);
         if (MT == 64) {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_tiled<64, 0>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_tiled<64, 0, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
         } else {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<128, 1>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_tiled<128, 0>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<128, 1, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_tiled<128, 0, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
         }
         e = hipGetLastError();
         if (e == hipSuccess && splits > 1 && a.mode != kPartial) {
             const size_t total = (size_t)a.M * (a.col_hi - a.col_lo);
             const int blocks = (int)std::min<size_t>((total + 255) / 256, (size_t)num_cus * 8);
-            hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_splitk_reduce<GA>, dim3(blocks), dim3(256), 0, st, a);
             e = hipGetLastError();
         }
     }
@@ -554,6 +559,15 @@ hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipS
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(k_swiglu, dim3(blocks), dim3(256), 0, st, a.C, a.ldc, I, a.out, a.ldo, a.out_bf16, a.M);
     return hipGetLastError();
+}
+
+hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag,
+                int* splits_out) {
+    if (a.nseg > kFewSeg) return gemm_impl(a, bf16, part_cap_floats, num_cus, st, tag, splits_out);
+    GemmArgsT<kFewSeg> b{};
+    static_cast<GemmHead&>(b) = a;
+    for (int s = 0; s < kFewSeg; ++s) b.seg[s] = a.seg[s];
+    return gemm_impl(b, bf16, part_cap_floats, num_cus, st, tag, splits_out);
 }
 
 }  // namespace kern

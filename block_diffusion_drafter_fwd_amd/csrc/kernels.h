@@ -51,7 +51,7 @@ struct GemmSeg {
 // max_splits slices); the consumer of C adds the slices
 enum GemmMode { kStore = 0, kAccumulate = 1, kSwiGLU = 2, kPartial = 3 };
 
-struct GemmArgs {
+struct GemmHead {
     int32_t M, K, kc, splits;
     float* C;
     int32_t ldc, accumulate;
@@ -62,8 +62,17 @@ struct GemmArgs {
     float* part;              // split-K partials [splits][M][ldc]
     int32_t nseg, ntiles;
     int32_t col_lo, col_hi;   // columns covered by the segments
-    GemmSeg seg[kMaxSeg];
 };
+
+// The argument block is copied to the device at every launch and its cache
+// lines are fetched by every workgroup at start-up, so launches with few
+// segments use a short form (the launcher converts).
+template <int NS>
+struct GemmArgsT : GemmHead {
+    GemmSeg seg[NS];
+};
+constexpr int kFewSeg = 4;
+using GemmArgs = GemmArgsT<kMaxSeg>;
 
 // y = RMSNorm(x) * gain with x = in[row] (optional) + sum of nsplit fp32
 // slices part[s * part_stride + row * in_stride]; x is written back to
