@@ -20,6 +20,7 @@ namespace kern {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;   // 16-byte operand piece
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ f32x4_t mfma32(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -286,6 +287,155 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
 }
 
 // ---------------------------------------------------------------------------
+// tiled, pipelined (M > 16, K a multiple of 256): 128 x 128 output tiles, 4
+// waves as 2 x 2 owning 64 x 64 each (4 x 4 MFMA tiles).  64-wide k tiles of
+// A and B are copied straight into LDS (global_load_lds, no registers) into
+// four stages, three ahead of the one being multiplied; each 128-byte row of
+// a stage has its 16-byte pieces XOR-permuted by (row / 2) mod 8, so the 16
+// rows of a fragment read fall on distinct banks.  The stages are separate
+// LDS objects and the k loop is unrolled over them, so the compiler sees the
+// copies into one stage as independent of the reads from another.
+// ---------------------------------------------------------------------------
+constexpr int kMtBM = 128, kMtBN = 128, kMtBK = 64;
+
+// per lane: the source rows (already offset to the lane's 16-byte piece) of
+// the 4 A and 4 B pieces it copies into every stage
+struct MtRows {
+    const uint16_t* pa[4];
+    const uint16_t* pb[4];
+};
+
+// copy k tile at k0 of A and B into one stage: per operand the 128 x 8
+// pieces are 16 wave instructions of 64 pieces (8 rows), 4 per wave
+__device__ __forceinline__ void mt_load(const MtRows& c, int wave, int k0, uint16_t* sA, uint16_t* sB) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = wave * 4 + i;                    // 8-row block of the stage
+        __builtin_amdgcn_global_load_lds(c.pa[i] + k0, (lds_void_t*)&sA[b * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(c.pb[i] + k0, (lds_void_t*)&sB[b * 512], 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ int mt_off(int row, int piece) { return row * 64 + ((piece ^ ((row >> 1) & 7)) << 3); }
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+template <int TAG, class GA>
+__global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[kMtBM * kMtBK], sA1[kMtBM * kMtBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA2[kMtBM * kMtBK], sA3[kMtBM * kMtBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[kMtBN * kMtBK], sB1[kMtBN * kMtBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB2[kMtBN * kMtBK], sB3[kMtBN * kMtBK];
+    const int tile = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
+    const GemmSeg g = a.seg[find_seg(a, tile)];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
+    const int m0 = mt * kMtBM, n0 = (tile - g.tile0) * kMtBN;
+    MtRows c;
+    {
+        // lane l of block b stores piece position l % 8 of row 8 b + l / 8,
+        // which holds logical piece (l % 8) ^ ((row / 2) % 8); rows past M or
+        // N repeat the last one (computed, never stored)
+        const int rl = lane >> 3, pp = lane & 7;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wave * 4 + i) * 8 + rl;
+            const int lp = pp ^ ((row >> 1) & 7);
+            const int am = min(m0 + row, a.M - 1);
+            const int ar = a.a_rows ? a.a_rows[am] : am;
+            c.pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + lp * 8;
+            c.pb[i] = (const uint16_t*)g.B + (size_t)min(n0 + row, g.N - 1) * g.ldb + lp * 8;
+        }
+    }
+    const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
+    const int nk = (ke - kb) / kMtBK;
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // fragment reads are issued as inline asm: the compiler, which cannot tell
+    // the stage being read from the stages being copied into, would otherwise
+    // wait for every copy in flight before each read; here the reads of one
+    // 32-wide k step are waited for (lgkmcnt) explicitly, tied to their values
+    uint32_t offA[4], offB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        offA[i] = (uint32_t)mt_off(wm * 64 + i * 16 + r, q) * 2;
+        offB[i] = (uint32_t)mt_off(wn * 64 + i * 16 + r, q) * 2;
+    }
+    auto compute = [&](const uint16_t* tA, const uint16_t* tB) {
+        const uint32_t baseA = lds_addr(tA), baseB = lds_addr(tB);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // piece kk * 4 + q of a row sits at (kk * 4 + q) ^ swz = (q ^ swz) ^ (kk * 4):
+            // the kk = 1 pieces are the kk = 0 ones with bit 2 of the position flipped
+            u32x4_t af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = lds_read16(baseA + (offA[i] ^ (kk * 64)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = lds_read16(baseB + (offB[j] ^ (kk * 64)));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]),
+                           "+v"(bf[2]), "+v"(bf[3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+        }
+    };
+    // step kt: wait for its stage (the two stages after it stay in flight:
+    // 8 copy instructions each per wave), then start the copy of tile kt + 3
+    // into the stage tile kt - 1 used, then multiply.  Copies are issued
+    // unconditionally (past the end the last tile is fetched again, unused) so
+    // the count of copies in flight is the same at every step.
+    auto step = [&](int kt, const uint16_t* tA, const uint16_t* tB, uint16_t* nA, uint16_t* nB) {
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        // a bare barrier: a fenced one would also wait for the later stages'
+        // copies (the LDS reads of the previous step completed before their
+        // MFMAs issued, so the stage refilled below is free)
+        __builtin_amdgcn_s_barrier();
+        mt_load(c, wave, kb + min(kt + 3, nk - 1) * kMtBK, nA, nB);
+        compute(tA, tB);
+    };
+    if (nk > 0) {
+        mt_load(c, wave, kb, sA0, sB0);
+        mt_load(c, wave, kb + min(1, nk - 1) * kMtBK, sA1, sB1);
+        mt_load(c, wave, kb + min(2, nk - 1) * kMtBK, sA2, sB2);
+    }
+    for (int kt = 0; kt < nk; kt += 4) {          // nk is a multiple of 4 (the launcher's split)
+        step(kt, sA0, sB0, sA3, sB3);
+        step(kt + 1, sA1, sB1, sA0, sB0);
+        step(kt + 2, sA2, sB2, sA1, sB1);
+        step(kt + 3, sA3, sB3, sA2, sB2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+    // output (m, n) of MFMA tile (i, j): lane (r, q) holds rows 4 q + e of column r
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + j * 16 + r;
+            const bool nok = n < g.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * 64 + i * 16 + 4 * q + e;
+                if (nok && m < a.M) store_out(a, split, m, g.c_col0 + n, acc[i][j][e]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // tiled: MT x 128 tiles, KT = 64, LDS double buffer
 // ---------------------------------------------------------------------------
 template <int MT, int TAG, class GA>
@@ -513,8 +663,11 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         hipLaunchKernelGGL(k_gemm_f32<GA>, grid, dim3(64), 0, st, a);
         e = hipGetLastError();
     } else {
+        // the pipelined kernel takes K in 256-wide groups (four 64-wide stages)
+        const bool pipelined = a.K % 256 == 0;
         const int NT = 128;
-        const int MT = a.M <= 64 ? 64 : 128;
+        const int MT = pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
+        const int kq = pipelined ? 256 : 64;
         int ntiles = 0;
         for (int s = 0; s < a.nseg; ++s) {
             a.seg[s].tile0 = ntiles;
@@ -523,13 +676,14 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         a.ntiles = ntiles;
         const int mtiles = (a.M + MT - 1) / MT;
         const int base = ntiles * mtiles;
-        // about one 256-thread tile per CU; keep a split at >= 512 k-values
+        // about one workgroup per CU (128 KiB of LDS each); keep a split at
+        // >= 512 k-values
         int splits = 1;
         while (base * splits < num_cus && a.K / (splits * 2) >= 512) splits *= 2;
         const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
         while (splits > 1 && ((size_t)splits * a.M * a.ldc > cap || splits > (a.mode == kPartial ? a.max_splits : 1 << 30)))
             splits /= 2;
-        int kc = ((a.K + splits - 1) / splits + 63) / 64 * 64;
+        int kc = ((a.K + splits - 1) / splits + kq - 1) / kq * kq;
         splits = (a.K + kc - 1) / kc;
         a.splits = splits;
         a.kc = kc;
@@ -537,13 +691,16 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             a.part = a.C;            // the partial slices are the output
             if (splits_out) *splits_out = splits;
         }
-        const dim3 blk(256);
-        if (MT == 64) {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_tiled<64, 0, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+        const dim3 blk(256), grid3(ntiles, mtiles, splits);
+        if (pipelined) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_mt<1, GA>), grid3, blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_mt<0, GA>), grid3, blk, 0, st, a);
+        } else if (MT == 64) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1, GA>), grid3, blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_tiled<64, 0, GA>), grid3, blk, 0, st, a);
         } else {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<128, 1, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_tiled<128, 0, GA>), dim3(ntiles, mtiles, splits), blk, 0, st, a);
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<128, 1, GA>), grid3, blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_tiled<128, 0, GA>), grid3, blk, 0, st, a);
         }
         e = hipGetLastError();
         if (e == hipSuccess && splits > 1 && a.mode != kPartial) {
