@@ -34,6 +34,8 @@ size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kSampleChunk = 4096;
 constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
+constexpr int kAttnRoundChunk = 4096;                // longest chunk worth a single resident round
+constexpr int kAttnManyChunk = 2048;                 // chunk when the split runs in several rounds
 constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 32 MiB
 constexpr int kMaxSlicesFc = 8;                      // K slices of the fc GEMM
 constexpr int kMaxSlicesKv = 2;                      // K slices of the context k|v GEMM
@@ -67,7 +69,7 @@ public:
         w.blk_slices = std::max(1, std::min(8, 4096 / w.r_blk));
         const int32_t rmax = std::max(w.r_ctx, w.r_blk);
         const int32_t L = c.layers, H = c.hidden, I = c.intermediate;
-        w.items_cap = std::max(1, attn_target_wg() / c.kv_heads) + ms;
+        w.items_cap = 4 * std::max(1, attn_target_wg() / c.kv_heads) + ms;
         w.nchunk_max = (c.vocab + kSampleChunk - 1) / kSampleChunk;
         size_t o = 0;
         auto put = [&](size_t bytes) { size_t at = o; o += al(bytes); return at; };
@@ -419,9 +421,22 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         descs.push_back(d);
     }
     if (R > w.r_blk) return fail(DFLASH_E_CAPACITY, "block rows exceed the workspace");
+    // attention split: every sequence's keys in chunks of one size.  If one
+    // resident round of workgroups (target_items per kv head) can hold the
+    // whole split with chunks of at most kAttnRoundChunk keys, use that (one
+    // round, no tail).  Otherwise (many sequences, or very long ones) use
+    // kAttnManyChunk-key chunks over several rounds, so that one long
+    // sequence does not leave the other workgroups idle; the workspace
+    // bounds the item count.
     const int32_t target_items = std::max(1, attn_target_wg() / c.kv_heads);
-    int32_t chunk = (int32_t)((total_keys + target_items - 1) / target_items);
-    chunk = std::max(kAttnMinChunk, (chunk + 63) / 64 * 64);
+    const int32_t nseq = (int32_t)seqs.size();
+    int64_t chunk64 = target_items > nseq ? (total_keys + target_items - nseq - 1) / (target_items - nseq)
+                                          : (int64_t)kAttnRoundChunk + 1;
+    if (chunk64 > kAttnRoundChunk) {
+        const int64_t room = std::max<int64_t>(1, (int64_t)w.items_cap - nseq);
+        chunk64 = std::max<int64_t>(kAttnManyChunk, (total_keys + room - 1) / room);
+    }
+    int32_t chunk = (int32_t)std::max<int64_t>(kAttnMinChunk, (chunk64 + 63) / 64 * 64);
     int32_t items = 0;
     for (SeqDesc& d : descs) {
         const int32_t nk = d.F + d.M - d.key_lo;
