@@ -56,7 +56,9 @@ def build_hip(verbose: bool = False) -> str:
     objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + HOST_SOURCES]
     lib = os.path.join(HERE, "libdflash.so")
     tmp = lib + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    # -z defs: an unresolved symbol (say, a kernel stub the host pass failed to
+    # emit) fails the build instead of the first dlopen
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,-z,defs", *objs, "-o", tmp])
     os.replace(tmp, lib)
     return lib
 

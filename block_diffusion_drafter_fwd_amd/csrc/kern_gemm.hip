@@ -296,27 +296,36 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
 // LDS objects and the k loop is unrolled over them, so the compiler sees the
 // copies into one stage as independent of the reads from another.
 // ---------------------------------------------------------------------------
-constexpr int kMtBM = 128, kMtBN = 128, kMtBK = 64;
+constexpr int kMtBM = 128, kMtBN = 128;
 
 // per lane: the source rows (already offset to the lane's 16-byte piece) of
-// the 4 A and 4 B pieces it copies into every stage
+// the A and B pieces it copies into every stage
+template <int BK>
 struct MtRows {
-    const uint16_t* pa[4];
-    const uint16_t* pb[4];
+    static constexpr int kInst = BK / 16;              // copy instructions per operand per wave
+    const uint16_t* pa[kInst];
+    const uint16_t* pb[kInst];
 };
 
-// copy k tile at k0 of A and B into one stage: per operand the 128 x 8
-// pieces are 16 wave instructions of 64 pieces (8 rows), 4 per wave
-__device__ __forceinline__ void mt_load(const MtRows& c, int wave, int k0, uint16_t* sA, uint16_t* sB) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = wave * 4 + i;                    // 8-row block of the stage
-        __builtin_amdgcn_global_load_lds(c.pa[i] + k0, (lds_void_t*)&sA[b * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(c.pb[i] + k0, (lds_void_t*)&sB[b * 512], 16, 0, 0);
-    }
+// 16-byte pieces of a BK-wide row are XOR-permuted by the row's position in
+// its 256-byte bank cycle, so a fragment read of 16 rows hits 64 banks
+template <int BK>
+__device__ __forceinline__ int mt_swz(int row) {
+    constexpr int P = BK / 8, SH = BK == 64 ? 1 : 2;   // pieces per row; log2(rows per bank cycle)
+    return (row >> SH) & (P - 1);
 }
 
-__device__ __forceinline__ int mt_off(int row, int piece) { return row * 64 + ((piece ^ ((row >> 1) & 7)) << 3); }
+template <int BK>
+__device__ __forceinline__ int mt_off(int row, int piece) {
+    return row * BK + ((piece ^ mt_swz<BK>(row)) << 3);
+}
+
+// one 16-byte piece per lane from global memory straight into LDS (the LDS
+// destination is wave-uniform; lane l lands at dst + 16 l).  Kept out of the
+// kernel templates: their host-side pass cannot compile the builtin.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
@@ -328,27 +337,30 @@ __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
     return v;
 }
 
-template <int TAG, class GA>
+template <int TAG, class GA, int BK>
 __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA0[kMtBM * kMtBK], sA1[kMtBM * kMtBK];
-    __shared__ __attribute__((aligned(16))) uint16_t sA2[kMtBM * kMtBK], sA3[kMtBM * kMtBK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB0[kMtBN * kMtBK], sB1[kMtBN * kMtBK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB2[kMtBN * kMtBK], sB3[kMtBN * kMtBK];
+    constexpr int KS = BK / 32;                         // 32-wide MFMA k steps per stage
+    constexpr int NI = MtRows<BK>::kInst;
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[kMtBM * BK], sA1[kMtBM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA2[kMtBM * BK], sA3[kMtBM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[kMtBN * BK], sB1[kMtBN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB2[kMtBN * BK], sB3[kMtBN * BK];
     const int tile = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
     const GemmSeg g = a.seg[find_seg(a, tile)];
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
     const int m0 = mt * kMtBM, n0 = (tile - g.tile0) * kMtBN;
-    MtRows c;
+    MtRows<BK> c;
     {
-        // lane l of block b stores piece position l % 8 of row 8 b + l / 8,
-        // which holds logical piece (l % 8) ^ ((row / 2) % 8); rows past M or
-        // N repeat the last one (computed, never stored)
-        const int rl = lane >> 3, pp = lane & 7;
+        // lane l of a block stores piece position l % P of the block's row
+        // l / P, which holds the logical piece that position maps to; rows
+        // past M or N repeat the last one (computed, never stored)
+        constexpr int P = BK / 8;
+        const int rl = lane / P, pp = lane % P;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wave * 4 + i) * 8 + rl;
-            const int lp = pp ^ ((row >> 1) & 7);
+        for (int i = 0; i < NI; ++i) {
+            const int row = (wave * NI + i) * (64 / P) + rl;
+            const int lp = pp ^ mt_swz<BK>(row);
             const int am = min(m0 + row, a.M - 1);
             const int ar = a.a_rows ? a.a_rows[am] : am;
             c.pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + lp * 8;
@@ -356,7 +368,17 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
         }
     }
     const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
-    const int nk = (ke - kb) / kMtBK;
+    const int nk = (ke - kb) / BK;
+    // copy one BK-wide k tile of A and B into a stage: per operand 128 rows x
+    // BK/8 pieces, i.e. BK/4 wave instructions of 64 pieces, NI per wave
+    auto mt_load = [&](int k0, uint16_t* sA, uint16_t* sB) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int b = wave * NI + i;               // 1 KiB block of the stage
+            dma16(c.pa[i] + k0, &sA[b * 512]);
+            dma16(c.pb[i] + k0, &sB[b * 512]);
+        }
+    };
 
     f32x4_t acc[4][4];
 #pragma unroll
@@ -371,15 +393,15 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
     uint32_t offA[4], offB[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        offA[i] = (uint32_t)mt_off(wm * 64 + i * 16 + r, q) * 2;
-        offB[i] = (uint32_t)mt_off(wn * 64 + i * 16 + r, q) * 2;
+        offA[i] = (uint32_t)mt_off<BK>(wm * 64 + i * 16 + r, q) * 2;
+        offB[i] = (uint32_t)mt_off<BK>(wn * 64 + i * 16 + r, q) * 2;
     }
     auto compute = [&](const uint16_t* tA, const uint16_t* tB) {
         const uint32_t baseA = lds_addr(tA), baseB = lds_addr(tB);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            // piece kk * 4 + q of a row sits at (kk * 4 + q) ^ swz = (q ^ swz) ^ (kk * 4):
-            // the kk = 1 pieces are the kk = 0 ones with bit 2 of the position flipped
+        for (int kk = 0; kk < KS; ++kk) {
+            // piece kk * 4 + q sits at (q ^ swz) ^ (kk * 4): the kk = 1 pieces
+            // are the kk = 0 ones with bit 2 of the position flipped
             u32x4_t af[4], bf[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = lds_read16(baseA + (offA[i] ^ (kk * 64)));
@@ -395,23 +417,24 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
         }
     };
     // step kt: wait for its stage (the two stages after it stay in flight:
-    // 8 copy instructions each per wave), then start the copy of tile kt + 3
-    // into the stage tile kt - 1 used, then multiply.  Copies are issued
-    // unconditionally (past the end the last tile is fetched again, unused) so
-    // the count of copies in flight is the same at every step.
+    // 2 NI copy instructions each per wave), then start the copy of tile
+    // kt + 3 into the stage tile kt - 1 used, then multiply.  Copies are
+    // issued unconditionally (past the end the last tile is fetched again,
+    // unused) so the count of copies in flight is the same at every step.
     auto step = [&](int kt, const uint16_t* tA, const uint16_t* tB, uint16_t* nA, uint16_t* nB) {
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        if constexpr (NI == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         // a bare barrier: a fenced one would also wait for the later stages'
         // copies (the LDS reads of the previous step completed before their
         // MFMAs issued, so the stage refilled below is free)
         __builtin_amdgcn_s_barrier();
-        mt_load(c, wave, kb + min(kt + 3, nk - 1) * kMtBK, nA, nB);
+        mt_load(kb + min(kt + 3, nk - 1) * BK, nA, nB);
         compute(tA, tB);
     };
     if (nk > 0) {
-        mt_load(c, wave, kb, sA0, sB0);
-        mt_load(c, wave, kb + min(1, nk - 1) * kMtBK, sA1, sB1);
-        mt_load(c, wave, kb + min(2, nk - 1) * kMtBK, sA2, sB2);
+        mt_load(kb, sA0, sB0);
+        mt_load(kb + min(1, nk - 1) * BK, sA1, sB1);
+        mt_load(kb + min(2, nk - 1) * BK, sA2, sB2);
     }
     for (int kt = 0; kt < nk; kt += 4) {          // nk is a multiple of 4 (the launcher's split)
         step(kt, sA0, sB0, sA3, sB3);
@@ -421,6 +444,113 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
     // output (m, n) of MFMA tile (i, j): lane (r, q) holds rows 4 q + e of column r
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + j * 16 + r;
+            const bool nok = n < g.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * 64 + i * 16 + 4 * q + e;
+                if (nok && m < a.M) store_out(a, split, m, g.c_col0 + n, acc[i][j][e]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// tiled, pipelined, 8 waves (M > 16): 256 x 128 output tiles, waves as 4 x 2
+// owning 64 x 64 each.  A CU's L2 read rate grows with the waves issuing
+// loads (about 45 GB/s with 4 waves, 85 with 8), and a 256 x 128 tile needs
+// fewer bytes per flop than 128 x 128, so this form feeds the MFMAs better.
+// 32-wide k tiles of A (16 KiB) and B (8 KiB) are copied straight into LDS,
+// four stages, three in flight; pieces of a 64-byte row are XOR-permuted by
+// (row / 4) mod 4.  Same read/wait scheme as k_gemm_mt.
+// ---------------------------------------------------------------------------
+constexpr int kW8BM = 256, kW8BN = 128, kW8BK = 32;
+
+template <int TAG, class GA>
+__global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[kW8BM * kW8BK], sA1[kW8BM * kW8BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA2[kW8BM * kW8BK], sA3[kW8BM * kW8BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[kW8BN * kW8BK], sB1[kW8BN * kW8BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB2[kW8BN * kW8BK], sB3[kW8BN * kW8BK];
+    const int tile = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
+    const GemmSeg g = a.seg[find_seg(a, tile)];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
+    const int m0 = mt * kW8BM, n0 = (tile - g.tile0) * kW8BN;
+    // copies per stage: A 16 blocks of 16 rows (2 per wave), B 8 blocks (1 per
+    // wave); lane l of a block stores position l % 4 of row l / 4, holding the
+    // logical piece (l % 4) ^ ((row / 4) % 4); rows past M or N repeat the last
+    const uint16_t* pa[2];
+    const uint16_t* pb;
+    {
+        const int rl = lane >> 2, pp = lane & 3;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = (wave * 2 + i) * 16 + rl;
+            const int am = min(m0 + row, a.M - 1);
+            const int ar = a.a_rows ? a.a_rows[am] : am;
+            pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + ((pp ^ mt_swz<32>(row)) << 3);
+        }
+        const int row = wave * 16 + rl;
+        pb = (const uint16_t*)g.B + (size_t)min(n0 + row, g.N - 1) * g.ldb + ((pp ^ mt_swz<32>(row)) << 3);
+    }
+    const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
+    const int nk = (ke - kb) / kW8BK;
+    auto load = [&](int k0, uint16_t* sA, uint16_t* sB) {
+        dma16(pa[0] + k0, &sA[(wave * 2) * 512]);
+        dma16(pa[1] + k0, &sA[(wave * 2 + 1) * 512]);
+        dma16(pb + k0, &sB[wave * 512]);
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint32_t offA[4], offB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        offA[i] = (uint32_t)mt_off<32>(wm * 64 + i * 16 + r, q) * 2;
+        offB[i] = (uint32_t)mt_off<32>(wn * 64 + i * 16 + r, q) * 2;
+    }
+    auto compute = [&](const uint16_t* tA, const uint16_t* tB) {
+        const uint32_t baseA = lds_addr(tA), baseB = lds_addr(tB);
+        u32x4_t af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = lds_read16(baseA + offA[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = lds_read16(baseB + offB[j]);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]),
+                       "+v"(bf[3]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    };
+    // step kt: its stage landed when at most the two later stages' copies
+    // (3 instructions each per wave) are in flight; refill the stage of kt - 1
+    auto step = [&](int kt, const uint16_t* tA, const uint16_t* tB, uint16_t* nA, uint16_t* nB) {
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        load(kb + min(kt + 3, nk - 1) * kW8BK, nA, nB);
+        compute(tA, tB);
+    };
+    if (nk > 0) {
+        load(kb, sA0, sB0);
+        load(kb + min(1, nk - 1) * kW8BK, sA1, sB1);
+        load(kb + min(2, nk - 1) * kW8BK, sA2, sB2);
+    }
+    for (int kt = 0; kt < nk; kt += 4) {          // nk is a multiple of 4 (the launcher's split)
+        step(kt, sA0, sB0, sA3, sB3);
+        step(kt + 1, sA1, sB1, sA0, sB0);
+        step(kt + 2, sA2, sB2, sA1, sB1);
+        step(kt + 3, sA3, sB3, sA2, sB2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -663,23 +793,27 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         hipLaunchKernelGGL(k_gemm_f32<GA>, grid, dim3(64), 0, st, a);
         e = hipGetLastError();
     } else {
-        // the pipelined kernel takes K in 256-wide groups (four 64-wide stages)
+        // kernels: k_gemm_w8 (256 x 128 tiles, 8 waves) when the column tiles
+        // alone give at least half a workgroup per CU; else k_gemm_mt
+        // (128 x 128, 4 waves) with K split to about one workgroup per CU;
+        // both take K in groups of four stages.  k_gemm_tiled otherwise.
         const bool pipelined = a.K % 256 == 0;
         const int NT = 128;
-        const int MT = pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
-        const int kq = pipelined ? 256 : 64;
         int ntiles = 0;
         for (int s = 0; s < a.nseg; ++s) {
             a.seg[s].tile0 = ntiles;
             ntiles += (a.seg[s].N + NT - 1) / NT;
         }
         a.ntiles = ntiles;
+        const bool w8 = pipelined && ntiles * ((a.M + kW8BM - 1) / kW8BM) * 2 >= num_cus;
+        const int MT = w8 ? kW8BM : pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
+        const int kq = pipelined ? 256 : 64;
         const int mtiles = (a.M + MT - 1) / MT;
         const int base = ntiles * mtiles;
-        // about one workgroup per CU (128 KiB of LDS each); keep a split at
-        // >= 512 k-values
+        // split K while the grid stays within one workgroup per CU (128 KiB of
+        // LDS each) and a split keeps >= 512 k-values
         int splits = 1;
-        while (base * splits < num_cus && a.K / (splits * 2) >= 512) splits *= 2;
+        while (base * splits * 2 <= num_cus && a.K / (splits * 2) >= 512) splits *= 2;
         const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
         while (splits > 1 && ((size_t)splits * a.M * a.ldc > cap || splits > (a.mode == kPartial ? a.max_splits : 1 << 30)))
             splits /= 2;
@@ -692,9 +826,12 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             if (splits_out) *splits_out = splits;
         }
         const dim3 blk(256), grid3(ntiles, mtiles, splits);
-        if (pipelined) {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_mt<1, GA>), grid3, blk, 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_mt<0, GA>), grid3, blk, 0, st, a);
+        if (w8) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_w8<1, GA>), grid3, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_w8<0, GA>), grid3, dim3(512), 0, st, a);
+        } else if (pipelined) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_mt<1, GA, 64>), grid3, blk, 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_mt<0, GA, 64>), grid3, blk, 0, st, a);
         } else if (MT == 64) {
             if (tag == 1) hipLaunchKernelGGL((k_gemm_tiled<64, 1, GA>), grid3, blk, 0, st, a);
             else hipLaunchKernelGGL((k_gemm_tiled<64, 0, GA>), grid3, blk, 0, st, a);

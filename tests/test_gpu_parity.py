@@ -90,17 +90,26 @@ def test_restored_offset_and_gap(cuda):
     assert s.state() == st
 
 
-def test_batched_propose_matches_oracle(cuda):
+BATCHED = {
+    # vocab 4099: the block-path and unembedding GEMMs take the 4-wave tiled kernel
+    "small_vocab": (4099, [260, 300, 17, 0, 45], [15, 3, 7, 5, 1]),
+    # vocab 20011 over 46 rows: the unembedding has enough column tiles for
+    # the 8-wave 256 x 128 kernel (ragged last tile)
+    "large_vocab": (20011, [130, 0, 70, 33], [15, 15, 15, 15]),
+}
+
+
+@pytest.mark.parametrize("case", list(BATCHED))
+def test_batched_propose_matches_oracle(cuda, case):
     """dflash_propose_batch over sessions of ragged context (one with none)
     equals each session's own oracle propose; one batched sample call draws
     every row with per-session penalties."""
     from block_diffusion_drafter_fwd_amd import propose_batch, sample
     from oracle.sampler import sample_row
-    cfg = synth.config("qwen", layers=2, vocab=4099)
+    vocab, lens, mts = BATCHED[case]
+    cfg = synth.config("qwen", layers=2, vocab=vocab)
     w = synth.make_weights(cfg, seed=4, gains="random")
-    d = _drafter(cfg, w, max_sessions=5)
-    lens = [260, 300, 17, 0, 45]
-    mts = [15, 3, 7, 5, 1]
+    d = _drafter(cfg, w, max_sessions=len(lens))
     pairs = [Pair(d, cfg, w, 512, seed=4, sid=k) for k in range(len(lens))]
     srcs = [synth.FeatureSource(cfg, 4, k) for k in range(len(lens))]
     for k, (pr, L) in enumerate(zip(pairs, lens)):
