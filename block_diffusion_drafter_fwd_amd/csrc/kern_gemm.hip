@@ -56,9 +56,10 @@ __device__ __forceinline__ void store_out(const GA& a, int split, int m, int col
 // ---------------------------------------------------------------------------
 constexpr int kSkWaves = 8;
 
-template <int TPW, int TAG, class GA>
+template <int TPW, int TAG, class GA, int BATCH>
 __global__ __launch_bounds__(512) void k_gemm_skinny(GA a) {
-    constexpr int BATCH = TPW == 1 ? 4 : 2;    // k steps per wave between waits
+    // BATCH: k steps per wave whose loads are in flight together (the launcher
+    // picks the steps each wave has, up to 4, so a wave makes one round trip)
     __shared__ float red[kSkWaves][TPW][256];
     const int b = blockIdx.x, split = blockIdx.y, S = gridDim.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -715,6 +716,28 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* in, int32_t ld, int
     }
 }
 
+template <class GA, int TPW, int TAG>
+static void launch_skinny_b(int batch, dim3 grid, hipStream_t st, const GA& a) {
+    switch (batch) {
+        case 1: hipLaunchKernelGGL((k_gemm_skinny<TPW, TAG, GA, 1>), grid, dim3(512), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_gemm_skinny<TPW, TAG, GA, 2>), grid, dim3(512), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((k_gemm_skinny<TPW, TAG, GA, 3>), grid, dim3(512), 0, st, a); break;
+        default: hipLaunchKernelGGL((k_gemm_skinny<TPW, TAG, GA, 4>), grid, dim3(512), 0, st, a); break;
+    }
+}
+
+template <class GA>
+static hipError_t launch_skinny(int tpw, int tag, int batch, dim3 grid, hipStream_t st, const GA& a) {
+    if (tpw == 2) {
+        if (tag == 1) launch_skinny_b<GA, 2, 1>(batch, grid, st, a);
+        else launch_skinny_b<GA, 2, 0>(batch, grid, st, a);
+    } else {
+        if (tag == 1) launch_skinny_b<GA, 1, 1>(batch, grid, st, a);
+        else launch_skinny_b<GA, 1, 0>(batch, grid, st, a);
+    }
+    return hipGetLastError();
+}
+
 template <class GA>
 static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag,
                             int* splits_out) {
@@ -771,14 +794,9 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         a.splits = splits;
         if (splits_out) *splits_out = splits;
         const dim3 grid2(nwg, splits);
-        if (tpw == 2) {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<2, 1, GA>), grid2, dim3(512), 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_skinny<2, 0, GA>), grid2, dim3(512), 0, st, a);
-        } else {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny<1, 1, GA>), grid2, dim3(512), 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_skinny<1, 0, GA>), grid2, dim3(512), 0, st, a);
-        }
-        return hipGetLastError();
+        const int spw = ((nsteps + splits - 1) / splits + kSkWaves - 1) / kSkWaves;   // k steps per wave
+        const int batch = std::max(1, std::min(4, spw));
+        return launch_skinny<GA>(tpw, tag, batch, grid2, st, a);
     }
     // larger M (or fp32): plain GEMM into C, then the SwiGLU pass if asked;
     // kPartial leaves the split partials [splits][M][ldc] in C
