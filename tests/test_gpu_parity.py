@@ -55,6 +55,13 @@ CASES = {
     "long_small": (synth.config("long", layers=1, vocab=3001),
                    W("lo", "long", context=270, commit_rows=256, rounds=4, max_tokens=7, temperature=1.0,
                      probs=True), 400),
+    # full sizes, in the launch configuration the bench times (5 layers, the
+    # 151936-token unembedding on the persistent kernel; window 512 ring with
+    # 4 layers and a 100352-token vocabulary), short contexts so the oracle
+    # keeps up
+    "qwen_full": (synth.config("qwen"), W("qf", "qwen", context=300, commit_rows=256, rounds=3), 512),
+    "laguna_full": (synth.config("laguna"), W("lf", "laguna", context=1100, commit_rows=300, rounds=3),
+                    512 + 8 - 1),
     "batched_shape_sampling": (synth.config("qwen", layers=1, vocab=3001),
                                W("bs", "qwen", context=130, commit_rows=40, rounds=5, max_tokens=-1,
                                  temperature=0.7, rep_penalty=1.1, history=512, probs=True), 300),
@@ -71,7 +78,11 @@ def test_round_script_parity(cuda, name):
     rep = run_session_script(d, cfg, wl, w, cap, seed=1, sid=3)
     say(f"[parity] {name}: worst {rep.worst} ids compared {rep.ids_compared} skipped {rep.ids_skipped}")
     assert rep.ids_compared > 0
-    assert rep.ids_skipped <= max(2, rep.ids_compared // 10)
+    # at full vocabulary (1e5+ ids of similar magnitude) the top-2 gap falls
+    # inside one bf16 ulp of the top score far more often, so a larger share
+    # of rows is a tie that both answers are right for (skipped, counted)
+    share = 3 if name.endswith("_full") else 10
+    assert rep.ids_skipped <= max(2, rep.ids_compared // share)
 
 
 def test_restored_offset_and_gap(cuda):
