@@ -462,13 +462,9 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
     float* part = (float*)(base + w.part);
     const int32_t ldq = qkv_ld();
     {
-        EmbedArgs e{m_.embed, h, d_info, d_desc, H, R, c.mask_id, bf16()};
+        // embedding rows and the first layer's input norm in one pass
+        EmbedArgs e{m_.embed, h, d_info, d_desc, H, R, c.mask_id, bf16(), m_.layer[0].in_ln, x, c.rms_eps, bf16()};
         HIP_OK(embed(e, st));
-        NormArgs n = norm_args(h, 0, H, R, H);
-        n.nout = 1;
-        n.gain[0] = m_.layer[0].in_ln;
-        n.out[0] = x;
-        HIP_OK(rmsnorm(n, st));
     }
     for (int32_t l = 0; l < c.layers; ++l) {
         const LayerW& lw = m_.layer[l];

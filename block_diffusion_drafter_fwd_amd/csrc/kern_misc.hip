@@ -158,12 +158,25 @@ hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st) {
 // mask token.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
+    __shared__ float sh[4];
+    __shared__ float xs[kNormMaxW];
     const int row = blockIdx.x;
     const RowInfo ri = a.rows[row];
     const SeqDesc sd = a.seqs[ri.seq];
     const int tok = ri.pos == sd.F ? sd.current : a.mask_id;
     const size_t src = (size_t)tok * a.H;
-    for (int j = threadIdx.x; j < a.H; j += 256) a.h[(size_t)row * a.H + j] = ld_any(a.table, src + j, a.w_bf16);
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < a.H; j += 256) {
+        const float v = ld_any(a.table, src + j, a.w_bf16);
+        a.h[(size_t)row * a.H + j] = v;
+        xs[j] = v;
+        ss += v * v;
+    }
+    if (!a.gain) return;                               // uniform over the launch
+    ss = block_sum(ss, sh);
+    const float rstd = 1.f / sqrtf(ss / (float)a.H + a.eps);
+    for (int j = threadIdx.x; j < a.H; j += 256)
+        st_any(a.out, (size_t)row * a.H + j, xs[j] * rstd * ld_any(a.gain, j, a.w_bf16), a.out_bf16);
 }
 
 hipError_t embed(const EmbedArgs& a, hipStream_t st) {

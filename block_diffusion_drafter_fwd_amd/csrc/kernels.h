@@ -112,12 +112,18 @@ struct HeadArgs {
     double inv_freq[64];      // theta^(-2d/D), d < D/2, computed on the host in fp64
 };
 
+// h[row] = table[token of row]; when `gain` is set, also out[row] =
+// RMSNorm(h[row]) * gain (the first layer's input norm), out_bf16 typed
 struct EmbedArgs {
     const void* table;
     float* h;
     const RowInfo* rows;
     const SeqDesc* seqs;
     int32_t H, nrows, mask_id, w_bf16;
+    const void* gain;
+    void* out;
+    float eps;
+    int32_t out_bf16;
 };
 
 struct AttnArgs {
