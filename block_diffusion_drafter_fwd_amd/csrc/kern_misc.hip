@@ -77,9 +77,85 @@ __global__ __launch_bounds__(512) void k_rmsnorm(NormArgs a) {
         }
 }
 
+// four consecutive elements, fp32 or bf16 (16- or 8-byte aligned)
+__device__ __forceinline__ float4 ld4_any(const void* p, size_t i, int bf16) {
+    if (bf16) {
+        const uint2 u = *(const uint2*)((const uint16_t*)p + i);
+        return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                      __uint_as_float(u.y & 0xFFFF0000u)};
+    }
+    return *(const float4*)((const float*)p + i);
+}
+
+__device__ __forceinline__ void st4_any(void* p, size_t i, float4 v, int bf16) {
+    if (bf16) {
+        const uint2 u = {(uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                         (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16)};
+        *(uint2*)((uint16_t*)p + i) = u;
+    } else {
+        *(float4*)((float*)p + i) = v;
+    }
+}
+
+// The same norm with every operand read and written four elements at a time
+// (the launcher checks widths, strides and alignment).  The slice loads of a
+// chunk are issued together, eight at a time (the latency of one L2 round
+// trip, not of one per slice), and added in slice order.
+constexpr int kNormSliceBatch = 8;
+__global__ __launch_bounds__(512) void k_rmsnorm4(NormArgs a) {
+    __shared__ float sh[8];
+    __shared__ float4 xs[kNormMaxW / 4];
+    const int orow = blockIdx.x, grp = blockIdx.y;
+    const int irow = a.row_src ? a.row_src[orow] : orow;
+    const int W = a.width / a.groups, W4 = W >> 2;
+    const size_t ibase = (size_t)irow * a.in_stride + (size_t)grp * W;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < W4; i += 512) {
+        float4 x = a.in ? ld4_any(a.in, ibase + 4 * i, a.in_bf16) : float4{0.f, 0.f, 0.f, 0.f};
+        const float* __restrict__ p = a.part + ibase + 4 * i;
+        for (int s0 = 0; s0 < a.nsplit; s0 += kNormSliceBatch) {
+            float4 v[kNormSliceBatch];
+#pragma unroll
+            for (int j = 0; j < kNormSliceBatch; ++j)   // past the last slice: re-read it, add nothing
+                v[j] = *(const float4*)(p + (size_t)min(s0 + j, a.nsplit - 1) * a.part_stride);
+#pragma unroll
+            for (int j = 0; j < kNormSliceBatch; ++j)
+                if (s0 + j < a.nsplit) {
+                    x.x += v[j].x;
+                    x.y += v[j].y;
+                    x.z += v[j].z;
+                    x.w += v[j].w;
+                }
+        }
+        xs[i] = x;
+        ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+    }
+    ss = block_sum(ss, sh);
+    const float rstd = 1.f / sqrtf(ss / (float)W + a.eps);
+    if (a.writeback)
+        for (int i = threadIdx.x; i < W4; i += 512) *(float4*)(a.writeback + ibase + 4 * i) = xs[i];
+    const size_t obase = (size_t)orow * a.out_stride + (size_t)grp * W;
+    const size_t gbase = (size_t)grp * a.gain_group_stride;
+    for (int o = 0; o < a.nout; ++o)
+        for (int i = threadIdx.x; i < W4; i += 512) {
+            const float4 gn = ld4_any(a.gain[o], gbase + 4 * i, a.gain_bf16);
+            const float4 x = xs[i];
+            st4_any(a.out[o], obase + 4 * i,
+                    float4{x.x * rstd * gn.x, x.y * rstd * gn.y, x.z * rstd * gn.z, x.w * rstd * gn.w}, a.out_bf16);
+        }
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 hipError_t rmsnorm(const NormArgs& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_rmsnorm, dim3(a.rows, a.groups), dim3(512), 0, st, a);
+    const int W = a.width / a.groups;
+    bool v4 = W % 4 == 0 && a.in_stride % 4 == 0 && (a.nsplit == 0 || a.part_stride % 4 == 0) &&
+              a.out_stride % 4 == 0 && a.gain_group_stride % 4 == 0 && aligned16(a.in) && aligned16(a.part) &&
+              aligned16(a.writeback);
+    for (int o = 0; o < a.nout; ++o) v4 = v4 && aligned16(a.gain[o]) && aligned16(a.out[o]);
+    if (v4) hipLaunchKernelGGL(k_rmsnorm4, dim3(a.rows, a.groups), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL(k_rmsnorm, dim3(a.rows, a.groups), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
