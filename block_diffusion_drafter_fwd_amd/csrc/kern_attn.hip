@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
 constexpr int kCombItems = 1024;
 
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
-    __shared__ float sw[kCombItems];
+    __shared__ float sw[kCombItems], sl[kCombItems];
     __shared__ float red[2][2];
     const int brow = blockIdx.x, hq = blockIdx.y, t = threadIdx.x;
     const RowInfo ri = a.rows[brow];
@@ -303,14 +303,29 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
     const int row = (ri.pos - sd.F) * G + hq % G;
     const size_t stride = (size_t)a.Hkv * 64;                    // between items
     const size_t base0 = ((size_t)sd.item0 * a.Hkv + g) * 64 + row;
+    // the output gate's pre-activation (the sum of the projection's K slices),
+    // loaded first so that its latency hides under the combine
+    float gv = 0.f;
+    if (a.gate) {
+        const float* gs = a.gate_src + (size_t)brow * a.gate_ld + a.gate_col + hq;
+        for (int s0 = 0; s0 < a.gate_nsplit; s0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = gs[(size_t)min(s0 + j, a.gate_nsplit - 1) * a.gate_stride];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < a.gate_nsplit) gv += v[j];
+        }
+    }
     float M_run = -INFINITY, L_run = 0.f, acc = 0.f;
     for (int c0 = 0; c0 < sd.nitems; c0 += kCombItems) {
         const int nc = min(kCombItems, sd.nitems - c0);
         float mx = -INFINITY;
         for (int c = t; c < nc; c += 128) {
-            const float m = a.part_ml[(base0 + (size_t)(c0 + c) * stride) * 2];
-            sw[c] = m;
-            mx = fmaxf(mx, m);
+            const float2 ml = *(const float2*)&a.part_ml[(base0 + (size_t)(c0 + c) * stride) * 2];
+            sw[c] = ml.x;
+            sl[c] = ml.y;
+            mx = fmaxf(mx, ml.x);
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
             const float m = sw[c];
             const float w = m == -INFINITY ? 0.f : __expf(m - M);
             sw[c] = w;
-            lsum += w * a.part_ml[(base0 + (size_t)(c0 + c) * stride) * 2 + 1];
+            lsum += w * sl[c];
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
@@ -339,12 +354,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
         __syncthreads();
     }
     float out = acc / L_run;
-    if (a.gate) {
-        float gv = 0.f;
-        for (int sp = 0; sp < a.gate_nsplit; ++sp)
-            gv += a.gate_src[(size_t)sp * a.gate_stride + (size_t)brow * a.gate_ld + a.gate_col + hq];
-        out *= 1.f / (1.f + __expf(-gv));
-    }
+    if (a.gate) out *= 1.f / (1.f + __expf(-gv));
     const size_t o = (size_t)brow * a.Hq * kD + (size_t)hq * kD + t;
     if (a.out_bf16) ((uint16_t*)a.out)[o] = f2bf(out);
     else ((float*)a.out)[o] = out;

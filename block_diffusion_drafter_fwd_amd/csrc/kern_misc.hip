@@ -183,12 +183,23 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
     if (task < nq) { kind = 0; head = task; col = a.q_col + head * a.D; }
     else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * a.D; }
     else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * a.D; }
-    const float* src = a.src + (size_t)row * a.ld;
+    const float* src = a.src + (size_t)row * a.ld + col + lane;
     float x1 = 0.f, x2 = 0.f;
-    if (act)
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            x1 += src[(size_t)sp * a.src_stride + col + lane];
-            x2 += src[(size_t)sp * a.src_stride + col + lane + half];
+    if (act)   // slices loaded kNormSliceBatch at a time (one L2 round trip each batch), added in order
+        for (int s0 = 0; s0 < a.nsplit; s0 += kNormSliceBatch) {
+            float v1[kNormSliceBatch], v2[kNormSliceBatch];
+#pragma unroll
+            for (int j = 0; j < kNormSliceBatch; ++j) {
+                const size_t o = (size_t)min(s0 + j, a.nsplit - 1) * a.src_stride;
+                v1[j] = src[o];
+                v2[j] = src[o + half];
+            }
+#pragma unroll
+            for (int j = 0; j < kNormSliceBatch; ++j)
+                if (s0 + j < a.nsplit) {
+                    x1 += v1[j];
+                    x2 += v2[j];
+                }
         }
     if (kind != 2) {
         if (a.qk_norm) {
@@ -241,13 +252,24 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
     const SeqDesc sd = a.seqs[ri.seq];
     const int tok = ri.pos == sd.F ? sd.current : a.mask_id;
     const size_t src = (size_t)tok * a.H;
+    // all loads first (into LDS), then the stores: a store to h between two
+    // table loads would make each load wait for the one before
     float ss = 0.f;
-    for (int j = threadIdx.x; j < a.H; j += 256) {
-        const float v = ld_any(a.table, src + j, a.w_bf16);
-        a.h[(size_t)row * a.H + j] = v;
-        xs[j] = v;
-        ss += v * v;
+    if (a.vec4) {
+        for (int j = 4 * threadIdx.x; j < a.H; j += 1024) {
+            const float4 v = ld4_any(a.table, src + j, a.w_bf16);
+            *(float4*)&xs[j] = v;
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+    } else {
+        for (int j = threadIdx.x; j < a.H; j += 256) {
+            const float v = ld_any(a.table, src + j, a.w_bf16);
+            xs[j] = v;
+            ss += v * v;
+        }
     }
+    __syncthreads();
+    for (int j = threadIdx.x; j < a.H; j += 256) a.h[(size_t)row * a.H + j] = xs[j];
     if (!a.gain) return;                               // uniform over the launch
     ss = block_sum(ss, sh);
     const float rstd = 1.f / sqrtf(ss / (float)a.H + a.eps);
@@ -255,8 +277,10 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
         st_any(a.out, (size_t)row * a.H + j, xs[j] * rstd * ld_any(a.gain, j, a.w_bf16), a.out_bf16);
 }
 
-hipError_t embed(const EmbedArgs& a, hipStream_t st) {
-    if (a.nrows <= 0) return hipSuccess;
+hipError_t embed(const EmbedArgs& args, hipStream_t st) {
+    if (args.nrows <= 0) return hipSuccess;
+    EmbedArgs a = args;
+    a.vec4 = a.H % 4 == 0 && aligned16(a.table);
     hipLaunchKernelGGL(k_embed, dim3(a.nrows), dim3(256), 0, st, a);
     return hipGetLastError();
 }

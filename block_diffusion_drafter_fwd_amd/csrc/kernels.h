@@ -124,6 +124,7 @@ struct EmbedArgs {
     void* out;
     float eps;
     int32_t out_bf16;
+    int32_t vec4;             // set by the launcher: rows read four elements at a time
 };
 
 struct AttnArgs {
