@@ -30,7 +30,17 @@ from oracle.numerics import rms_norm
 from oracle.session import OracleSession
 from tests.helpers import rel_err
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _fp64_default():
+    """The library modules of the cross-check take the default dtype: fp64
+    for these tests only (set at import, it would leak into every module
+    collected after this one)."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def _tiny(**kw):
