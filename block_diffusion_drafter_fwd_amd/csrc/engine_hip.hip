@@ -34,6 +34,7 @@ size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kSampleChunk = 4096;
 constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
+constexpr int kAttnShortChunk = 256;                 // below: one attention workgroup per CU
 constexpr int kAttnRoundChunk = 4096;                // longest chunk worth a single resident round
 constexpr int kAttnManyChunk = 2048;                 // chunk when the split runs in several rounds
 constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 32 MiB
@@ -427,16 +428,23 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
     // round, no tail).  Otherwise (many sequences, or very long ones) use
     // kAttnManyChunk-key chunks over several rounds, so that one long
     // sequence does not leave the other workgroups idle; the workspace
-    // bounds the item count.
-    const int32_t target_items = std::max(1, attn_target_wg() / c.kv_heads);
+    // bounds the item count.  When that gives short chunks (little work in
+    // all), one workgroup per CU instead: a second one on a CU only splits
+    // its bandwidth, and every extra item costs a partial to write and to
+    // combine.
     const int32_t nseq = (int32_t)seqs.size();
-    int64_t chunk64 = target_items > nseq ? (total_keys + target_items - nseq - 1) / (target_items - nseq)
-                                          : (int64_t)kAttnRoundChunk + 1;
-    if (chunk64 > kAttnRoundChunk) {
-        const int64_t room = std::max<int64_t>(1, (int64_t)w.items_cap - nseq);
-        chunk64 = std::max<int64_t>(kAttnManyChunk, (total_keys + room - 1) / room);
-    }
-    int32_t chunk = (int32_t)std::max<int64_t>(kAttnMinChunk, (chunk64 + 63) / 64 * 64);
+    auto pick_chunk = [&](int32_t target_wg) {
+        const int32_t target_items = std::max(1, target_wg / c.kv_heads);
+        int64_t chunk64 = target_items > nseq ? (total_keys + target_items - nseq - 1) / (target_items - nseq)
+                                              : (int64_t)kAttnRoundChunk + 1;
+        if (chunk64 > kAttnRoundChunk) {
+            const int64_t room = std::max<int64_t>(1, (int64_t)w.items_cap - nseq);
+            chunk64 = std::max<int64_t>(kAttnManyChunk, (total_keys + room - 1) / room);
+        }
+        return (int32_t)std::max<int64_t>(kAttnMinChunk, (chunk64 + 63) / 64 * 64);
+    };
+    int32_t chunk = pick_chunk(attn_target_wg());
+    if (chunk < kAttnShortChunk) chunk = pick_chunk(cus_);
     int32_t items = 0;
     for (SeqDesc& d : descs) {
         const int32_t nk = d.F + d.M - d.key_lo;
