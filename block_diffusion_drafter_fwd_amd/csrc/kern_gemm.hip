@@ -154,14 +154,14 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GA a) {
         for (int e = 0; e < 4; ++e) red[wave][j][lane * 4 + e] = acc[e];
     }
     __syncthreads();
-    // output (m, nn) of a tile lives at lane nn + 16 (m / 4), element m % 4
+    // output (m, nn) of a tile lives at lane nn + 16 (m / 4), element m % 4;
+    // threads 256 j' .. 256 j' + 255 finish tiles j', j' + 2, ...
     const int t = threadIdx.x;
-    const int j = t >> 8;              // tile of this thread (TPW == 2: threads 256..511 take tile 1)
     const int m = (t & 255) >> 4, nn = t & 15;
-    if (j >= TPW || m >= a.M) return;
+    if (m >= a.M) return;
     const int idx = (nn + 16 * (m >> 2)) * 4 + (m & 3);
     if (pair) {
-        if (j != 0 || b * 16 + nn >= a.seg[0].N) return;
+        if (t >= 256 || b * 16 + nn >= a.seg[0].N) return;
         float gt = 0.f, up = 0.f;
         for (int w = 0; w < kSkWaves; ++w) {
             gt += red[w][0][idx];
@@ -178,20 +178,22 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GA a) {
         }
         return;
     }
-    const int tile = b * TPW + j;
-    if (tile >= a.ntiles) return;
-    const GemmSeg& g = a.seg[find_seg(a, tile)];
-    const int n = (tile - g.tile0) * 16 + nn;
-    if (n >= g.N) return;
-    float s0 = 0.f;
-    for (int w = 0; w < kSkWaves; ++w) s0 += red[w][j][idx];
-    if (a.mode == kPartial) {
-        // this split's share; the consumer of C sums the splits
-        a.C[((size_t)split * a.M + m) * a.ldc + g.c_col0 + n] = s0;
-        return;
+    for (int j = t >> 8; j < TPW; j += 2) {
+        const int tile = b * TPW + j;
+        if (tile >= a.ntiles) return;
+        const GemmSeg& g = a.seg[find_seg(a, tile)];
+        const int n = (tile - g.tile0) * 16 + nn;
+        if (n >= g.N) continue;
+        float s0 = 0.f;
+        for (int w = 0; w < kSkWaves; ++w) s0 += red[w][j][idx];
+        if (a.mode == kPartial) {
+            // this split's share; the consumer of C sums the splits
+            a.C[((size_t)split * a.M + m) * a.ldc + g.c_col0 + n] = s0;
+            continue;
+        }
+        float* p = a.C + (size_t)m * a.ldc + g.c_col0 + n;
+        *p = a.mode == kAccumulate ? *p + s0 : s0;
     }
-    float* p = a.C + (size_t)m * a.ldc + g.c_col0 + n;
-    *p = a.mode == kAccumulate ? *p + s0 : s0;
 }
 
 // ---------------------------------------------------------------------------
@@ -781,14 +783,16 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             }
             return hipGetLastError();
         }
-        // two tiles per workgroup (shared A) when there are enough columns;
-        // kPartial: split K over workgroups until about two workgroups per CU,
-        // keeping at least two 64-wide k steps per wave
-        const int tpw = swiglu ? 2 : ((shared_a && ntiles >= num_cus) ? 2 : 1);
+        // two tiles per workgroup when they share A (the A loads of a k step
+        // serve both); kPartial: split K over workgroups while the grid stays
+        // within four workgroups per CU and every wave keeps a k step (measured
+        // on the M = 16 block shapes: more, shorter workgroups beat fewer, longer
+        // ones until the splits leave waves idle)
+        const int tpw = swiglu ? 2 : (shared_a ? 2 : 1);
         const int nwg = swiglu ? ntiles : (ntiles + tpw - 1) / tpw;
         int splits = 1;
         const int nsteps = a.K / 64;
-        while (a.mode == kPartial && nwg * splits * 2 <= 2 * num_cus && nsteps / (splits * 2 * kSkWaves) >= 2 &&
+        while (a.mode == kPartial && nwg * splits * 2 <= 4 * num_cus && nsteps / (splits * 2) >= kSkWaves &&
                splits * 2 <= a.max_splits)
             splits *= 2;
         a.splits = splits;
