@@ -348,6 +348,17 @@ extern "C" int dflash_committed(dflash_session* s, const int32_t* tokens_host, c
     if (!s->ring && frontier + c.block_size > s->cap)
         return fail(DFLASH_E_CAPACITY, "cache capacity exceeded");
     const char* src = (const char*)features_dev + (size_t)start * s->row_bytes();
+    if (s->pending + fresh < c.flush_rows && s->hist_head + fresh <= kHistory) {
+        // the usual round: the history tokens and the rows in one step
+        int rc = s->ctx->engine->commit_rows(s->view(), s->hist_head, tokens_host + start, fresh,
+                                             s->pending_buf() + (size_t)s->pending * s->row_bytes(), src,
+                                             (size_t)fresh * s->row_bytes(), s->stream);
+        if (rc) return rc;
+        s->hist_head = (s->hist_head + fresh) % kHistory;
+        s->hist_count += fresh;
+        s->pending += fresh;
+        return 0;
+    }
     int rc = append_history(s, tokens_host + start, fresh);
     if (rc) return rc;
     if (s->pending + fresh < c.flush_rows) {

@@ -71,6 +71,13 @@ public:
     virtual int copy_rows(void* dst, const void* src, size_t bytes, void* stream) = 0;
     virtual int write_history(const SessView& s, int32_t slot0, const int32_t* tokens,
                               int32_t count, void* stream) = 0;
+    // write_history and then copy_rows, as one step where the backend can
+    // (the history run must not wrap the ring)
+    virtual int commit_rows(const SessView& s, int32_t slot0, const int32_t* tokens, int32_t count, void* dst,
+                            const void* src, size_t bytes, void* stream) {
+        if (int rc = write_history(s, slot0, tokens, count, stream)) return rc;
+        return bytes ? copy_rows(dst, src, bytes, stream) : 0;
+    }
     virtual int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs,
                             void* ws, int32_t ws_sessions, void* stream) = 0;
     virtual int block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs,

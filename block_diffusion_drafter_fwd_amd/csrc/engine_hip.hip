@@ -120,6 +120,15 @@ public:
         return 0;
     }
 
+    int commit_rows(const SessView& s, int32_t slot0, const int32_t* tokens, int32_t count, void* dst,
+                    const void* src, size_t bytes, void* stream) override {
+        if (count <= kCommitTokens && bytes % 16 == 0 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst & 15) == 0) {
+            HIP_OK(kern::commit_rows(s.hist + slot0, tokens, count, dst, src, bytes, (hipStream_t)stream));
+            return 0;
+        }
+        return Engine::commit_rows(s, slot0, tokens, count, dst, src, bytes, stream);
+    }
+
     int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs, void* ws,
                     int32_t ws_sessions, void* stream) override;
     int block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs, float* logits,

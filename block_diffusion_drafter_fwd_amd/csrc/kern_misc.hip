@@ -310,6 +310,30 @@ hipError_t upload(void* dst, const void* host, size_t bytes, hipStream_t st) {
     return hipSuccess;
 }
 
+__global__ __launch_bounds__(256) void k_commit(CommitArgs a) {
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < a.count; i += 256) a.hist[i] = a.tokens[i];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.n16; i += (int64_t)gridDim.x * 256)
+        a.dst[i] = a.src[i];
+}
+
+hipError_t commit_rows(int32_t* hist, const int32_t* tokens, int32_t count, void* dst, const void* src, size_t bytes,
+                       hipStream_t st) {
+    if (count < 0 || count > kCommitTokens || bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
+        return hipErrorInvalidValue;
+    CommitArgs a;
+    a.hist = hist;
+    a.src = (const uint4*)src;
+    a.dst = (uint4*)dst;
+    a.n16 = (int64_t)(bytes / 16);
+    a.count = count;
+    a.pad = 0;
+    for (int i = 0; i < count; ++i) a.tokens[i] = tokens[i];
+    const int64_t wgs = std::min<int64_t>(1024, std::max<int64_t>(1, (a.n16 + 255) / 256));
+    hipLaunchKernelGGL(k_commit, dim3((unsigned)wgs), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_gather_rows(uint4* dst, const uint64_t* src, size_t row_words) {
     const int row = blockIdx.x;
     const uint4* s = (const uint4*)src[row];

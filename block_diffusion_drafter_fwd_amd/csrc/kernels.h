@@ -160,6 +160,17 @@ struct UploadArgs {
     uint32_t data[kUploadWords];
 };
 
+// history tokens (payload in the kernel arguments) + a 16-byte-aligned copy
+constexpr int kCommitTokens = 256;
+struct CommitArgs {
+    int32_t* hist;
+    const uint4* src;
+    uint4* dst;
+    int64_t n16;              // 16-byte units to copy
+    int32_t count, pad;
+    int32_t tokens[kCommitTokens];
+};
+
 // launchers (return hipError_t of the launch)
 // tag 1 launches a separate instantiation (the unembedding) so that profilers
 // can tell it apart from the per-layer GEMMs
@@ -173,6 +184,11 @@ hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st);
 hipError_t sample(const SampleArgs& a, hipStream_t st);
 hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st);
 hipError_t upload(void* dst, const void* host, size_t bytes, hipStream_t st);
+// count <= kCommitTokens tokens to hist, then bytes from src to dst; returns
+// hipErrorInvalidValue (nothing launched) when bytes or a pointer is not
+// 16-byte aligned
+hipError_t commit_rows(int32_t* hist, const int32_t* tokens, int32_t count, void* dst, const void* src, size_t bytes,
+                       hipStream_t st);
 hipError_t cache_read(const void* cache, int32_t cap, int32_t ring, int32_t Hkv, int32_t D, int32_t layer,
                       int32_t pos0, int32_t count, int32_t bf16, float* k_out, float* v_out, hipStream_t st);
 
