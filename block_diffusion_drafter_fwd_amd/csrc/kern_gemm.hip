@@ -470,29 +470,42 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
 // four stages, three in flight; pieces of a 64-byte row are XOR-permuted by
 // (row / 4) mod 4.  Same read/wait scheme as k_gemm_mt.
 // ---------------------------------------------------------------------------
-constexpr int kW8BM = 256, kW8BN = 128, kW8BK = 32;
+constexpr int kW8BN = 128, kW8BK = 32;
 
-template <int TAG, class GA>
+// MI: 16-row MFMA tiles per wave along M (waves as 4 x 2): MI = 4 gives
+// 256 x 128 output tiles (64 x 64 per wave), MI = 8 gives 512 x 128 (128 x 64
+// per wave: all the rows of a batched unembedding in one tile, so every
+// weight byte is read from HBM once, and twice the products per A/B byte in
+// LDS).  Stages: 4 x (BM x 32 + 128 x 32) bf16 = 96 KiB (MI 4) or 160 KiB.
+template <int MI>
+struct W8 {
+    static constexpr int BM = 64 * MI;
+    static constexpr int ABLK = MI / 2;   // 1 KiB copies of A per wave per stage
+};
+
+template <int TAG, class GA, int MI>
 __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA0[kW8BM * kW8BK], sA1[kW8BM * kW8BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sA2[kW8BM * kW8BK], sA3[kW8BM * kW8BK];
+    constexpr int BM = W8<MI>::BM, ABLK = W8<MI>::ABLK;
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[BM * kW8BK], sA1[BM * kW8BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA2[BM * kW8BK], sA3[BM * kW8BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB0[kW8BN * kW8BK], sB1[kW8BN * kW8BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB2[kW8BN * kW8BK], sB3[kW8BN * kW8BK];
     const int tile = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
     const GemmSeg g = a.seg[find_seg(a, tile)];
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
-    const int m0 = mt * kW8BM, n0 = (tile - g.tile0) * kW8BN;
-    // copies per stage: A 16 blocks of 16 rows (2 per wave), B 8 blocks (1 per
-    // wave); lane l of a block stores position l % 4 of row l / 4, holding the
-    // logical piece (l % 4) ^ ((row / 4) % 4); rows past M or N repeat the last
-    const uint16_t* pa[2];
+    const int m0 = mt * BM, n0 = (tile - g.tile0) * kW8BN;
+    // copies per stage: A BM / 16 blocks of 16 rows (ABLK per wave), B 8
+    // blocks (1 per wave); lane l of a block stores position l % 4 of row
+    // l / 4, holding the logical piece (l % 4) ^ ((row / 4) % 4); rows past M
+    // or N repeat the last
+    const uint16_t* pa[ABLK];
     const uint16_t* pb;
     {
         const int rl = lane >> 2, pp = lane & 3;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = (wave * 2 + i) * 16 + rl;
+        for (int i = 0; i < ABLK; ++i) {
+            const int row = (wave * ABLK + i) * 16 + rl;
             const int am = min(m0 + row, a.M - 1);
             const int ar = a.a_rows ? a.a_rows[am] : am;
             pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + ((pp ^ mt_swz<32>(row)) << 3);
@@ -503,45 +516,52 @@ __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
     const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
     const int nk = (ke - kb) / kW8BK;
     auto load = [&](int k0, uint16_t* sA, uint16_t* sB) {
-        dma16(pa[0] + k0, &sA[(wave * 2) * 512]);
-        dma16(pa[1] + k0, &sA[(wave * 2 + 1) * 512]);
+#pragma unroll
+        for (int i = 0; i < ABLK; ++i) dma16(pa[i] + k0, &sA[(wave * ABLK + i) * 512]);
         dma16(pb + k0, &sB[wave * 512]);
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint32_t offA[4], offB[4];
+    uint32_t offA[MI], offB[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        offA[i] = (uint32_t)mt_off<32>(wm * 64 + i * 16 + r, q) * 2;
-        offB[i] = (uint32_t)mt_off<32>(wn * 64 + i * 16 + r, q) * 2;
-    }
+    for (int i = 0; i < MI; ++i) offA[i] = (uint32_t)mt_off<32>(wm * (16 * MI) + i * 16 + r, q) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) offB[j] = (uint32_t)mt_off<32>(wn * 64 + j * 16 + r, q) * 2;
     auto compute = [&](const uint16_t* tA, const uint16_t* tB) {
         const uint32_t baseA = lds_addr(tA), baseB = lds_addr(tB);
-        u32x4_t af[4], bf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = lds_read16(baseA + offA[i]);
+        u32x4_t bf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) bf[j] = lds_read16(baseB + offB[j]);
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]),
-                       "+v"(bf[3]));
+        // A fragments four at a time (MI = 8: the second four are read while
+        // the first four's products run)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i0 = 0; i0 < MI; i0 += 4) {
+            u32x4_t af[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+            for (int i = 0; i < 4; ++i) af[i] = lds_read16(baseA + offA[i0 + i]);
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]),
+                           "+v"(bf[3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i0 + i][j] = mfma32(af[i], bf[j], acc[i0 + i][j]);
+        }
     };
     // step kt: its stage landed when at most the two later stages' copies
-    // (3 instructions each per wave) are in flight; refill the stage of kt - 1
+    // (ABLK + 1 instructions each per wave) are in flight; refill the stage of kt - 1
     auto step = [&](int kt, const uint16_t* tA, const uint16_t* tB, uint16_t* nA, uint16_t* nB) {
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        if constexpr (ABLK == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         load(kb + min(kt + 3, nk - 1) * kW8BK, nA, nB);
         compute(tA, tB);
     };
+    static_assert(ABLK == 2 || ABLK == 4, "copy waits are written for 2 or 4 A blocks per wave");
     if (nk > 0) {
         load(kb, sA0, sB0);
         load(kb + min(1, nk - 1) * kW8BK, sA1, sB1);
@@ -555,14 +575,14 @@ __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = n0 + wn * 64 + j * 16 + r;
             const bool nok = n < g.N;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int m = m0 + wm * 64 + i * 16 + 4 * q + e;
+                const int m = m0 + wm * (16 * MI) + i * 16 + 4 * q + e;
                 if (nok && m < a.M) store_out(a, split, m, g.c_col0 + n, acc[i][j][e]);
             }
         }
@@ -816,9 +836,11 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         e = hipGetLastError();
     } else {
         // kernels: k_gemm_w8 (256 x 128 tiles, 8 waves) when the column tiles
-        // alone give at least half a workgroup per CU; else k_gemm_mt
+        // alone give at least half a workgroup per CU, with 512 x 128 tiles
+        // when M fits one and there are two column tiles per CU or more (a
+        // batched unembedding: the weights are read once); else k_gemm_mt
         // (128 x 128, 4 waves) with K split to about one workgroup per CU;
-        // both take K in groups of four stages.  k_gemm_tiled otherwise.
+        // all take K in groups of four stages.  k_gemm_tiled otherwise.
         const bool pipelined = a.K % 256 == 0;
         const int NT = 128;
         int ntiles = 0;
@@ -827,8 +849,9 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             ntiles += (a.seg[s].N + NT - 1) / NT;
         }
         a.ntiles = ntiles;
-        const bool w8 = pipelined && ntiles * ((a.M + kW8BM - 1) / kW8BM) * 2 >= num_cus;
-        const int MT = w8 ? kW8BM : pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
+        const bool w8 = pipelined && ntiles * ((a.M + W8<4>::BM - 1) / W8<4>::BM) * 2 >= num_cus;
+        const bool w8big = w8 && a.M > W8<4>::BM && a.M <= W8<8>::BM && ntiles >= 2 * num_cus;
+        const int MT = w8big ? W8<8>::BM : w8 ? W8<4>::BM : pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
         const int kq = pipelined ? 256 : 64;
         const int mtiles = (a.M + MT - 1) / MT;
         const int base = ntiles * mtiles;
@@ -848,9 +871,12 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             if (splits_out) *splits_out = splits;
         }
         const dim3 blk(256), grid3(ntiles, mtiles, splits);
-        if (w8) {
-            if (tag == 1) hipLaunchKernelGGL((k_gemm_w8<1, GA>), grid3, dim3(512), 0, st, a);
-            else hipLaunchKernelGGL((k_gemm_w8<0, GA>), grid3, dim3(512), 0, st, a);
+        if (w8big) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_w8<1, GA, 8>), grid3, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_w8<0, GA, 8>), grid3, dim3(512), 0, st, a);
+        } else if (w8) {
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_w8<1, GA, 4>), grid3, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_w8<0, GA, 4>), grid3, dim3(512), 0, st, a);
         } else if (pipelined) {
             if (tag == 1) hipLaunchKernelGGL((k_gemm_mt<1, GA, 64>), grid3, blk, 0, st, a);
             else hipLaunchKernelGGL((k_gemm_mt<0, GA, 64>), grid3, blk, 0, st, a);

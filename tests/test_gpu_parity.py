@@ -101,12 +101,43 @@ def test_restored_offset_and_gap(cuda):
     assert s.state() == st
 
 
+def test_committed_rows_from_unaligned_features(cuda):
+    """Feature rows whose device address is not 16-byte aligned take the
+    separate history write + copy path; both paths leave the same cache and
+    the same block logits (bit for bit)."""
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg, seed=3)
+    d = _drafter(cfg, w)
+    fs = synth.FeatureSource(cfg, 4)
+    T = 11                                  # below the flush threshold: rows stay pending until propose
+    feats = feats_dev(cfg, fs.features(0, T))
+    flat = torch.empty(feats.numel() + 1, dtype=feats.dtype, device="cuda")
+    flat[1:].copy_(feats.reshape(-1))
+    unaligned = flat[1:].view(feats.shape)  # contiguous, 4-byte aligned
+    assert unaligned.data_ptr() % 16 != 0
+    outs = []
+    for f in (feats, unaligned):
+        s = d.session(128)
+        s.committed(fs.tokens(0, T), f, 0)
+        n, lg, _ = s.propose(int(fs.tokens(T, 1)[0]), cfg.block_size - 1)
+        k, v = s.cache_read(0, 0, T)
+        torch.cuda.synchronize()
+        outs.append((lg[:n].cpu(), k.cpu(), v.cpu()))
+        s.close()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
 BATCHED = {
     # vocab 4099: the block-path and unembedding GEMMs take the 4-wave tiled kernel
     "small_vocab": (4099, [260, 300, 17, 0, 45], [15, 3, 7, 5, 1]),
     # vocab 20011 over 46 rows: the unembedding has enough column tiles for
     # the 8-wave 256 x 128 kernel (ragged last tile)
     "large_vocab": (20011, [130, 0, 70, 33], [15, 15, 15, 15]),
+    # 270 logit rows over vocab 66001 (516 column tiles): the unembedding takes
+    # the 512 x 128 tile form of the 8-wave kernel (all rows in one tile)
+    "rows_over_256": (66001, [37, 0, 52, 18, 90, 25, 61, 44, 33, 70, 29, 48, 56, 21, 64, 39, 27, 81, 45],
+                      [15] * 19, 2),
 }
 
 
@@ -117,7 +148,8 @@ def test_batched_propose_matches_oracle(cuda, case):
     every row with per-session penalties."""
     from block_diffusion_drafter_fwd_amd import propose_batch, sample
     from oracle.sampler import sample_row
-    vocab, lens, mts = BATCHED[case]
+    vocab, lens, mts = BATCHED[case][:3]
+    rounds = BATCHED[case][3] if len(BATCHED[case]) > 3 else 3
     cfg = synth.config("qwen", layers=2, vocab=vocab)
     w = synth.make_weights(cfg, seed=4, gains="random")
     d = _drafter(cfg, w, max_sessions=len(lens))
@@ -129,7 +161,7 @@ def test_batched_propose_matches_oracle(cuda, case):
             pr.committed(srcs[k].tokens(p, T), srcs[k].features(p, T), p)
     rep = Report()
     rng = np.random.default_rng(0)
-    for r in range(3):
+    for r in range(rounds):
         say(f"[parity] batched round {r}")
         cur = [int(x) for x in rng.integers(0, cfg.vocab - 1, len(lens))]
         outs = [[o.propose(c, m) for o in pr.o] for pr, c, m in zip(pairs, cur, mts)]
