@@ -46,13 +46,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// The last sequence with item0 <= item (item0 ascends; sequences without
+// items repeat the next one's).  Every lane of a wave reads one descriptor and
+// the wave counts the hits, so a batch of up to 64 sequences costs one load
+// round trip rather than a binary search's chain of them.
 __device__ __forceinline__ int find_item_seq(const SeqDesc* seqs, int nseq, int item) {
-    int lo = 0, hi = nseq - 1;
-    while (lo < hi) {                       // last seq with item0 <= item
-        const int mid = (lo + hi + 1) >> 1;
-        if (seqs[mid].item0 <= item) lo = mid; else hi = mid - 1;
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int b = 0; b < nseq; b += 64) {
+        const int i = b + lane;
+        const bool le = i < nseq && seqs[i].item0 <= item;
+        cnt += __popcll(__ballot(le));
     }
-    return lo;
+    return cnt - 1;                         // seqs[0].item0 == 0 <= item
 }
 
 // (bitwise, not short-circuit: keeps the masking branch-free)
