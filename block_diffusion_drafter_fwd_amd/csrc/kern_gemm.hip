@@ -310,12 +310,15 @@ struct MtRows {
     const uint16_t* pb[kInst];
 };
 
-// 16-byte pieces of a BK-wide row are XOR-permuted by the row's position in
-// its 256-byte bank cycle, so a fragment read of 16 rows hits 64 banks
+// 16-byte pieces of a BK-wide row are XOR-permuted by row / 2, so that the
+// fragment reads (16 rows, one piece each) are free of bank conflicts: with
+// 64-byte rows, row / 4 as the key left a two-way conflict in every read
+// (rocprofv3 SQ_LDS_BANK_CONFLICT: 4.0 stall cycles per LDS instruction,
+// 0 with row / 2)
 template <int BK>
 __device__ __forceinline__ int mt_swz(int row) {
-    constexpr int P = BK / 8, SH = BK == 64 ? 1 : 2;   // pieces per row; log2(rows per bank cycle)
-    return (row >> SH) & (P - 1);
+    constexpr int P = BK / 8;                           // pieces per row
+    return (row >> 1) & (P - 1);
 }
 
 template <int BK>
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
 // fewer bytes per flop than 128 x 128, so this form feeds the MFMAs better.
 // 32-wide k tiles of A (16 KiB) and B (8 KiB) are copied straight into LDS,
 // four stages, three in flight; pieces of a 64-byte row are XOR-permuted by
-// (row / 4) mod 4.  Same read/wait scheme as k_gemm_mt.
+// (row / 2) mod 4.  Same read/wait scheme as k_gemm_mt.
 // ---------------------------------------------------------------------------
 constexpr int kW8BN = 128, kW8BK = 32;
 
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
     const int m0 = mt * BM, n0 = (tile - g.tile0) * kW8BN;
     // copies per stage: A BM / 16 blocks of 16 rows (ABLK per wave), B 8
     // blocks (1 per wave); lane l of a block stores position l % 4 of row
-    // l / 4, holding the logical piece (l % 4) ^ ((row / 4) % 4); rows past M
+    // l / 4, holding the logical piece (l % 4) ^ ((row / 2) % 4); rows past M
     // or N repeat the last
     const uint16_t* pa[ABLK];
     const uint16_t* pb;
