@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512, help="context rows of the oracle sample")
     ap.add_argument("--stages", action="store_true", help="also time the attention, sampler and flush stages")
+    ap.add_argument("--no-width-sweep", action="store_true",
+                    help="skip the propose-time-vs-n sweep and the truncated-block comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (PMC byte-counter calibration)")
     return ap.parse_args()
@@ -288,6 +290,8 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
             kernels["flush_kv"] = mfma_line(2.0 * wl.commit_rows * cfg.hidden * kvn, avg, rows=wl.commit_rows,
                                             avg_launch_us=round(avg * 1e6, 2), launches=l_k)
 
+    sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
+
     return {
         "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
         "value": round(blocks_per_s, 2),
@@ -309,7 +313,52 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
         "flushed_ctx_rows_per_s": round(flush_rows_per_s, 1),
         "roofline": roofline,
         "kernels": kernels,
+        **({"width_sweep": sweep} if sweep else {}),
     }
+
+
+def width_sweep(s, cfg, current, logits, torch, np, reps=20):
+    """Propose time against the drafted width n = 1..B-1 on the session's
+    current context (each propose rewound, so the context is the same for
+    every n), fit as fixed + per-row by least squares; and what drafting only
+    n rows instead of the full block does to rows 1..n: nothing under a causal
+    block mask, a shifted proposal distribution under a bidirectional one
+    (the pages note that only the causal case is exact)."""
+    B = cfg.block_size
+    ns = list(range(1, B))
+    ms = []
+    for n in ns:
+        for _ in range(3):
+            s.propose(current, n, logits=logits)
+            s.commit_block()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            s.propose(current, n, logits=logits)
+            s.commit_block()
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - t) / reps * 1e3)
+    per_row, fixed = np.polyfit(np.array(ns, dtype=np.float64), np.array(ms), 1)
+    _, full, _ = s.propose(current, B - 1, logits=logits)
+    full = full.double().cpu().numpy()
+    s.commit_block()
+    trunc = {"n": [], "max_abs_logit_diff": [], "mean_kl_full_vs_truncated": []}
+    for n in sorted({1, 3, (B - 1) // 2, B - 2} - {0}):
+        k, part, _ = s.propose(current, n, logits=logits)
+        part = part.double().cpu().numpy()
+        s.commit_block()
+
+        def logp(z):
+            z = z - z.max(axis=1, keepdims=True)
+            return z - np.log(np.exp(z).sum(axis=1, keepdims=True))
+        lf, lt = logp(full[:k]), logp(part[:k])
+        kl = float(np.mean(np.sum(np.exp(lf) * (lf - lt), axis=1)))
+        trunc["n"].append(k)
+        trunc["max_abs_logit_diff"].append(float(np.max(np.abs(full[:k] - part[:k]))))
+        trunc["mean_kl_full_vs_truncated"].append(kl)
+    return {"n": ns, "propose_ms": [round(x, 4) for x in ms], "fixed_ms": round(float(fixed), 4),
+            "per_row_ms": round(float(per_row), 5), "block_mask": "causal" if cfg.causal else "bidirectional",
+            "truncation": trunc}
 
 
 def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
@@ -406,6 +455,8 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
                                      launches=l_s)
     for x in sess:
         x.close()
+    sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
+
     return {
         "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
         "value": round(blocks_per_s, 2),

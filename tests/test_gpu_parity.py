@@ -128,6 +128,31 @@ def test_committed_rows_from_unaligned_features(cuda):
         assert torch.equal(a, b)
 
 
+def test_truncated_block_matches_full_block_under_causal_mask(cuda):
+    """Drafting n < B-1 rows gives the full block's first n rows when the block
+    mask is causal (rows never see later rows): the truncation is exact there,
+    as the pages say; the bidirectional shift is measured by bench.py."""
+    cfg = synth.config("tiny")
+    assert cfg.causal
+    w = synth.make_weights(cfg, seed=5)
+    d = _drafter(cfg, w)
+    fs = synth.FeatureSource(cfg, 6)
+    s = d.session(128)
+    s.committed(fs.tokens(0, 40), feats_dev(cfg, fs.features(0, 40)), 0)
+    cur = int(fs.tokens(40, 1)[0])
+    n_full, full, _ = s.propose(cur, cfg.block_size - 1)
+    full = full.cpu().clone()
+    s.commit_block()
+    assert n_full == cfg.block_size - 1
+    for n in range(1, cfg.block_size - 1):
+        k, part, _ = s.propose(cur, n)
+        s.commit_block()
+        assert k == n
+        e = rel_err(part.double().cpu().numpy(), full[:n].double().numpy())
+        assert e < 1e-5, (n, e)
+    s.close()
+
+
 BATCHED = {
     # vocab 4099: the block-path and unembedding GEMMs take the 4-wave tiled kernel
     "small_vocab": (4099, [260, 300, 17, 0, 45], [15, 3, 7, 5, 1]),
