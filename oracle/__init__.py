@@ -17,7 +17,10 @@ It is a plain, slow, float64 NumPy restatement of what the pages define:
   fused QKV, per-head gate, sliding window, drop-before-fc), in
   ``oracle.model``;
 * the batched sampler (penalties from committed history only, temperature,
-  softmax, Gumbel-max with Philox4x64-10), in ``oracle.sampler``.
+  softmax, Gumbel-max with Philox4x64-10), in ``oracle.sampler``;
+* speculative verification of a drafted block against target logits (greedy
+  per-position argmax; the speculative-sampling acceptance rule with the
+  draft's proposal probabilities), in ``oracle.verify``.
 
 With ``emulate_bf16=True`` it rounds to bf16 at the points where the GPU path
 stores bf16 (every GEMM input operand, Q after norm and RoPE, every K/V cache
@@ -26,6 +29,7 @@ entry, the gated attention output); everything else stays float64.
 Pins: every function is checked in ``tests/test_oracle_*.py`` against
 something other than itself (transformers' Qwen3 attention and MLP, torch's
 ``rms_norm`` and ``scaled_dot_product_attention``, numpy's Philox, closed
-forms and invariants the pages state).  The window/gate/aux-norm variant is
+forms and invariants the pages state; verification against the
+rejection-sampling theorem it exists to satisfy).  The window/gate/aux-norm variant is
 pinned only by invariants (no library implements it); see the test headers.
 """
