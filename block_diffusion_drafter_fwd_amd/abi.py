@@ -46,6 +46,10 @@ class SampleParams(ctypes.Structure):
     _fields_ = [("temperature", c_float), ("rep_penalty", c_float), ("history", c_int32), ("round", c_int32)]
 
 
+class VerifyParams(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("round", c_int32)]
+
+
 SYMBOLS = {
     "dflash_last_error": (c_char_p, []),
     "dflash_create": (c_int, [POINTER(Config), POINTER(Weights), POINTER(c_void_p)]),
@@ -64,6 +68,8 @@ SYMBOLS = {
                                      c_void_p, POINTER(c_int32)]),
     "dflash_sample": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p,
                               POINTER(SampleParams), c_void_p, c_void_p]),
+    "dflash_verify": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p,
+                              POINTER(VerifyParams), c_void_p, c_void_p]),
     "dflash_session_state": (c_int, [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32),
                                      POINTER(c_int32), POINTER(c_int64)]),
     "dflash_cache_read": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),

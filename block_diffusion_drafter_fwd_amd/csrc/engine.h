@@ -86,6 +86,9 @@ public:
     virtual int sample(const std::vector<SessView>& sess, const int32_t* row_offsets,
                        const float* logits, const dflash_sample_params& p, int32_t* ids,
                        float* probs, void* ws, int32_t ws_sessions, void* stream) = 0;
+    virtual int verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+                       const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
+                       int32_t* accepted, int32_t* next, void* ws, int32_t ws_sessions, void* stream) = 0;
     virtual int cache_read(const SessView& s, int32_t layer, int32_t pos0, int32_t count,
                            float* k_out, float* v_out, void* stream) = 0;
     // event timing of one named stage (see dflash_profile_begin)

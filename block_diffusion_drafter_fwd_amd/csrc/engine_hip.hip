@@ -45,7 +45,7 @@ struct WsLayout {
     size_t tables;
     size_t ctx_stage, ctx_fc, ctx_c, ctx_x, ctx_kv;
     size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_part, blk_mlp, blk_act;
-    size_t attn_o, attn_ml, part, bitmap, stats;
+    size_t attn_o, attn_ml, part, bitmap, stats, stats2;
     size_t total;
     int32_t r_ctx, r_blk, items_cap, nchunk_max, blk_slices;
 };
@@ -95,6 +95,7 @@ public:
         w.part = put(bf16 ? 4 * kPartCapFloats : 0);
         w.bitmap = put(4 * (size_t)ms * ((c.vocab + 31) / 32));
         w.stats = put(16 * (size_t)w.r_blk * w.nchunk_max);
+        w.stats2 = put(16 * (size_t)w.r_blk * w.nchunk_max);   // verification's second pass
         w.total = o;
         return w;
     }
@@ -136,6 +137,10 @@ public:
     int sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
                const dflash_sample_params& p, int32_t* ids, float* probs, void* ws, int32_t ws_sessions,
                void* stream) override;
+
+    int verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+               const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p, int32_t* accepted,
+               int32_t* next, void* ws, int32_t ws_sessions, void* stream) override;
 
     int cache_read(const SessView& s, int32_t layer, int32_t pos0, int32_t count, float* k_out, float* v_out,
                    void* stream) override {
@@ -609,6 +614,50 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         Timed tm(this, "unembed", st);
         HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 1));
     }
+    return 0;
+}
+
+int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+                      const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
+                      int32_t* accepted, int32_t* next, void* ws, int32_t ws_sessions, void* stream) {
+    const dflash_config& c = m_.cfg;
+    const WsLayout w = layout(ws_sessions);
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const int32_t count = (int32_t)sess.size();
+    const int32_t Rt = draft_offsets[count] + count;     // target rows: n_k + 1 per session
+    if (Rt > w.r_blk) return fail(DFLASH_E_CAPACITY, "verified rows exceed the workspace");
+    std::vector<SeqDesc> descs(count);
+    std::vector<RowInfo> info;
+    for (int32_t k = 0; k < count; ++k) {
+        descs[k] = desc_of(sess[k]);
+        for (int32_t i = 0; i <= draft_offsets[k + 1] - draft_offsets[k]; ++i) info.push_back({k, i});
+    }
+    Tables tb;
+    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+    const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+    const size_t o_offs = tb.add(draft_offsets, sizeof(int32_t) * (size_t)(count + 1));
+    char* tab = base + w.tables;
+    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+    VerifyArgs a{};
+    a.target = target;
+    a.draft_ids = draft_ids;
+    a.draft_probs = draft_probs;
+    a.seqs = (const SeqDesc*)(tab + o_desc);
+    a.rows = (const RowInfo*)(tab + o_info);
+    a.offs = (const int32_t*)(tab + o_offs);
+    a.stats = (float*)(base + w.stats);
+    a.stats2 = (float*)(base + w.stats2);
+    a.accepted = accepted;
+    a.next = next;
+    a.V = c.vocab;
+    a.Rt = Rt;
+    a.nseq = count;
+    a.chunk = kSampleChunk;
+    a.nchunk = w.nchunk_max;
+    a.round = p.round;
+    a.temperature = p.temperature;
+    HIP_OK(kern::verify(a, st));
     return 0;
 }
 

@@ -49,6 +49,12 @@ public:
                      " M=" + std::to_string(b.M) + " cur=" + std::to_string(b.current));
         return 0;
     }
+    int verify(const std::vector<SessView>& sess, const int32_t* offs, const float*, const int32_t*, const float*,
+               const dflash_verify_params& p, int32_t*, int32_t*, void*, int32_t, void*) override {
+        log_line("verify drafts=" + std::to_string(offs[sess.size()]) + " sessions=" +
+                 std::to_string(sess.size()) + " round=" + std::to_string(p.round));
+        return 0;
+    }
     int sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float*,
                const dflash_sample_params& p, int32_t*, float*, void*, int32_t, void*) override {
         std::string s = "sample rows=" + std::to_string(row_offsets[sess.size()]) +

@@ -553,5 +553,158 @@ hipError_t sample(const SampleArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Speculative verification.  Pass 1, per (row, 4096-token chunk): max and
+// sum-exp of row / T and the argmax.  Pass 2 (T > 0), per (row, chunk): the
+// Gumbel-max candidate of the draw that the row would emit, with the row's
+// normaliser from pass 1: over log(max(0, p - q)) on a drafted position,
+// over row / T on the bonus position.  Pass 3, per session: walk the drafted
+// tokens (argmax match, or u * q(x) <= p(x)) to the first rejection and take
+// that row's draw (or argmax).  Draws: Philox4x64-10 under (seed, stream),
+// counters (0, i, round, 1) for the acceptance uniforms and
+// (t div 4, i, round, 2) for the Gumbel draws of row i.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float u23(uint64_t w) { return ((float)(w >> 41) + 0.5f) * 0x1p-23f; }
+
+__global__ __launch_bounds__(256) void k_verify_stats(VerifyArgs a) {
+    const int c = blockIdx.x, r = blockIdx.y;
+    const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
+    const float* z = a.target + (size_t)r * a.V;
+    const float inv_t = a.temperature > 0.f ? 1.f / a.temperature : 1.f;
+    Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    for (int t = t_lo + threadIdx.x; t < t_hi; t += 256) {
+        const float zt = z[t];
+        if (a.temperature > 0.f) {
+            const float sv = zt * inv_t;
+            if (sv > s.m) {
+                s.l = s.l * (s.m == -INFINITY ? 0.f : __expf(s.m - sv)) + 1.f;
+                s.m = sv;
+            } else {
+                s.l += __expf(sv - s.m);
+            }
+        }
+        if (zt > s.best) {      // threads walk ascending ids: a tie keeps the lower one
+            s.best = zt;
+            s.idx = t;
+        }
+    }
+    s = block_stat(s);
+    if (threadIdx.x == 0) {
+        float* o = a.stats + ((size_t)r * a.nchunk + c) * 4;
+        o[0] = s.m;
+        o[1] = s.l;
+        o[2] = s.best;
+        o[3] = __int_as_float(s.idx);
+    }
+}
+
+// the row's statistics over all chunks, merged by the first 64 threads
+__device__ Stat row_stat(const float* stats, int nchunk, int r) {
+    Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    for (int j = threadIdx.x & 63; j < nchunk; j += 64) {
+        const float* o = stats + ((size_t)r * nchunk + j) * 4;
+        stat_merge(s, Stat{o[0], o[1], o[2], __float_as_int(o[3])});
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        Stat b{__shfl_xor(s.m, o), __shfl_xor(s.l, o), __shfl_xor(s.best, o), __shfl_xor(s.idx, o)};
+        stat_merge(s, b);
+    }
+    return s;
+}
+
+__global__ __launch_bounds__(256) void k_verify_next(VerifyArgs a) {
+    __shared__ float tot[2];
+    const int c = blockIdx.x, r = blockIdx.y;
+    if (threadIdx.x < 64) {
+        const Stat s = row_stat(a.stats, a.nchunk, r);
+        if (threadIdx.x == 0) {
+            tot[0] = s.m;
+            tot[1] = s.l;
+        }
+    }
+    __syncthreads();
+    const float M = tot[0], inv_z = 1.f / tot[1], inv_t = 1.f / a.temperature;
+    const RowInfo ri = a.rows[r];
+    const SeqDesc sd = a.seqs[ri.seq];
+    const int n = a.offs[ri.seq + 1] - a.offs[ri.seq];
+    const int i = ri.pos;                      // row within the block: i < n drafted, i == n bonus
+    const float* z = a.target + (size_t)r * a.V;
+    const float* q = i < n ? a.draft_probs + (size_t)(a.offs[ri.seq] + i) * a.V : nullptr;
+    const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
+    Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    for (int qd = (t_lo >> 2) + threadIdx.x; qd * 4 < t_hi; qd += 256) {
+        uint64_t w[4] = {(uint64_t)qd, (uint64_t)i, (uint64_t)a.round, 2};
+        philox4x64_10(w, sd.seed, sd.stream);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = qd * 4 + j;
+            if (t >= t_hi) break;
+            const float sv = z[t] * inv_t;
+            float key;
+            if (q) {
+                const float d = __expf(sv - M) * inv_z - q[t];
+                key = d > 0.f ? logf(d) : -INFINITY;
+            } else {
+                key = sv;
+            }
+            key -= logf(-logf(u23(w[j])));
+            if (key > s.best || (key == s.best && t < s.idx)) {
+                s.best = key;
+                s.idx = t;
+            }
+        }
+    }
+    s = block_stat(s);
+    if (threadIdx.x == 0) {
+        float* o = a.stats2 + ((size_t)r * a.nchunk + c) * 4;
+        o[0] = -INFINITY;
+        o[1] = 0.f;
+        o[2] = s.best;
+        o[3] = __int_as_float(s.idx);
+    }
+}
+
+__global__ __launch_bounds__(64) void k_verify_final(VerifyArgs a) {
+    const int k = blockIdx.x;
+    const int off = a.offs[k], n = a.offs[k + 1] - off, r0 = off + k;
+    const SeqDesc sd = a.seqs[k];
+    int acc = 0;
+    for (; acc < n; ++acc) {
+        const Stat s = row_stat(a.stats, a.nchunk, r0 + acc);
+        const int x = a.draft_ids[off + acc];
+        bool ok;
+        if (a.temperature == 0.f) {
+            ok = s.idx == x;
+        } else {
+            const float p = __expf(a.target[(size_t)(r0 + acc) * a.V + x] / a.temperature - s.m) / s.l;
+            const float q = a.draft_probs[(size_t)(off + acc) * a.V + x];
+            uint64_t w[4] = {0, (uint64_t)acc, (uint64_t)a.round, 1};
+            philox4x64_10(w, sd.seed, sd.stream);
+            ok = u23(w[0]) * q <= p;
+        }
+        if (!ok) break;
+    }
+    const Stat s = row_stat(a.temperature == 0.f ? a.stats : a.stats2, a.nchunk, r0 + acc);
+    if (threadIdx.x == 0) {
+        a.accepted[k] = acc;
+        a.next[k] = s.idx;
+    }
+}
+
+hipError_t verify(const VerifyArgs& a, hipStream_t st) {
+    if (a.nseq <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_verify_stats, dim3(a.nchunk, a.Rt), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.temperature > 0.f) {
+        hipLaunchKernelGGL(k_verify_next, dim3(a.nchunk, a.Rt), dim3(256), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_verify_final, dim3(a.nseq), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace kern
 }  // namespace dflash

@@ -154,6 +154,24 @@ struct SampleArgs {
     float temperature, rho;
 };
 
+// Speculative verification of drafted blocks: session k drafted
+// offs[k+1] - offs[k] tokens and has that many + 1 target rows, from target
+// row offs[k] + k on.
+struct VerifyArgs {
+    const float* target;      // [Rt][V] target logits
+    const int32_t* draft_ids; // [Rd]
+    const float* draft_probs; // [Rd][V] (temperature > 0)
+    const SeqDesc* seqs;      // seed, stream
+    const RowInfo* rows;      // per target row: session, row within its block
+    const int32_t* offs;      // [nseq + 1]
+    float* stats;             // [Rt][nchunk][4]: max / sum-exp of row / T, argmax
+    float* stats2;            // [Rt][nchunk][4]: best Gumbel key of the next-token draw
+    int32_t* accepted;        // [nseq]
+    int32_t* next;            // [nseq]
+    int32_t V, Rt, nseq, chunk, nchunk, round;
+    float temperature;
+};
+
 struct UploadArgs {
     uint32_t* dst;
     int32_t nwords, pad;
@@ -182,6 +200,7 @@ hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st);
 hipError_t embed(const EmbedArgs& a, hipStream_t st);
 hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st);
 hipError_t sample(const SampleArgs& a, hipStream_t st);
+hipError_t verify(const VerifyArgs& a, hipStream_t st);
 hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st);
 hipError_t upload(void* dst, const void* host, size_t bytes, hipStream_t st);
 // count <= kCommitTokens tokens to hist, then bytes from src to dst; returns

@@ -199,6 +199,29 @@ def propose_batch(sessions: Sequence[Session], current: Sequence[int], max_token
     return list(offs), logits
 
 
+def verify(sessions: Sequence[Session], draft_offsets: Sequence[int], target_logits: torch.Tensor,
+           draft_ids: Optional[torch.Tensor], draft_probs: Optional[torch.Tensor], temperature: float,
+           round: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Speculative verification (dflash_verify): per session, the number of
+    accepted drafts and the next token (correction or bonus).  target_logits
+    holds n_k + 1 rows per session, draft_ids / draft_probs n_k rows."""
+    d = sessions[0].d
+    n = len(sessions)
+    acc = torch.empty((n,), dtype=torch.int32, device=d.device)
+    nxt = torch.empty((n,), dtype=torch.int32, device=d.device)
+    for t, dt in ((target_logits, torch.float32), (draft_ids, torch.int32), (draft_probs, torch.float32)):
+        if t is not None and (not t.is_contiguous() or t.device.type != "cuda" or t.dtype != dt):
+            raise ValueError("verify operands: contiguous device tensors, fp32 logits / probabilities, int32 ids")
+    hs = (c_void_p * n)(*[s.h for s in sessions])
+    offs = (c_int32 * (n + 1))(*[int(x) for x in draft_offsets])
+    p = abi.VerifyParams(float(temperature), int(round))
+    check(d.lib, d.lib.dflash_verify(hs, n, offs, target_logits.data_ptr(),
+                                     draft_ids.data_ptr() if draft_ids is not None else None,
+                                     draft_probs.data_ptr() if draft_probs is not None else None,
+                                     byref(p), acc.data_ptr(), nxt.data_ptr()))
+    return acc, nxt
+
+
 def sample(sessions: Sequence[Session], row_offsets: Sequence[int], logits: torch.Tensor, temperature: float,
            rep_penalty: float = 1.0, history: int = 512, round: int = 0,
            probs: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:

@@ -136,6 +136,12 @@ typedef struct {
     int32_t round;           /* Philox counter field: one value per round */
 } dflash_sample_params;
 
+/* Verification settings of one dflash_verify call. */
+typedef struct {
+    float temperature;       /* 0: greedy (argmax) verification */
+    int32_t round;           /* Philox counter field: one value per round */
+} dflash_verify_params;
+
 /* Thread-local text of the last error. */
 const char* dflash_last_error(void);
 
@@ -222,6 +228,34 @@ int dflash_propose_batch(dflash_session* const* sessions, int32_t count, const i
 int dflash_sample(dflash_session* const* sessions, int32_t count, const int32_t* row_offsets,
                   const float* logits, const dflash_sample_params* params, int32_t* ids_out,
                   float* probs_out);
+
+/* Speculative verification of drafted blocks against the target's logits
+ * (the round loop's check of a draft; Ollama dflash.go propose: verification
+ * uses each position's actual proposal distribution to keep the output exact;
+ * mlxcel Laguna PR review: the greedy round loop verifies by a raw
+ * per-position argmax).  Session k drafted n_k = draft_offsets[k+1] -
+ * draft_offsets[k] tokens (0 <= n_k <= blockSize-1), draft_ids[draft_offsets[k]
+ * + i] for i < n_k, and supplies n_k + 1 target rows from row
+ * draft_offsets[k] + k of target_logits (device fp32 [draft_offsets[count] +
+ * count, V]): row i scores the token after block position i, row n_k is the
+ * bonus position.
+ *   temperature 0: accepted_k = the number of leading drafts equal to their
+ *     row's argmax (lowest id on a tie); next_k = the argmax of row accepted_k.
+ *   temperature T > 0 (speculative sampling): with p_i = softmax(row i / T) and
+ *     q_i = draft_probs row draft_offsets[k] + i (device fp32 [rows, V], the
+ *     distribution draft i was drawn from, as dflash_sample returns it), draft
+ *     i is accepted while u_i * q_i(x_i) <= p_i(x_i); at the first rejection,
+ *     row a, next_k is drawn from max(0, p_a - q_a) renormalised, and after n_k
+ *     acceptances from p_{n_k}.  Every emitted token is then an exact draw from
+ *     the target.  Draws are keyed by the session's (seed, stream_id):
+ *     u_i from Philox4x64-10 counter (0, i, round, 1), the draw from row a by
+ *     Gumbel-max with counter (t div 4, a, round, 2).
+ * accepted_out and next_out are device int32 [count].  The session state is
+ * not touched (commit the accepted run with dflash_committed).  Sessions
+ * share context, workspace and stream.  Errors: E_ARG. */
+int dflash_verify(dflash_session* const* sessions, int32_t count, const int32_t* draft_offsets,
+                  const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
+                  const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out);
 
 /* Host-side state: ctxOffset, pending rows, cache length (Offset()), block
  * outstanding flag, and the number of context rows projected so far. */

@@ -1,0 +1,115 @@
+"""GPU parity of speculative verification (dflash_verify) against the oracle.
+
+Random target logits over a ragged vocabulary (9001 ids: three 4096-id
+chunks, the last one short) for five sessions of different draft lengths
+(one with none), greedy and sampling; the drafts are argmax runs broken at
+chosen places (greedy), or draws from a draft distribution q, with q equal
+to the target's p in some rows and concentrated on a token the target gives
+almost no mass in others (sampling).  Decisions whose two sides lie within
+float32 rounding of each other are counted and skipped."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.verify import softmax, verify_block
+
+pytestmark = pytest.mark.gpu
+
+V = 9001
+DRAFTS = [7, 0, 3, 7, 5]
+
+
+@pytest.fixture(scope="module")
+def setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_fwd_amd import Drafter, abi
+    from tests.parity import device_tensors
+    abi.load("hip")
+    cfg = synth.config("tiny", vocab=V)
+    w = synth.make_weights(cfg, seed=9)
+    d = Drafter(cfg, device_tensors(cfg, w), max_sessions=len(DRAFTS))
+    sessions = [d.session(64, seed=100 + k, stream_id=k) for k in range(len(DRAFTS))]
+    return cfg, d, sessions
+
+
+def _offsets():
+    return np.concatenate([[0], np.cumsum(DRAFTS)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("rnd", [0, 1, 2])
+def test_greedy_verify_matches_oracle(setup, rnd):
+    from block_diffusion_drafter_fwd_amd import verify
+    cfg, d, sessions = setup
+    rng = np.random.default_rng(rnd)
+    offs = _offsets()
+    target = rng.normal(scale=2.0, size=(int(offs[-1]) + len(DRAFTS), V)).astype(np.float32)
+    ids = np.zeros(max(1, int(offs[-1])), np.int32)
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        brk = int(rng.integers(0, n + 1))                   # drafts agree with the target up to here
+        for i in range(n):
+            am = int(np.argmax(target[r0 + i]))
+            ids[offs[k] + i] = am if i < brk else (am + 1 + int(rng.integers(0, V - 1))) % V
+    acc, nxt = verify(sessions, offs, torch.from_numpy(target).cuda(), torch.from_numpy(ids).cuda(), None,
+                      0.0, rnd)
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        a, x, _ = verify_block(target[r0:r0 + n + 1], ids[offs[k]:offs[k] + n], None, 0.0, 100 + k, k, rnd)
+        assert (acc[k], nxt[k]) == (a, x), (k, acc[k], nxt[k], a, x)
+
+
+@pytest.mark.parametrize("rnd,temperature", [(0, 1.0), (1, 0.7), (2, 1.0), (3, 0.7)])
+def test_sampling_verify_matches_oracle(setup, rnd, temperature):
+    from block_diffusion_drafter_fwd_amd import verify
+    cfg, d, sessions = setup
+    rng = np.random.default_rng(10 + rnd)
+    offs = _offsets()
+    R = int(offs[-1])
+    target = rng.normal(scale=2.0, size=(R + len(DRAFTS), V)).astype(np.float32)
+    q = np.zeros((max(1, R), V), np.float32)
+    ids = np.zeros(max(1, R), np.int32)
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        for i in range(n):
+            kind = int(rng.integers(0, 3))
+            if kind == 0:                                   # the draft proposes from the target itself
+                qi = softmax(target[r0 + i], temperature)
+            elif kind == 1:                                 # an unrelated draft distribution
+                qi = softmax(rng.normal(scale=2.0, size=V), 1.0)
+            else:                                           # a confident draft on a token the target shuns
+                qi = np.full(V, 1e-6)
+                qi[int(np.argmin(target[r0 + i]))] = 1.0
+                qi /= qi.sum()
+            q[offs[k] + i] = qi.astype(np.float32)
+            qi64 = q[offs[k] + i].astype(np.float64)
+            ids[offs[k] + i] = int(rng.choice(V, p=qi64 / qi64.sum()))
+    acc, nxt = verify(sessions, offs, torch.from_numpy(target).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(q).cuda(), temperature, rnd)
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    compared = skipped = 0
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        a, x, info = verify_block(target[r0:r0 + n + 1], ids[offs[k]:offs[k] + n], q[offs[k]:offs[k] + n],
+                                  temperature, 100 + k, k, rnd)
+        close_test = any(abs(uq - p) <= 1e-5 * max(uq, p, 1e-30) for uq, p in info["tests"])
+        sc = np.sort(info["scores"][np.isfinite(info["scores"])])
+        close_draw = sc.size > 1 and sc[-1] - sc[-2] < 1e-4
+        if close_test or close_draw:
+            skipped += 1
+            continue
+        compared += 1
+        assert (acc[k], nxt[k]) == (a, x), (k, acc[k], nxt[k], a, x)
+    assert compared >= 3 and skipped <= 1, (compared, skipped)
+
+
+def test_verify_rejects_sampling_without_draft_probabilities(setup):
+    from block_diffusion_drafter_fwd_amd import DFlashError, verify
+    cfg, d, sessions = setup
+    offs = _offsets()
+    target = torch.zeros((int(offs[-1]) + len(DRAFTS), V), device="cuda")
+    ids = torch.zeros((int(offs[-1]),), dtype=torch.int32, device="cuda")
+    with pytest.raises(DFlashError):
+        verify(sessions, offs, target, ids, None, 0.5, 0)
