@@ -273,6 +273,25 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
                 sb = n * cfg.vocab * 4 * (2 if wl.probs and wl.temperature > 0 else 1)
                 kernels[name] = hbm_line(sb, avg, alg_bytes_per_launch=sb, avg_launch_us=round(avg * 1e6, 2),
                                          launches=l_s)
+        # verification of one block against synthetic target logits (n drafts,
+        # n + 1 target rows; with the draft probabilities when sampling)
+        from block_diffusion_drafter_fwd_amd import verify
+        gen = torch.Generator(device=dev).manual_seed(0)
+        tgt = torch.randn((n + 1, cfg.vocab), generator=gen, device=dev)
+        dids = torch.randint(0, cfg.vocab, (n,), generator=gen, device=dev, dtype=torch.int32)
+        T = wl.temperature
+        dpr = torch.softmax(torch.randn((n, cfg.vocab), generator=gen, device=dev), dim=1) if T > 0 else None
+        for r in range(3):
+            verify([s], [0, n], tgt, dids, dpr, T, r)
+        st.begin("verify")
+        for r in range(20):
+            verify([s], [0, n], tgt, dids, dpr, T, r)
+        ms_v, l_v = st.end()
+        if l_v:
+            avg = ms_v / 1e3 / l_v
+            vb = (n + 1) * cfg.vocab * 4 + (n * cfg.vocab * 4 if T > 0 else 0)
+            kernels["verify"] = hbm_line(vb, avg, alg_bytes_per_launch=vb, avg_launch_us=round(avg * 1e6, 2),
+                                         launches=l_v)
         if fc_stage and fc_stage[1]:
             avg = fc_stage[0] / 1e3 / fc_stage[1]
             rows = wl.commit_rows

@@ -98,7 +98,8 @@ public:
 
 // Stages that can be timed.
 inline bool known_stage(const std::string& s) {
-    return s == "unembed" || s == "attention" || s == "flush_fc" || s == "flush_kv" || s == "sampler";
+    return s == "unembed" || s == "attention" || s == "flush_fc" || s == "flush_kv" || s == "sampler" ||
+           s == "verify";
 }
 
 // Defined by the backend translation unit that is linked in.

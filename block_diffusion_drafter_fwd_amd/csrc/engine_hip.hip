@@ -657,6 +657,7 @@ int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_of
     a.nchunk = w.nchunk_max;
     a.round = p.round;
     a.temperature = p.temperature;
+    Timed tm(this, "verify", st);
     HIP_OK(kern::verify(a, st));
     return 0;
 }
