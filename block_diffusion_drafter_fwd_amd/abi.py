@@ -70,6 +70,12 @@ SYMBOLS = {
                               POINTER(SampleParams), c_void_p, c_void_p]),
     "dflash_verify": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p,
                               POINTER(VerifyParams), c_void_p, c_void_p]),
+    "dflash_width_policy_create": (c_int, [c_int32, c_float, c_float, c_float, c_float, c_float,
+                                           POINTER(c_void_p)]),
+    "dflash_width_policy_observe": (c_int, [c_void_p, c_int32, c_int32]),
+    "dflash_width_policy_choose": (c_int, [c_void_p]),
+    "dflash_width_policy_rates": (c_int, [c_void_p, POINTER(c_float)]),
+    "dflash_width_policy_destroy": (None, [c_void_p]),
     "dflash_session_state": (c_int, [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32),
                                      POINTER(c_int32), POINTER(c_int64)]),
     "dflash_cache_read": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),

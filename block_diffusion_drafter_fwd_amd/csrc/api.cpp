@@ -558,3 +558,72 @@ extern "C" int dflash_profile_end(dflash_ctx* ctx, double* total_ms, int32_t* la
     if (!ctx || !total_ms || !launches) return fail(DFLASH_E_ARG, "null argument");
     return ctx->engine->profile_end(total_ms, launches);
 }
+
+// ---------------------------------------------------------------------------
+// Draft width controller: per-position conditional acceptance counts with
+// exponential decay (prior: one success in two trials), expected emitted
+// tokens per unit of round time maximised over the width.
+// ---------------------------------------------------------------------------
+struct dflash_width_policy {
+    int32_t max_width;
+    float draft_fixed, draft_per_row, verify_fixed, verify_per_row, decay;
+    std::vector<double> succ, trials;
+};
+
+extern "C" int dflash_width_policy_create(int32_t max_width, float draft_fixed, float draft_per_row,
+                                          float verify_fixed, float verify_per_row, float decay,
+                                          dflash_width_policy** out) {
+    if (!out) return fail(DFLASH_E_ARG, "null argument");
+    *out = nullptr;
+    if (max_width < 1 || max_width > 511 || !(draft_fixed >= 0.f) || !(draft_per_row >= 0.f) ||
+        !(verify_fixed >= 0.f) || !(verify_per_row >= 0.f) || !(decay > 0.f && decay <= 1.f) ||
+        !(draft_fixed + draft_per_row + verify_fixed + verify_per_row > 0.f))
+        return fail(DFLASH_E_ARG, "width policy parameters out of range");
+    auto* p = new dflash_width_policy{max_width, draft_fixed, draft_per_row, verify_fixed, verify_per_row, decay,
+                                      std::vector<double>(max_width, 1.0), std::vector<double>(max_width, 2.0)};
+    *out = p;
+    return 0;
+}
+
+extern "C" int dflash_width_policy_observe(dflash_width_policy* p, int32_t drafted, int32_t accepted) {
+    if (!p) return fail(DFLASH_E_ARG, "null policy");
+    if (drafted < 0 || accepted < 0 || accepted > drafted) return fail(DFLASH_E_ARG, "need 0 <= accepted <= drafted");
+    for (int32_t i = 0; i < p->max_width; ++i) {
+        p->succ[i] *= p->decay;
+        p->trials[i] *= p->decay;
+    }
+    // drafts 1..accepted passed their test; draft accepted+1 (if drafted) failed
+    // its; later drafts were never tested
+    const int32_t tested = std::min(std::min(drafted, accepted + 1), p->max_width);
+    for (int32_t i = 0; i < tested; ++i) {
+        p->trials[i] += 1.0;
+        if (i < accepted) p->succ[i] += 1.0;
+    }
+    return 0;
+}
+
+extern "C" int dflash_width_policy_choose(const dflash_width_policy* p) {
+    if (!p) return fail(DFLASH_E_ARG, "null policy");
+    int best = 1;
+    double best_rate = -1.0, expect = 1.0, run = 1.0;
+    for (int32_t n = 1; n <= p->max_width; ++n) {
+        run *= p->succ[n - 1] / p->trials[n - 1];
+        expect += run;
+        const double cost = p->draft_fixed + (double)p->draft_per_row * n + p->verify_fixed +
+                            (double)p->verify_per_row * (n + 1);
+        const double rate = expect / cost;
+        if (rate > best_rate) {
+            best_rate = rate;
+            best = n;
+        }
+    }
+    return best;
+}
+
+extern "C" int dflash_width_policy_rates(const dflash_width_policy* p, float* out) {
+    if (!p || !out) return fail(DFLASH_E_ARG, "null argument");
+    for (int32_t i = 0; i < p->max_width; ++i) out[i] = (float)(p->succ[i] / p->trials[i]);
+    return 0;
+}
+
+extern "C" void dflash_width_policy_destroy(dflash_width_policy* p) { delete p; }

@@ -238,3 +238,44 @@ def sample(sessions: Sequence[Session], row_offsets: Sequence[int], logits: torc
     check(d.lib, d.lib.dflash_sample(hs, n, offs, logits.data_ptr(), byref(p), ids.data_ptr(),
                                      pr.data_ptr() if pr is not None else None))
     return ids[:R], (pr[:R] if pr is not None else None)
+
+
+class WidthPolicy:
+    """Draft width controller (dflash_width_policy_*): per-position acceptance
+    estimates and the width that maximises expected emitted tokens per unit of
+    round time.  Host-only; ``lib`` defaults to the HIP library."""
+
+    def __init__(self, max_width: int, draft_fixed: float, draft_per_row: float, verify_fixed: float = 0.0,
+                 verify_per_row: float = 0.0, decay: float = 0.95, lib=None):
+        self.lib = lib if lib is not None else abi.load("hip")
+        self.max_width = int(max_width)
+        h = c_void_p()
+        check(self.lib, self.lib.dflash_width_policy_create(self.max_width, float(draft_fixed), float(draft_per_row),
+                                                            float(verify_fixed), float(verify_per_row),
+                                                            float(decay), byref(h)))
+        self.h = h.value
+
+    def observe(self, drafted: int, accepted: int) -> None:
+        check(self.lib, self.lib.dflash_width_policy_observe(self.h, int(drafted), int(accepted)))
+
+    def choose(self) -> int:
+        n = self.lib.dflash_width_policy_choose(self.h)
+        if n < 0:
+            check(self.lib, n)
+        return n
+
+    def rates(self) -> list:
+        buf = (ctypes.c_float * self.max_width)()
+        check(self.lib, self.lib.dflash_width_policy_rates(self.h, buf))
+        return list(buf)
+
+    def close(self) -> None:
+        if self.h:
+            h, self.h = self.h, None
+            self.lib.dflash_width_policy_destroy(h)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass

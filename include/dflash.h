@@ -257,6 +257,28 @@ int dflash_verify(dflash_session* const* sessions, int32_t count, const int32_t*
                   const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
                   const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out);
 
+/* Draft width controller (host only).  The pages: DFlash2 drafts a fixed
+ * seven tokens per round instead of following Ollama's depth controller, whose
+ * shallower picks lose more accepted tokens than they save in verify time.
+ * This controller makes that trade explicit: it keeps, per draft position i,
+ * a decayed estimate of P(draft i accepted | drafts before it accepted)
+ * (prior 1/2), and picks the width n in [1, max_width] that maximises the
+ * expected tokens a round emits, 1 + sum_{j<=n} prod_{i<=j} alpha_i (accepted
+ * drafts plus the correction or bonus token), per unit of round time
+ * draft_fixed + draft_per_row * n + verify_fixed + verify_per_row * (n + 1)
+ * (any time unit; bench.py measures the draft terms).  decay in (0, 1]
+ * weights past rounds.  Errors: E_ARG. */
+typedef struct dflash_width_policy dflash_width_policy;
+int dflash_width_policy_create(int32_t max_width, float draft_fixed, float draft_per_row, float verify_fixed,
+                               float verify_per_row, float decay, dflash_width_policy** out);
+/* One round: `drafted` tokens were proposed and `accepted` of them accepted. */
+int dflash_width_policy_observe(dflash_width_policy* p, int32_t drafted, int32_t accepted);
+/* The width to draft next (>= 1), or a negative error code. */
+int dflash_width_policy_choose(const dflash_width_policy* p);
+/* Current acceptance estimates alpha_1..alpha_max_width into out[max_width]. */
+int dflash_width_policy_rates(const dflash_width_policy* p, float* out);
+void dflash_width_policy_destroy(dflash_width_policy* p);
+
 /* Host-side state: ctxOffset, pending rows, cache length (Offset()), block
  * outstanding flag, and the number of context rows projected so far. */
 int dflash_session_state(const dflash_session* s, int32_t* ctx_offset, int32_t* pending,
