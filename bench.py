@@ -474,8 +474,6 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
                                      launches=l_s)
     for x in sess:
         x.close()
-    sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
-
     return {
         "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
         "value": round(blocks_per_s, 2),
