@@ -36,7 +36,7 @@ constexpr int kSampleChunk = 4096;
 constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
 constexpr int kAttnShortChunk = 256;                 // below: one attention workgroup per CU
 constexpr int kAttnRoundChunk = 4096;                // longest chunk worth a single resident round
-constexpr int kAttnManyChunk = 2048;                 // chunk when the split runs in several rounds
+constexpr int kAttnManyChunk = 4096;                 // chunk when the split runs in several rounds
 constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 32 MiB
 constexpr int kMaxSlicesFc = 8;                      // K slices of the fc GEMM
 constexpr int kMaxSlicesKv = 2;                      // K slices of the context k|v GEMM
