@@ -39,7 +39,7 @@ constexpr int kAttnRoundChunk = 4096;                // longest chunk worth a si
 constexpr int kAttnManyChunk = 4096;                 // chunk when the split runs in several rounds
 constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 32 MiB
 constexpr int kMaxSlicesFc = 8;                      // K slices of the fc GEMM
-constexpr int kMaxSlicesKv = 2;                      // K slices of the context k|v GEMM
+constexpr int kMaxSlicesKv = 4;                      // K slices of the context k|v GEMM
 
 struct WsLayout {
     size_t tables;

@@ -343,6 +343,22 @@ __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
     return v;
 }
 
+// Work item (column tile, row tile, K split) of this workgroup.  Workgroups
+// are dispatched round-robin over the 8 XCDs, each with its own L2; when the
+// grid divides evenly, consecutive items (column tiles first, then row tiles,
+// then splits: the items that share A rows) are gathered onto one XCD, so an
+// XCD reads its K slice of A once from HBM and then from its L2.
+struct TileItem {
+    int tile, mt, split;
+};
+__device__ __forceinline__ TileItem tile_item(int xcd_remap) {
+    const int nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+    int l = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    if (xcd_remap && (total & 7) == 0) l = (l & 7) * (total >> 3) + (l >> 3);
+    const int r = l / nx;
+    return TileItem{l - r * nx, r % ny, r / ny};
+}
+
 template <int TAG, class GA, int BK>
 __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
     constexpr int KS = BK / 32;                         // 32-wide MFMA k steps per stage
@@ -351,7 +367,8 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
     __shared__ __attribute__((aligned(16))) uint16_t sA2[kMtBM * BK], sA3[kMtBM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB0[kMtBN * BK], sB1[kMtBN * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB2[kMtBN * BK], sB3[kMtBN * BK];
-    const int tile = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
+    const TileItem it = tile_item(a.xcd_remap);
+    const int tile = it.tile, mt = it.mt, split = it.split;
     const GemmSeg g = a.seg[find_seg(a, tile)];
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
@@ -493,7 +510,8 @@ __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
     __shared__ __attribute__((aligned(16))) uint16_t sA2[BM * kW8BK], sA3[BM * kW8BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB0[kW8BN * kW8BK], sB1[kW8BN * kW8BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB2[kW8BN * kW8BK], sB3[kW8BN * kW8BK];
-    const int tile = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
+    const TileItem it = tile_item(a.xcd_remap);
+    const int tile = it.tile, mt = it.mt, split = it.split;
     const GemmSeg g = a.seg[find_seg(a, tile)];
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
@@ -852,10 +870,25 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             ntiles += (a.seg[s].N + NT - 1) / NT;
         }
         a.ntiles = ntiles;
-        const bool w8 = pipelined && ntiles * ((a.M + W8<4>::BM - 1) / W8<4>::BM) * 2 >= num_cus;
+        const int mt4 = (a.M + W8<4>::BM - 1) / W8<4>::BM;
+        bool w8 = pipelined && ntiles * mt4 * 2 >= num_cus;
         const bool w8big = w8 && a.M > W8<4>::BM && a.M <= W8<8>::BM && ntiles >= 2 * num_cus;
+        // 256-row tiles also for M > 128 when K splits (any count within the
+        // partial slices the consumer sums, each >= 512 k-values) fill at
+        // least 7/8 of the CUs: measured on the 256-row flush shapes (context
+        // k|v 24.3 vs 26.5 us, 4096-wide fc 66 vs 70 us); where they cannot,
+        // 128 x 128 tiles with power-of-two splits
+        int w4_splits = 0;
+        if (pipelined && !w8 && a.M > kMtBM && a.mode == kPartial) {
+            int s = std::min(a.max_splits, num_cus / (ntiles * mt4));
+            while (s > 1 && a.K / s < 512) --s;
+            if (s >= 1 && ntiles * mt4 * s * 8 >= 7 * num_cus) {
+                w8 = true;
+                w4_splits = s;
+            }
+        }
         const int MT = w8big ? W8<8>::BM : w8 ? W8<4>::BM : pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
-        const int kq = pipelined ? 256 : 64;
+        const int kq = w4_splits ? 128 : pipelined ? 256 : 64;
         const int mtiles = (a.M + MT - 1) / MT;
         const int base = ntiles * mtiles;
         // split K while the grid stays within one workgroup per CU (128 KiB of
@@ -865,10 +898,12 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
         while (splits > 1 && ((size_t)splits * a.M * a.ldc > cap || splits > (a.mode == kPartial ? a.max_splits : 1 << 30)))
             splits /= 2;
+        if (w4_splits) splits = w4_splits;
         int kc = ((a.K + splits - 1) / splits + kq - 1) / kq * kq;
         splits = (a.K + kc - 1) / kc;
         a.splits = splits;
         a.kc = kc;
+        a.xcd_remap = 1;
         if (a.mode == kPartial) {
             a.part = a.C;            // the partial slices are the output
             if (splits_out) *splits_out = splits;

@@ -62,6 +62,7 @@ struct GemmHead {
     float* part;              // split-K partials [splits][M][ldc]
     int32_t nseg, ntiles;
     int32_t col_lo, col_hi;   // columns covered by the segments
+    int32_t xcd_remap, pad;   // tiled kernels: gather the items that share A onto one XCD
 };
 
 // The argument block is copied to the device at every launch and its cache
