@@ -30,12 +30,6 @@ namespace kern {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-__device__ __forceinline__ uint16_t f2bf(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -293,26 +287,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     }
 }
 
-// One workgroup per (block row, q head), one thread per output dim.  The
-// chunk maxima and sums are staged in LDS (independent loads), turned into
-// weights exp(m_c - M), and the partial outputs are summed with those
-// weights; chunks are taken 1024 at a time with a running merge.
+// One workgroup per (block row, 4 q heads): 32 threads per head, four
+// output dims each (float4 partial loads), so a batched launch is one
+// resident round of workgroups instead of several rounds of one thread per
+// dim.  The chunk maxima and sums are staged in LDS (independent loads),
+// turned into weights exp(m_c - M), and the partial outputs are summed with
+// those weights; chunks are taken kCombItems at a time with a running merge.
 constexpr int kCombItems = 1024;
+constexpr int kCombHeads = 4;
 
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
-    __shared__ float sw[kCombItems], sl[kCombItems];
-    __shared__ float red[2][2];
-    const int brow = blockIdx.x, hq = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(32 * kCombHeads) void k_attn_combine(AttnArgs a) {
+    __shared__ float sw[kCombHeads][kCombItems], sl[kCombHeads][kCombItems];
+    const int brow = blockIdx.x, t = threadIdx.x, hl = t >> 5, lane = t & 31;
+    const int hq = blockIdx.y * kCombHeads + hl;
+    const bool act = hq < a.Hq;
     const RowInfo ri = a.rows[brow];
     const SeqDesc sd = a.seqs[ri.seq];
-    const int G = a.Hq / a.Hkv, g = hq / G;
-    const int row = (ri.pos - sd.F) * G + hq % G;
+    const int G = a.Hq / a.Hkv, hqc = act ? hq : 0, g = hqc / G;
+    const int row = (ri.pos - sd.F) * G + hqc % G;
     const size_t stride = (size_t)a.Hkv * 64;                    // between items
     const size_t base0 = ((size_t)sd.item0 * a.Hkv + g) * 64 + row;
     // the output gate's pre-activation (the sum of the projection's K slices),
     // loaded first so that its latency hides under the combine
     float gv = 0.f;
-    if (a.gate) {
+    if (a.gate && act) {
         const float* gs = a.gate_src + (size_t)brow * a.gate_ld + a.gate_col + hq;
         for (int s0 = 0; s0 < a.gate_nsplit; s0 += 8) {
             float v[8];
@@ -323,47 +321,63 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
                 if (s0 + j < a.gate_nsplit) gv += v[j];
         }
     }
-    float M_run = -INFINITY, L_run = 0.f, acc = 0.f;
+    float M_run = -INFINITY, L_run = 0.f;
+    float4 acc = float4{0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < sd.nitems; c0 += kCombItems) {
         const int nc = min(kCombItems, sd.nitems - c0);
         float mx = -INFINITY;
-        for (int c = t; c < nc; c += 128) {
-            const float2 ml = *(const float2*)&a.part_ml[(base0 + (size_t)(c0 + c) * stride) * 2];
-            sw[c] = ml.x;
-            sl[c] = ml.y;
-            mx = fmaxf(mx, ml.x);
-        }
+        if (act)
+            for (int c = lane; c < nc; c += 32) {
+                const float2 ml = *(const float2*)&a.part_ml[(base0 + (size_t)(c0 + c) * stride) * 2];
+                sw[hl][c] = ml.x;
+                sl[hl][c] = ml.y;
+                mx = fmaxf(mx, ml.x);
+            }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        if ((t & 63) == 0) red[0][t >> 6] = mx;
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));   // within the head's 32 lanes
         __syncthreads();
-        const float M = fmaxf(fmaxf(red[0][0], red[0][1]), M_run);
+        const float M = fmaxf(mx, M_run);
         float lsum = 0.f;
-        for (int c = t; c < nc; c += 128) {
-            const float m = sw[c];
+        for (int c = lane; c < nc; c += 32) {
+            const float m = sw[hl][c];
             const float w = m == -INFINITY ? 0.f : __expf(m - M);
-            sw[c] = w;
-            lsum += w * sl[c];
+            sw[hl][c] = w;
+            lsum += w * sl[hl][c];
         }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
-        if ((t & 63) == 0) red[1][t >> 6] = lsum;
+        for (int o = 16; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
         __syncthreads();
         const float sc = M_run == -INFINITY ? 0.f : __expf(M_run - M);
-        float part = 0.f;
-        const float* po = a.part_o + (base0 + (size_t)c0 * stride) * kD + t;
+        float4 part = float4{0.f, 0.f, 0.f, 0.f};
+        if (act) {
+            const float* po = a.part_o + (base0 + (size_t)c0 * stride) * kD + 4 * lane;
 #pragma unroll 8
-        for (int c = 0; c < nc; ++c) part += sw[c] * po[(size_t)c * stride * kD];
-        acc = acc * sc + part;
-        L_run = L_run * sc + red[1][0] + red[1][1];
+            for (int c = 0; c < nc; ++c) {
+                const float w = sw[hl][c];
+                const float4 v = *(const float4*)(po + (size_t)c * stride * kD);
+                part.x += w * v.x;
+                part.y += w * v.y;
+                part.z += w * v.z;
+                part.w += w * v.w;
+            }
+        }
+        acc.x = acc.x * sc + part.x;
+        acc.y = acc.y * sc + part.y;
+        acc.z = acc.z * sc + part.z;
+        acc.w = acc.w * sc + part.w;
+        L_run = L_run * sc + lsum;
         M_run = M;
         __syncthreads();
     }
-    float out = acc / L_run;
-    if (a.gate) out *= 1.f / (1.f + __expf(-gv));
-    const size_t o = (size_t)brow * a.Hq * kD + (size_t)hq * kD + t;
-    if (a.out_bf16) ((uint16_t*)a.out)[o] = f2bf(out);
-    else ((float*)a.out)[o] = out;
+    if (!act) return;
+    float f = 1.f / L_run;
+    if (a.gate) f *= 1.f / (1.f + __expf(-gv));
+    const size_t o = (size_t)brow * a.Hq * kD + (size_t)hq * kD + 4 * lane;
+    if (a.out_bf16) {
+        *(uint2*)((uint16_t*)a.out + o) = uint2{pack_bf16(acc.x * f, acc.y * f), pack_bf16(acc.z * f, acc.w * f)};
+    } else {
+        *(float4*)((float*)a.out + o) = float4{acc.x * f, acc.y * f, acc.z * f, acc.w * f};
+    }
 }
 
 // fp32: one workgroup of 64 threads per (block row, q head); D <= 64
@@ -432,7 +446,8 @@ hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st) {
     hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items, a.Hkv), dim3(kAttnThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, a.Hq), dim3(kD), 0, st, a);
+    hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, (a.Hq + kCombHeads - 1) / kCombHeads), dim3(32 * kCombHeads),
+                       0, st, a);
     return hipGetLastError();
 }
 
