@@ -454,6 +454,17 @@ __device__ Stat block_stat(Stat s) {
     return t;
 }
 
+// -ln(-ln u) on the hardware base-2 logarithm (u in [2^-24, 1 - 2^-24], so
+// both arguments are normal floats)
+__device__ __forceinline__ float gumbel(float u) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u) * kLn2) * kLn2;
+}
+
+// Per (row, vocabulary chunk): max and sum-exp of z'/T (online), and the
+// Gumbel-max candidate (or the argmax when greedy).  Four consecutive tokens
+// per thread: one 16-byte logits load, one history-bitmap word, one Philox
+// call whose four words are the tokens' draws.
 __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int c = blockIdx.x, r = blockIdx.y;
     const RowInfo ri = a.rows[r];
@@ -462,37 +473,59 @@ __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     const bool greedy = a.temperature == 0.f;
+    const float inv_t = greedy ? 0.f : 1.f / a.temperature;
+    const bool vec = (a.V & 3) == 0;
+    const float* zr = a.logits + (size_t)r * a.V;
     for (int qd = (t_lo >> 2) + threadIdx.x; qd * 4 < t_hi; qd += 256) {
-        uint64_t w[4] = {0, 0, 0, 0};
-        if (!greedy) {
-            w[0] = (uint64_t)qd;
-            w[1] = (uint64_t)ri.pos;
-            w[2] = (uint64_t)a.round;
-            w[3] = 0;
-            philox4x64_10(w, sd.seed, sd.stream);
+        const int t0 = qd * 4;
+        float z[4];
+        if (vec) {   // t0 + 3 < V: V and the chunk bounds are multiples of 4
+            const float4 v = *(const float4*)(zr + t0);
+            z[0] = v.x;
+            z[1] = v.y;
+            z[2] = v.z;
+            z[3] = v.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) z[j] = t0 + j < t_hi ? zr[t0 + j] : -INFINITY;
+        }
+        if (a.use_penalty) {
+            const uint32_t word = bm[t0 >> 5] >> (t0 & 31);   // the four tokens share one word
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((word >> j) & 1u) z[j] = z[j] > 0.f ? z[j] / a.rho : z[j] * a.rho;
+        }
+        if (greedy) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (t0 + j < t_hi && (z[j] > s.best || (z[j] == s.best && t0 + j < s.idx))) {
+                    s.best = z[j];
+                    s.idx = t0 + j;
+                }
+            continue;
+        }
+        uint64_t w[4] = {(uint64_t)qd, (uint64_t)ri.pos, (uint64_t)a.round, 0};
+        philox4x64_10(w, sd.seed, sd.stream);
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sv[j] = t0 + j < t_hi ? z[j] * inv_t : -INFINITY;
+            mx = fmaxf(mx, sv[j]);
+        }
+        if (mx > s.m) {
+            s.l = s.m == -INFINITY ? 0.f : s.l * __expf(s.m - mx);
+            s.m = mx;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int t = qd * 4 + j;
-            if (t >= t_hi) break;
-            const float z = penalized(a, bm, r, t);
-            float key;
-            if (greedy) {
-                key = z;
-            } else {
-                const float sv = z / a.temperature;
-                if (sv > s.m) {
-                    s.l = s.l * (s.m == -INFINITY ? 0.f : __expf(s.m - sv)) + 1.f;
-                    s.m = sv;
-                } else {
-                    s.l += __expf(sv - s.m);
-                }
-                const float u = ((float)(w[j] >> 41) + 0.5f) * 0x1p-23f;
-                key = sv - logf(-logf(u));
-            }
-            if (key > s.best || (key == s.best && t < s.idx)) {
+            if (t0 + j >= t_hi) break;
+            s.l += __expf(sv[j] - s.m);
+            const float u = ((float)(w[j] >> 41) + 0.5f) * 0x1p-23f;
+            const float key = sv[j] + gumbel(u);
+            if (key > s.best || (key == s.best && t0 + j < s.idx)) {
                 s.best = key;
-                s.idx = t;
+                s.idx = t0 + j;
             }
         }
     }
@@ -532,9 +565,10 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     const RowInfo ri = a.rows[r];
     const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
+    const float inv_t = 1.f / a.temperature, inv_z = 1.f / Z;
     for (int t = t_lo + threadIdx.x; t < t_hi; t += 256) {
-        const float sv = penalized(a, bm, r, t) / a.temperature;
-        a.probs[(size_t)r * a.V + t] = __expf(sv - M) / Z;
+        const float sv = penalized(a, bm, r, t) * inv_t;   // as in k_sample_stats
+        a.probs[(size_t)r * a.V + t] = __expf(sv - M) * inv_z;
     }
 }
 
