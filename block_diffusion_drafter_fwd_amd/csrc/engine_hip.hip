@@ -17,6 +17,8 @@
 // CUs; the slices are added by whichever kernel reads the result next, so no
 // reduction pass is launched.
 #include <algorithm>
+#include <functional>
+#include <queue>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -36,7 +38,8 @@ constexpr int kSampleChunk = 4096;
 constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
 constexpr int kAttnShortChunk = 256;                 // below: one attention workgroup per CU
 constexpr int kAttnRoundChunk = 4096;                // longest chunk worth a single resident round
-constexpr int kAttnManyChunk = 4096;                 // chunk when the split runs in several rounds
+constexpr int kAttnManyLo = 1024, kAttnManyHi = 4096;  // chunk range when the split runs in several rounds
+constexpr int kAttnItemStartTiles = 6;               // an item's start-up, in 64-key tiles (measured fit)
 constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 32 MiB
 constexpr int kMaxSlicesFc = 8;                      // K slices of the fc GEMM
 constexpr int kMaxSlicesKv = 4;                      // K slices of the context k|v GEMM
@@ -75,7 +78,8 @@ public:
         size_t o = 0;
         auto put = [&](size_t bytes) { size_t at = o; o += al(bytes); return at; };
         w.tables = put(sizeof(SeqDesc) * (size_t)ms + sizeof(RowInfo) * (size_t)rmax +
-                       sizeof(int32_t) * (size_t)w.r_blk + sizeof(uint64_t) * (size_t)w.r_ctx + 64);
+                       sizeof(int32_t) * (size_t)w.r_blk + sizeof(uint64_t) * (size_t)w.r_ctx +
+                       sizeof(uint32_t) * (size_t)w.items_cap + 128);
         w.ctx_stage = put(act * (size_t)w.r_ctx * m_.fc_in);
         w.ctx_fc = put(4 * (size_t)kMaxSlicesFc * w.r_ctx * H);
         w.ctx_c = put(4 * (size_t)w.r_ctx * H);
@@ -439,21 +443,58 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
     // attention split: every sequence's keys in chunks of one size.  If one
     // resident round of workgroups (target_items per kv head) can hold the
     // whole split with chunks of at most kAttnRoundChunk keys, use that (one
-    // round, no tail).  Otherwise (many sequences, or very long ones) use
-    // kAttnManyChunk-key chunks over several rounds, so that one long
-    // sequence does not leave the other workgroups idle; the workspace
-    // bounds the item count.  When that gives short chunks (little work in
+    // round, no tail).  Otherwise (many sequences, or very long ones) split
+    // into chunks of 1024..4096 keys over several rounds, so that one long
+    // sequence does not leave the other workgroups idle, the size chosen by
+    // the schedule model below; the workspace bounds the item count.  When
+    // that gives short chunks (little work in
     // all), one workgroup per CU instead: a second one on a CU only splits
     // its bandwidth, and every extra item costs a partial to write and to
     // combine.
     const int32_t nseq = (int32_t)seqs.size();
+    // Several rounds: items are dispatched largest first (every kv head of an
+    // item side by side), so the chunk decides how evenly the resident slots
+    // finish.  Each candidate's schedule is simulated on the host (an item
+    // costs its 64-key tiles plus a fixed start-up) and the earliest finish
+    // wins; the model ranks the batched workload's measured chunk times
+    // (2048..4096 keys) in the measured order.
+    auto many_chunk = [&](int32_t slots, int64_t min_chunk) {
+        int32_t best = 0;
+        int64_t best_t = 0;
+        std::vector<int32_t> sizes;
+        for (int32_t ch = kAttnManyLo; ch <= kAttnManyHi; ch += 512) {
+            if (ch < min_chunk) continue;
+            sizes.clear();
+            for (const SeqDesc& d : descs) {
+                const int32_t nk = d.F + d.M - d.key_lo;
+                for (int32_t k0 = 0; k0 < nk; k0 += ch) sizes.push_back((std::min(ch, nk - k0) + 63) / 64);
+            }
+            if ((int64_t)sizes.size() > w.items_cap) continue;
+            std::sort(sizes.begin(), sizes.end(), std::greater<int32_t>());
+            std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> fin;
+            for (int32_t i = 0; i < slots; ++i) fin.push(0);
+            int64_t t_end = 0;
+            for (int32_t tiles : sizes) {
+                const int64_t t = fin.top() + tiles + kAttnItemStartTiles;
+                fin.pop();
+                fin.push(t);
+                t_end = std::max(t_end, t);
+            }
+            if (!best || t_end < best_t) {
+                best = ch;
+                best_t = t_end;
+            }
+        }
+        return best ? best : kAttnManyHi;
+    };
     auto pick_chunk = [&](int32_t target_wg) {
         const int32_t target_items = std::max(1, target_wg / c.kv_heads);
         int64_t chunk64 = target_items > nseq ? (total_keys + target_items - nseq - 1) / (target_items - nseq)
                                               : (int64_t)kAttnRoundChunk + 1;
         if (chunk64 > kAttnRoundChunk) {
             const int64_t room = std::max<int64_t>(1, (int64_t)w.items_cap - nseq);
-            chunk64 = std::max<int64_t>(kAttnManyChunk, (total_keys + room - 1) / room);
+            const int64_t need = (total_keys + room - 1) / room;   // the workspace bounds the item count
+            chunk64 = need > kAttnManyHi ? need : many_chunk(target_items, need);
         }
         return (int32_t)std::max<int64_t>(kAttnMinChunk, (chunk64 + 63) / 64 * 64);
     };
@@ -467,15 +508,30 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         items += d.nitems;
     }
     if (bf16() && items > w.items_cap) return fail(DFLASH_E_CAPACITY, "attention work exceeds the workspace");
+    if (items > 0xffff || nseq > 0xffff) return fail(DFLASH_E_CAPACITY, "attention work items exceed 16-bit indices");
+    // dispatch order of the attention items: largest chunks first (stable),
+    // so the partial chunks at the sequences' ends fill the launch's tail
+    std::vector<uint32_t> order;
+    order.reserve(items);
+    for (int32_t s = 0; s < nseq; ++s)
+        for (int32_t i = 0; i < descs[s].nitems; ++i) order.push_back(((uint32_t)s << 16) | (uint32_t)(descs[s].item0 + i));
+    auto item_keys = [&](uint32_t od) {
+        const SeqDesc& d = descs[od >> 16];
+        const int32_t i = (int32_t)(od & 0xffffu) - d.item0;
+        return std::min(chunk, d.F + d.M - d.key_lo - i * chunk);
+    };
+    std::stable_sort(order.begin(), order.end(), [&](uint32_t x, uint32_t y) { return item_keys(x) > item_keys(y); });
     Tables tb;
     const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
     const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
     const size_t o_src = tb.add(rowsrc.data(), sizeof(int32_t) * rowsrc.size());
+    const size_t o_ord = tb.add(order.data(), sizeof(uint32_t) * order.size());
     char* tab = base + w.tables;
     HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
     const SeqDesc* d_desc = (const SeqDesc*)(tab + o_desc);
     const RowInfo* d_info = (const RowInfo*)(tab + o_info);
     const int32_t* d_rowsrc = (const int32_t*)(tab + o_src);
+    const uint32_t* d_order = (const uint32_t*)(tab + o_ord);
 
     float* h = (float*)(base + w.blk_h);
     void* x = base + w.blk_x;
@@ -536,6 +592,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             a.part_o = (float*)(base + w.attn_o);
             a.part_ml = (float*)(base + w.attn_ml);
             a.gate_src = qkv;
+            a.order = d_order;
             a.gate_nsplit = qkv_slices;
             a.gate_stride = (int64_t)R * ldq;
             a.out = base + w.blk_attn;

@@ -40,21 +40,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// The last sequence with item0 <= item (item0 ascends; sequences without
-// items repeat the next one's).  Every lane of a wave reads one descriptor and
-// the wave counts the hits, so a batch of up to 64 sequences costs one load
-// round trip rather than a binary search's chain of them.
-__device__ __forceinline__ int find_item_seq(const SeqDesc* seqs, int nseq, int item) {
-    const int lane = threadIdx.x & 63;
-    int cnt = 0;
-    for (int b = 0; b < nseq; b += 64) {
-        const int i = b + lane;
-        const bool le = i < nseq && seqs[i].item0 <= item;
-        cnt += __popcll(__ballot(le));
-    }
-    return cnt - 1;                         // seqs[0].item0 == 0 <= item
-}
-
 // (bitwise, not short-circuit: keeps the masking branch-free)
 __device__ __forceinline__ bool visible(int s, int p, int kend, int causal, int window) {
     return (s < kend) & ((causal == 0) | (s <= p)) & ((window == 0) | (p - s < window));
@@ -99,8 +84,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sV0[kKT * kD];
     __shared__ __attribute__((aligned(16))) uint16_t sV1[kKT * kD];
 
-    const int item = blockIdx.x, g = blockIdx.y;
-    const SeqDesc sd = a.seqs[find_item_seq(a.seqs, a.nseq, item)];
+    // work items in the host's order (largest chunks first, so the short
+    // ones fill the end of the launch), every kv head of an item together
+    const int rank = blockIdx.x / a.Hkv, g = blockIdx.x - rank * a.Hkv;
+    const uint32_t od = a.order[rank];
+    const int item = (int)(od & 0xffffu);
+    const SeqDesc sd = a.seqs[od >> 16];
     const int c = item - sd.item0;
     const int kend = sd.F + sd.M;
     const int kb = sd.key_lo + c * a.chunk;
@@ -443,7 +432,7 @@ hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st) {
         hipLaunchKernelGGL(k_attn_f32, dim3(a.nrows, a.Hq), dim3(64), 0, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items, a.Hkv), dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items * a.Hkv), dim3(kAttnThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, (a.Hq + kCombHeads - 1) / kCombHeads), dim3(32 * kCombHeads),

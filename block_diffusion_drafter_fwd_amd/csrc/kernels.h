@@ -135,6 +135,7 @@ struct AttnArgs {
     float* part_o;            // [items][Hkv][64][D]
     float* part_ml;           // [items][Hkv][64][2]
     const float* gate_src;    // projection rows holding the g columns (gate_nsplit slices, summed)
+    const uint32_t* order;    // [total_items]: (sequence << 16 | item), largest chunks first
     void* out;                // [rows][Hq*D]
     int32_t nseq, nrows, layer, L, Hq, Hkv, D, causal, window, chunk, total_items;
     int32_t gate, gate_ld, gate_col, out_bf16;
