@@ -610,6 +610,120 @@ __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
 }
 
 // ---------------------------------------------------------------------------
+// 8 waves on 256 x 256 tiles (waves as 2 x 4, 128 x 64 each: the wave tile
+// of k_gemm_w8<8>).  Per 32-wide k step a workgroup copies 32 KiB (A and B
+// 16 KiB each) for the products that cost k_gemm_w8<8> 40 KiB, and these
+// GEMMs are bound by the copies into LDS.  Used for the batched unembedding:
+// the row tiles of one column tile are consecutive work items (dispatched
+// together, so the weight tile is fetched from HBM once), and the grid is
+// padded to a multiple of 8 so that they share an XCD.  Four stages of
+// 32 KiB, three in flight; same read/wait scheme as k_gemm_mt.
+// ---------------------------------------------------------------------------
+constexpr int kSqB = 256;
+
+template <int TAG, class GA>
+__global__ __launch_bounds__(512) void k_gemm_sq(GA a) {
+    constexpr int BK = kW8BK, MI = 8, SA = kSqB * BK;
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[SA], sA1[SA], sA2[SA], sA3[SA];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[SA], sB1[SA], sB2[SA], sB3[SA];
+    // item l: row tile fastest, then column tile; consecutive items on one XCD
+    const int mtiles = (a.M + kSqB - 1) / kSqB, items = a.ntiles * mtiles;
+    const int total = gridDim.x;   // items rounded up to a multiple of 8
+    int l = blockIdx.x;
+    l = (l & 7) * (total >> 3) + (l >> 3);
+    if (l >= items) return;
+    const int mt = l % mtiles, tile = l / mtiles;
+    const GemmSeg g = a.seg[find_seg(a, tile)];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave >> 2, wn = wave & 3, r = lane & 15, q = lane >> 4;
+    const int m0 = mt * kSqB, n0 = (tile - g.tile0) * kSqB;
+    // copies per stage: A and B 16 blocks of 16 rows each, two of each per
+    // wave; lane l of a block stores position l % 4 of row l / 4, holding the
+    // logical piece (l % 4) ^ ((row / 2) % 4); rows past M or N repeat the last
+    const uint16_t* pa[2];
+    const uint16_t* pb[2];
+    {
+        const int rl = lane >> 2, pp = lane & 3;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = (wave * 2 + i) * 16 + rl;
+            const int am = min(m0 + row, a.M - 1);
+            const int ar = a.a_rows ? a.a_rows[am] : am;
+            pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + ((pp ^ mt_swz<32>(row)) << 3);
+            pb[i] = (const uint16_t*)g.B + (size_t)min(n0 + row, g.N - 1) * g.ldb + ((pp ^ mt_swz<32>(row)) << 3);
+        }
+    }
+    const int nk = a.K / BK;   // the launcher checks K % 128 == 0
+    auto load = [&](int k0, uint16_t* sA, uint16_t* sB) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(pa[i] + k0, &sA[(wave * 2 + i) * 512]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(pb[i] + k0, &sB[(wave * 2 + i) * 512]);
+    };
+    f32x4_t acc[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint32_t offA[MI], offB[4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) offA[i] = (uint32_t)mt_off<32>(wm * (16 * MI) + i * 16 + r, q) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) offB[j] = (uint32_t)mt_off<32>(wn * 64 + j * 16 + r, q) * 2;
+    auto compute = [&](const uint16_t* tA, const uint16_t* tB) {
+        const uint32_t baseA = lds_addr(tA), baseB = lds_addr(tB);
+        u32x4_t bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = lds_read16(baseB + offB[j]);
+#pragma unroll
+        for (int i0 = 0; i0 < MI; i0 += 4) {
+            u32x4_t af[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = lds_read16(baseA + offA[i0 + i]);
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]),
+                           "+v"(bf[3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i0 + i][j] = mfma32(af[i], bf[j], acc[i0 + i][j]);
+        }
+    };
+    // step kt: its stage landed when at most the two later stages' copies (4
+    // instructions each per wave) are in flight; refill the stage of kt - 1
+    auto step = [&](int kt, const uint16_t* tA, const uint16_t* tB, uint16_t* nA, uint16_t* nB) {
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        load(min(kt + 3, nk - 1) * BK, nA, nB);
+        compute(tA, tB);
+    };
+    if (nk > 0) {
+        load(0, sA0, sB0);
+        load(min(1, nk - 1) * BK, sA1, sB1);
+        load(min(2, nk - 1) * BK, sA2, sB2);
+    }
+    for (int kt = 0; kt < nk; kt += 4) {          // nk is a multiple of 4
+        step(kt, sA0, sB0, sA3, sB3);
+        step(kt + 1, sA1, sB1, sA0, sB0);
+        step(kt + 2, sA2, sB2, sA1, sB1);
+        step(kt + 3, sA3, sB3, sA2, sB2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + j * 16 + r;
+            const bool nok = n < g.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * (16 * MI) + i * 16 + 4 * q + e;
+                if (nok && m < a.M) store_out(a, 0, m, g.c_col0 + n, acc[i][j][e]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // tiled: MT x 128 tiles, KT = 64, LDS double buffer
 // ---------------------------------------------------------------------------
 template <int MT, int TAG, class GA>
@@ -862,6 +976,27 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         // batched unembedding: the weights are read once); else k_gemm_mt
         // (128 x 128, 4 waves) with K split to about one workgroup per CU;
         // all take K in groups of four stages.  k_gemm_tiled otherwise.
+        // 257..512 rows over many columns (the batched unembedding): 256 x 256
+        // tiles, each weight tile fetched once for both row tiles
+        if (a.M > kSqB && a.M <= 2 * kSqB && a.K % 128 == 0 && (a.mode == kStore || a.mode == kAccumulate)) {
+            int nt = 0;
+            for (int s = 0; s < a.nseg; ++s) nt += (a.seg[s].N + kSqB - 1) / kSqB;
+            if (nt >= num_cus) {
+                nt = 0;
+                for (int s = 0; s < a.nseg; ++s) {
+                    a.seg[s].tile0 = nt;
+                    nt += (a.seg[s].N + kSqB - 1) / kSqB;
+                }
+                a.ntiles = nt;
+                a.splits = 1;
+                a.kc = a.K;
+                const int items = nt * 2;
+                const dim3 grid((items + 7) / 8 * 8);
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_sq<1, GA>), grid, dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_sq<0, GA>), grid, dim3(512), 0, st, a);
+                return hipGetLastError();
+            }
+        }
         const bool pipelined = a.K % 256 == 0;
         const int NT = 128;
         int ntiles = 0;
