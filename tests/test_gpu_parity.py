@@ -62,6 +62,17 @@ CASES = {
     "qwen_full": (synth.config("qwen"), W("qf", "qwen", context=300, commit_rows=256, rounds=3), 512),
     "laguna_full": (synth.config("laguna"), W("lf", "laguna", context=1100, commit_rows=300, rounds=3),
                     512 + 8 - 1),
+    # the long configuration's widths (hidden 4096, fc 20480 -> 4096, 8 fc
+    # slices on the 256-row tiles) with a vocabulary large enough for the
+    # persistent unembedding at K = 4096 (eight 64-wide k steps per wave);
+    # 40009 is not a multiple of any tile
+    "long_wide": (synth.config("long", layers=1, vocab=40009),
+                  W("lw", "long", context=270, commit_rows=256, rounds=3, max_tokens=7, temperature=1.0,
+                    probs=True), 400),
+    # the long configuration at full size (5 layers, hidden 4096, the
+    # 262144-token unembedding and sampler with probabilities), short context
+    "long_full": (synth.config("long"), W("lf5", "long", context=270, commit_rows=256, rounds=2, max_tokens=7,
+                                            temperature=1.0, probs=True), 400),
     "batched_shape_sampling": (synth.config("qwen", layers=1, vocab=3001),
                                W("bs", "qwen", context=130, commit_rows=40, rounds=5, max_tokens=-1,
                                  temperature=0.7, rep_penalty=1.1, history=512, probs=True), 300),
