@@ -174,6 +174,12 @@ BATCHED = {
     # the 512 x 128 tile form of the 8-wave kernel (all rows in one tile)
     "rows_over_256": (66001, [37, 0, 52, 18, 90, 25, 61, 44, 33, 70, 29, 48, 56, 21, 64, 39, 27, 81, 45],
                       [15] * 19, 2),
+    # 63 sessions whose keys exceed one resident round of attention
+    # workgroups: the split runs in several rounds, items dispatched largest
+    # first, the chunk chosen by the host's schedule model (the 1300-key
+    # sessions split into several items at the smaller candidates); 945 logit
+    # rows take the tiled unembedding with four row tiles
+    "multi_round": (3001, [30] * 57 + [1300] * 6, [15] * 63, 2, 1400),
 }
 
 
@@ -186,10 +192,11 @@ def test_batched_propose_matches_oracle(cuda, case):
     from oracle.sampler import sample_row
     vocab, lens, mts = BATCHED[case][:3]
     rounds = BATCHED[case][3] if len(BATCHED[case]) > 3 else 3
+    capacity = BATCHED[case][4] if len(BATCHED[case]) > 4 else 512
     cfg = synth.config("qwen", layers=2, vocab=vocab)
     w = synth.make_weights(cfg, seed=4, gains="random")
     d = _drafter(cfg, w, max_sessions=len(lens))
-    pairs = [Pair(d, cfg, w, 512, seed=4, sid=k) for k in range(len(lens))]
+    pairs = [Pair(d, cfg, w, capacity, seed=4, sid=k) for k in range(len(lens))]
     srcs = [synth.FeatureSource(cfg, 4, k) for k in range(len(lens))]
     for k, (pr, L) in enumerate(zip(pairs, lens)):
         for p in range(0, L, 100):
@@ -241,3 +248,42 @@ def test_batched_propose_matches_oracle(cuda, case):
         pr.check_state("final")
         pr.check_cache(rep)
     assert rep.ids_compared > 0
+
+
+def test_long_context_cache_rows_at_full_length(cuda):
+    """The long configuration's whole 131072-slot prompt through 256-row
+    flushes, checked at sampled slots: a context row's K/V depend only on the
+    features at its own slot and its position (DFlash context rows are local
+    to their slot), so the oracle computes just the sampled rows.  Feature
+    rows repeat with period 4096 (row S carries the seeded features of row
+    S mod 4096, as in the bench); positions, slots and RoPE angles run over
+    the full length."""
+    from oracle.model import DraftModel
+    cfg = synth.config("long")
+    w = synth.make_weights(cfg, seed=0, gains="random")
+    d = _drafter(cfg, w)
+    total, period = 131072, 4096
+    s = d.session(total + cfg.block_size)
+    src = synth.FeatureSource(cfg, seed=0, session=0)
+    feats = src.features(0, period)
+    toks = src.tokens(0, period)
+    fd = feats_dev(cfg, feats)
+    say(f"long full-length flush: {total} slots in {cfg.flush_rows}-row flushes")
+    for p0 in range(0, total, period):
+        s.committed(toks, fd, p0)
+    s.flush()
+    torch.cuda.synchronize()
+    assert s.state()[0] == total and s.state()[1] == 0
+    slots = np.array([0, 1, 255, 256, 4095, 4096, 65535, 65536, 100003, total - 257, total - 2, total - 1])
+    for emulate in (False, True):
+        model = DraftModel(cfg, w, emulate_bf16=emulate)
+        ref = model.context_kv(feats[slots % period], slots)
+        for l in range(cfg.layers):
+            for j, S in enumerate(slots):
+                k, v = s.cache_read(l, int(S), 1)
+                k = k.double().cpu().numpy()[0]
+                v = v.double().cpu().numpy()[0]
+                ek, ev = rel_err(k, ref[l][0][j]), rel_err(v, ref[l][1][j])
+                assert ek < tol(cfg) and ev < tol(cfg), (emulate, l, int(S), ek, ev)
+    s.close()
+    d.close()
