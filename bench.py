@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen", choices=["qwen", "laguna", "long", "batched", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="context rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="context rows of the oracle sample")
+    ap.add_argument("--cpu-rounds", type=int, default=8, help="propose + sample rounds of the oracle sample")
     ap.add_argument("--stages", action="store_true", help="also time the attention, sampler and flush stages")
     ap.add_argument("--no-width-sweep", action="store_true",
                     help="skip the propose-time-vs-n sweep and the truncated-block comparison")
@@ -142,7 +143,7 @@ def main():
     else:
         out = bench_single(args, cfg, wl, w_dev, steps, torch, synth)
     if not args.no_cpu_baseline and args.config == "qwen":
-        out["cpu_baseline"] = cpu_baseline(cfg, wl, w_np, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(cfg, wl, w_np, args.cpu_rows, args.cpu_rounds)
     else:
         out.setdefault("cpu_baseline", None)
     out["setup_s"] = round(gen_s, 1)
@@ -498,9 +499,9 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
     }
 
 
-def cpu_baseline(cfg, wl, w_np, rows):
+def cpu_baseline(cfg, wl, w_np, rows, rounds=8):
     """The float64 oracle on a bounded sample of the same workload: `rows`
-    context rows flushed in 256-row chunks, then 2 rounds of propose + greedy
+    context rows flushed in 256-row chunks, then `rounds` rounds of propose +
     sample over that context.  Reported per unit (blocks/s)."""
     import numpy as np
 
@@ -521,7 +522,6 @@ def cpu_baseline(cfg, wl, w_np, rows):
     o.flush()
     t_flush = time.perf_counter() - t
     t = time.perf_counter()
-    rounds = 2
     cur = 5
     for r in range(rounds):
         out = o.propose(cur, cfg.block_size - 1)
