@@ -385,7 +385,7 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
     """64 sessions, one batched propose + one batched sample per round."""
     import numpy as np
 
-    from block_diffusion_drafter_fwd_amd import Drafter, propose_batch, sample
+    from block_diffusion_drafter_fwd_amd import Drafter, flush_batch, propose_batch, sample
 
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -422,9 +422,9 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
 
     def step():
         r = state["r"]
-        for k, sc in enumerate(scripts):
-            if sc.flush_before:
-                sess[k].flush()
+        flushing = [sess[k] for k, sc in enumerate(scripts) if sc.flush_before]
+        if flushing:   # the sessions that flush before this round's propose, in one context pass
+            flush_batch(flushing)
         offs, lg = propose_batch(sess, cur, mts, logits=logits)
         sample(sess, offs, lg, wl.temperature, wl.rep_penalty, wl.history, r, probs=wl.probs)
         state["rows"].append(offs[S])

@@ -7,11 +7,12 @@ the library was not built.
 """
 from .abi import ContextGap, DFlashError  # noqa: F401
 
-__all__ = ["Drafter", "Session", "propose_batch", "sample", "verify", "WidthPolicy", "ContextGap", "DFlashError"]
+__all__ = ["Drafter", "Session", "flush_batch", "propose_batch", "sample", "verify", "WidthPolicy", "ContextGap",
+           "DFlashError"]
 
 
 def __getattr__(name):
-    if name in ("Drafter", "Session", "propose_batch", "sample", "verify", "WidthPolicy"):
+    if name in ("Drafter", "Session", "flush_batch", "propose_batch", "sample", "verify", "WidthPolicy"):
         from . import drafter
         return getattr(drafter, name)
     raise AttributeError(name)

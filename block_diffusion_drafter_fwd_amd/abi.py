@@ -62,6 +62,7 @@ SYMBOLS = {
     "dflash_session_close": (c_int, [c_void_p]),
     "dflash_committed": (c_int, [c_void_p, POINTER(c_int32), c_void_p, c_int32, c_int32]),
     "dflash_flush": (c_int, [c_void_p]),
+    "dflash_flush_batch": (c_int, [POINTER(c_void_p), c_int32]),
     "dflash_commit_block": (c_int, [c_void_p]),
     "dflash_propose": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
     "dflash_propose_batch": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), POINTER(c_int32),

@@ -378,6 +378,54 @@ extern "C" int dflash_flush(dflash_session* s) {
     return write_context(s, nullptr, 0);
 }
 
+// dflash_flush over several sessions: each rewinds, and every session's
+// pending rows go through one context pass (segments gathered, as in the
+// batched propose); the per-row context path makes it equal to flushing the
+// sessions one by one.
+extern "C" int dflash_flush_batch(dflash_session* const* ss, int32_t count) {
+    if (!ss || count <= 0) return fail(DFLASH_E_ARG, "null argument");
+    dflash_ctx* ctx = ss[0] ? ss[0]->ctx : nullptr;
+    if (!ctx) return fail(DFLASH_E_ARG, "null session");
+    const dflash_config& c = ctx->model.cfg;
+    if (count > ss[0]->ws_sessions) return fail(DFLASH_E_CAPACITY, "more sessions than the workspace serves");
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = ss[k];
+        if (!s || s->ctx != ctx || s->ws != ss[0]->ws || s->stream != ss[0]->stream)
+            return fail(DFLASH_E_ARG, "batched sessions must share context, workspace and stream");
+        for (int32_t j = 0; j < k; ++j)
+            if (ss[j] == s) return fail(DFLASH_E_ARG, "a session appears twice in one batch");
+    }
+    std::vector<SessView> views(count);
+    std::vector<CtxSeg> segs;
+    std::vector<int32_t> kept(count, 0);
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = ss[k];
+        commit_block(s);
+        views[k] = s->view();
+        const int32_t P = s->pending;
+        if (!P) continue;
+        const int32_t frontier = s->ctx_offset + P;
+        int32_t first = 0;
+        if (c.window) first = std::max(0, std::min(P, frontier - (c.window - 1) - s->ctx_offset));
+        if (first < P)
+            segs.push_back({k, s->pending_buf() + (size_t)first * s->row_bytes(), P - first, s->ctx_offset + first});
+        kept[k] = P - first;
+    }
+    if (!segs.empty()) {
+        int rc = ctx->engine->ctx_forward(views, segs, ss[0]->ws, ss[0]->ws_sessions, ss[0]->stream);
+        if (rc) return rc;
+    }
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = ss[k];
+        if (!s->pending) continue;
+        s->rows_written += kept[k];
+        s->ctx_offset += s->pending;
+        s->pending = 0;
+        s->cache_len = s->ctx_offset;
+    }
+    return 0;
+}
+
 extern "C" int dflash_commit_block(dflash_session* s) {
     if (!s) return fail(DFLASH_E_ARG, "null session");
     commit_block(s);

@@ -184,6 +184,13 @@ class Session:
             check(self.lib, self.lib.dflash_session_close(h))
 
 
+def flush_batch(sessions: Sequence[Session]) -> None:
+    """dflash_flush_batch: every session's pending rows in one context pass."""
+    d = sessions[0].d
+    hs = (c_void_p * len(sessions))(*[s.h for s in sessions])
+    check(d.lib, d.lib.dflash_flush_batch(hs, len(sessions)))
+
+
 def propose_batch(sessions: Sequence[Session], current: Sequence[int], max_tokens: Sequence[int],
                   logits: Optional[torch.Tensor] = None) -> Tuple[list, torch.Tensor]:
     d = sessions[0].d

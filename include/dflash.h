@@ -195,6 +195,17 @@ int dflash_committed(dflash_session* s, const int32_t* tokens_host, const void* 
  * per-row locality makes equal to one pass). */
 int dflash_flush(dflash_session* s);
 
+/* dflash_flush over `count` sessions in one context forward (the flush of
+ * dflash.go, once per session, with every session's pending rows gathered
+ * into one pass as the Batch of dflash.go gathers its sequences).  Each
+ * session rewinds an outstanding block, writes its pending rows to its cache
+ * and advances ctxOffset past them; since a context row depends only on the
+ * features at its own slot, the result equals flushing the sessions one by
+ * one.  The sessions share one context, workspace and stream, count <= the
+ * workspace's max_sessions, and none appears twice.  Errors (state
+ * unchanged): E_ARG, E_CAPACITY. */
+int dflash_flush_batch(dflash_session* const* sessions, int32_t count);
+
 /* dflash.go commitBlock: when a block is outstanding, cut the cache back to
  * ctxOffset; otherwise nothing.  Idempotent. */
 int dflash_commit_block(dflash_session* s);

@@ -318,3 +318,79 @@ def test_batch_rules(host):
     tr = _trace(host)
     assert tr == ["ctx sess=0 pos0=0 rows=3", "ctx sess=1 pos0=0 rows=4",
                   "block sess=0 F=3 M=3 cur=5", "block sess=1 F=4 M=8 cur=6"]
+
+
+def _shared_sessions(host, ctx, count, max_sessions=4, capacity=64):
+    """`count` sessions over one workspace (what a batched call requires)."""
+    ws = np.zeros(host.dflash_workspace_bytes(ctx, max_sessions), dtype=np.uint8)
+    out = []
+    for k in range(count):
+        s = HostSession.__new__(HostSession)
+        s.lib = host
+        n = host.dflash_session_bytes(ctx, capacity)
+        s.arena = np.zeros(n, dtype=np.uint8)
+        s.ws = ws
+        s.h = c_void_p()
+        abi.check(host, host.dflash_session_open(ctx, s.arena.ctypes.data, n, capacity, ws.ctypes.data, ws.size,
+                                                 max_sessions, 0, 0, k, None, byref(s.h)))
+        s.feat = np.zeros(1 << 16, dtype=np.uint8)
+        out.append(s)
+    return out
+
+
+def _prepare_for_flush(sessions):
+    """Session 0: 3 pending rows; 1: nothing; 2: an outstanding block, then 5
+    pending rows committed after the rewind; 3: 12 pending rows."""
+    a, b, c, d = sessions
+    a.committed(np.arange(3), None, 0)
+    c.committed(np.arange(4), None, 0)
+    assert c.propose(5, 3) == 3
+    c.commit_block()
+    c.committed(np.arange(5), None, 4)
+    d.committed(np.arange(12), None, 0)
+
+
+@pytest.mark.parametrize("window", [0, 6])
+def test_flush_batch_equals_single_flushes(host, window):
+    """dflash_flush_batch gives every session the state, and plans the same
+    context rows (window drop included), as dflash_flush per session."""
+    fm = FakeModel(host, window=window)
+    rc, ctx = fm.create()
+    assert rc == 0
+    one = _shared_sessions(host, ctx, 4)
+    many = _shared_sessions(host, ctx, 4)
+    _prepare_for_flush(one)
+    _prepare_for_flush(many)
+    _trace(host)
+    for s in one:
+        s.flush()
+    t_one = _trace(host)
+    hs = (c_void_p * 4)(*[s.h for s in many])
+    abi.check(host, host.dflash_flush_batch(hs, 4))
+    t_many = _trace(host)
+    assert [s.state() for s in many] == [s.state() for s in one]
+    assert [s.rows_written for s in many] == [s.rows_written for s in one]
+    # a single-session flush names its session 0; sessions 0, 2 and 3 have rows
+    single = [ln.split(" ", 2)[2] for ln in t_one if ln.startswith("ctx ")]
+    batched = [ln.split(" ", 2) for ln in t_many if ln.startswith("ctx ")]
+    assert [(b[1], b[2]) for b in batched] == list(zip(["sess=0", "sess=2", "sess=3"], single))
+    st = [s.state() for s in many]
+    assert st[0] == (3, 0, 3, 0) and st[1] == (0, 0, 0, 0) and st[2] == (9, 0, 9, 0) and st[3] == (12, 0, 12, 0)
+    if window:
+        # frontier 12, window 6: only slots 7..11 of session 3 are projected
+        assert "ctx sess=3 pos0=7 rows=5" in t_many
+
+
+def test_flush_batch_rejects_bad_batches(host):
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    a, b = _shared_sessions(host, ctx, 2)
+    a.committed(np.arange(3), None, 0)
+    before = a.state()
+    hs = (c_void_p * 2)(a.h, a.h)
+    assert host.dflash_flush_batch(hs, 2) == abi.E_ARG            # a session twice
+    other = HostSession(host, ctx)
+    hs = (c_void_p * 2)(a.h, other.h)
+    assert host.dflash_flush_batch(hs, 2) == abi.E_ARG            # another workspace
+    assert host.dflash_flush_batch(hs, 0) == abi.E_ARG
+    assert a.state() == before                                    # state unchanged on every error

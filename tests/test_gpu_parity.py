@@ -287,3 +287,36 @@ def test_long_context_cache_rows_at_full_length(cuda):
                 assert ek < tol(cfg) and ev < tol(cfg), (emulate, l, int(S), ek, ev)
     s.close()
     d.close()
+
+
+@pytest.mark.parametrize("name", ["qwen", "laguna"])
+def test_flush_batch_matches_oracle(cuda, name):
+    """dflash_flush_batch over sessions sharing a workspace (one with no
+    rows, one with an outstanding block, ragged pending counts; the window
+    ring and its drop-before-fc on laguna) leaves every session in the state,
+    and with the cache rows, of the oracle's flush of each session."""
+    from block_diffusion_drafter_fwd_amd import flush_batch
+    cfg = synth.config(name, layers=2, vocab=3001)
+    w = synth.make_weights(cfg, seed=5, gains="random")
+    d = _drafter(cfg, w, max_sessions=4)
+    cap = 2048 if not cfg.window else cfg.window + cfg.block_size - 1
+    pairs = [Pair(d, cfg, w, cap, seed=5, sid=k) for k in range(4)]
+    srcs = [synth.FeatureSource(cfg, 5, k) for k in range(4)]
+    rep = Report()
+    for r, counts in enumerate([(3, 0, 9, 255), (1, 17, 0, 200)]):
+        say(f"[parity] flush_batch {name} pass {r}")
+        if r == 0:   # session 2 drafts a block first, so the batched flush has to rewind it
+            pairs[2].committed(srcs[2].tokens(0, 4), srcs[2].features(0, 4), 0)
+            pairs[2].propose(11, 5, rep, hidden=False)
+        for k, (pr, T) in enumerate(zip(pairs, counts)):
+            F = pr.o[0].ctx_offset + pr.o[0].pending_count
+            if T:
+                pr.committed(srcs[k].tokens(F, T), srcs[k].features(F, T), F)
+        for pr in pairs:
+            for o in pr.o:
+                o.flush()
+        flush_batch([pr.g for pr in pairs])
+        for k, pr in enumerate(pairs):
+            pr.check_state(f"flush_batch pass {r} session {k}")
+            pr.check_cache(rep)
+    say(f"[parity] flush_batch {name} worst {rep.worst}")
