@@ -385,7 +385,7 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
     """64 sessions, one batched propose + one batched sample per round."""
     import numpy as np
 
-    from block_diffusion_drafter_fwd_amd import Drafter, flush_batch, propose_batch, sample
+    from block_diffusion_drafter_fwd_amd import Drafter, committed_batch, flush_batch, propose_batch, sample
 
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -428,6 +428,8 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
         offs, lg = propose_batch(sess, cur, mts, logits=logits)
         sample(sess, offs, lg, wl.temperature, wl.rep_penalty, wl.history, r, probs=wl.probs)
         state["rows"].append(offs[S])
+        # every session rewinds and commits its accepted run (one batched call)
+        runs, fts, poss = [], [], []
         for k, sc in enumerate(scripts):
             nk = offs[k + 1] - offs[k]
             a = sc.accept(nk)
@@ -435,9 +437,11 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
             sess[k].commit_block()
             F = sess[k].state()[0]
             tk, ft = pool.at(F, a + 1)
-            run = np.concatenate([[cur[k]], tk[1:a + 1]]).astype(np.int32)
-            sess[k].committed(run, ft, F)
+            runs.append(np.concatenate([[cur[k]], tk[1:a + 1]]).astype(np.int32))
+            fts.append(ft)
+            poss.append(F)
             cur[k] = bonus
+        committed_batch(sess, runs, fts, poss)
         state["r"] = r + 1
 
     for _ in range(args.warmup):

@@ -63,6 +63,8 @@ SYMBOLS = {
     "dflash_committed": (c_int, [c_void_p, POINTER(c_int32), c_void_p, c_int32, c_int32]),
     "dflash_flush": (c_int, [c_void_p]),
     "dflash_flush_batch": (c_int, [POINTER(c_void_p), c_int32]),
+    "dflash_committed_batch": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), POINTER(c_int32),
+                                        POINTER(c_void_p), POINTER(c_int32)]),
     "dflash_commit_block": (c_int, [c_void_p]),
     "dflash_propose": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
     "dflash_propose_batch": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), POINTER(c_int32),

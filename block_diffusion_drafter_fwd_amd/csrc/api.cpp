@@ -372,6 +372,68 @@ extern "C" int dflash_committed(dflash_session* s, const int32_t* tokens_host, c
     return write_context(s, src, fresh);
 }
 
+// dflash_committed for several sessions.  Every run is checked first (any
+// error leaves every session unchanged); the runs that stay below the flush
+// threshold go to the backend together, the others take the single-session
+// path (which flushes).
+extern "C" int dflash_committed_batch(dflash_session* const* ss, int32_t count, const int32_t* tokens_host,
+                                      const int32_t* token_offsets, const void* const* features_dev,
+                                      const int32_t* positions) {
+    if (!ss || count <= 0 || !token_offsets || !features_dev || !positions)
+        return fail(DFLASH_E_ARG, "null argument");
+    dflash_ctx* ctx = ss[0] ? ss[0]->ctx : nullptr;
+    if (!ctx) return fail(DFLASH_E_ARG, "null session");
+    const dflash_config& c = ctx->model.cfg;
+    std::vector<int32_t> start(count, 0), fresh(count, 0);
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = ss[k];
+        if (!s || s->ctx != ctx || s->stream != ss[0]->stream)
+            return fail(DFLASH_E_ARG, "batched sessions must share context and stream");
+        for (int32_t j = 0; j < k; ++j)
+            if (ss[j] == s) return fail(DFLASH_E_ARG, "a session appears twice in one batch");
+        const int32_t T = token_offsets[k + 1] - token_offsets[k];
+        if (T < 0 || positions[k] < 0 || token_offsets[k] < 0) return fail(DFLASH_E_ARG, "negative length or position");
+        if (T > 0 && (!tokens_host || !features_dev[k])) return fail(DFLASH_E_ARG, "null tokens or features");
+        const int64_t st = (int64_t)s->ctx_offset + s->pending - positions[k];
+        if (st < 0)
+            return fail(DFLASH_E_CONTEXT_GAP, "committed run at " + std::to_string(positions[k]) +
+                                                  " leaves a context gap at " +
+                                                  std::to_string(s->ctx_offset + s->pending));
+        if (st >= T) continue;
+        const int64_t frontier = (int64_t)s->ctx_offset + s->pending + (T - st);
+        if (frontier > INT_MAX - 2 * 512) return fail(DFLASH_E_CAPACITY, "position overflow");
+        if (!s->ring && frontier + c.block_size > s->cap) return fail(DFLASH_E_CAPACITY, "cache capacity exceeded");
+        start[k] = (int32_t)st;
+        fresh[k] = T - (int32_t)st;
+    }
+    std::vector<CommitItem> items;
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = ss[k];
+        if (!fresh[k] || s->pending + fresh[k] >= c.flush_rows || fresh[k] > kHistory) continue;
+        const size_t rb = s->row_bytes();
+        items.push_back({s->view().hist, s->hist_head, tokens_host + token_offsets[k] + start[k], fresh[k],
+                         s->pending_buf() + (size_t)s->pending * rb,
+                         (const char*)features_dev[k] + (size_t)start[k] * rb, (size_t)fresh[k] * rb});
+    }
+    if (!items.empty()) {
+        if (int rc = ctx->engine->commit_many(items, ss[0]->stream)) return rc;
+    }
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = ss[k];
+        if (!fresh[k]) continue;
+        if (s->pending + fresh[k] < c.flush_rows && fresh[k] <= kHistory) {
+            s->hist_head = (s->hist_head + fresh[k]) % kHistory;
+            s->hist_count += fresh[k];
+            s->pending += fresh[k];
+        } else {
+            const int32_t T = token_offsets[k + 1] - token_offsets[k];
+            if (int rc = dflash_committed(s, tokens_host + token_offsets[k], features_dev[k], T, positions[k]))
+                return rc;
+        }
+    }
+    return 0;
+}
+
 extern "C" int dflash_flush(dflash_session* s) {
     if (!s) return fail(DFLASH_E_ARG, "null session");
     commit_block(s);

@@ -4,6 +4,7 @@
 // can be tested on a host without a GPU.
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -38,6 +39,18 @@ struct ArenaLayout {
 ArenaLayout arena_layout(const Model& m, int32_t capacity);
 
 // What a backend needs to know about one session.
+// One session's commit of a round: history tokens (host) into the ring at
+// slot0 (wrapping), and `bytes` of feature rows from src to dst (device).
+struct CommitItem {
+    int32_t* hist;
+    int32_t slot0;
+    const int32_t* tokens;
+    int32_t count;
+    void* dst;
+    const void* src;
+    size_t bytes;
+};
+
 struct SessView {
     void* cache;        // arena base: [L][2][Hkv][cap][D]
     int32_t cap;
@@ -77,6 +90,23 @@ public:
                             const void* src, size_t bytes, void* stream) {
         if (int rc = write_history(s, slot0, tokens, count, stream)) return rc;
         return bytes ? copy_rows(dst, src, bytes, stream) : 0;
+    }
+    // commit_rows for several sessions, in as few launches as the backend can
+    // (here: the history in at most two runs, as the ring wraps at most once
+    // for count <= kHistory, then the rows)
+    virtual int commit_many(const std::vector<CommitItem>& items, void* stream) {
+        for (const CommitItem& c : items) {
+            SessView v{};
+            v.hist = c.hist;
+            const int32_t first = std::min(c.count, kHistory - c.slot0);
+            if (first > 0)
+                if (int rc = write_history(v, c.slot0, c.tokens, first, stream)) return rc;
+            if (c.count > first)
+                if (int rc = write_history(v, 0, c.tokens + first, c.count - first, stream)) return rc;
+            if (c.bytes)
+                if (int rc = copy_rows(c.dst, c.src, c.bytes, stream)) return rc;
+        }
+        return 0;
     }
     virtual int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs,
                             void* ws, int32_t ws_sessions, void* stream) = 0;

@@ -134,6 +134,41 @@ public:
         return Engine::commit_rows(s, slot0, tokens, count, dst, src, bytes, stream);
     }
 
+    // every session's history tokens and feature rows from the kernel
+    // arguments of one launch per kCommitItems sessions / kCommitBatchTokens
+    // tokens; an item that does not fit a launch's rules goes alone
+    int commit_many(const std::vector<CommitItem>& items, void* stream) override {
+        CommitBatchArgs a{};
+        int32_t ntok = 0;
+        auto launch = [&]() -> int {
+            if (a.n) HIP_OK(kern::commit_batch(a, (hipStream_t)stream));
+            a.n = 0;
+            ntok = 0;
+            return 0;
+        };
+        for (const CommitItem& c : items) {
+            const bool fits = c.count <= kCommitBatchTokens && c.bytes % 16 == 0 &&
+                              ((uintptr_t)c.src & 15) == 0 && ((uintptr_t)c.dst & 15) == 0;
+            if (!fits) {
+                if (int rc = Engine::commit_many({c}, stream)) return rc;
+                continue;
+            }
+            if (a.n == kCommitItems || ntok + c.count > kCommitBatchTokens)
+                if (int rc = launch()) return rc;
+            CommitItemArgs& it = a.item[a.n++];
+            it.hist = c.hist;
+            it.src = (const uint4*)c.src;
+            it.dst = (uint4*)c.dst;
+            it.n16 = (int64_t)(c.bytes / 16);
+            it.slot0 = c.slot0;
+            it.tok0 = ntok;
+            it.count = c.count;
+            for (int32_t j = 0; j < c.count; ++j) a.tokens[ntok + j] = c.tokens[j];
+            ntok += c.count;
+        }
+        return launch();
+    }
+
     int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs, void* ws,
                     int32_t ws_sessions, void* stream) override;
     int block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs, float* logits,

@@ -334,6 +334,31 @@ hipError_t commit_rows(int32_t* hist, const int32_t* tokens, int32_t count, void
     return hipGetLastError();
 }
 
+// grid (items, copy blocks): block (i, 0) also writes item i's history tokens
+__global__ __launch_bounds__(256) void k_commit_batch(CommitBatchArgs a) {
+    const CommitItemArgs& it = a.item[blockIdx.x];
+    if (blockIdx.y == 0)
+        for (int j = threadIdx.x; j < it.count; j += 256) it.hist[(it.slot0 + j) % 512] = a.tokens[it.tok0 + j];
+    for (int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x; i < it.n16; i += (int64_t)gridDim.y * 256)
+        it.dst[i] = it.src[i];
+}
+
+hipError_t commit_batch(const CommitBatchArgs& a, hipStream_t st) {
+    if (a.n <= 0) return hipSuccess;
+    if (a.n > kCommitItems) return hipErrorInvalidValue;
+    int64_t most = 1;
+    for (int i = 0; i < a.n; ++i) {
+        const CommitItemArgs& it = a.item[i];
+        if (it.count < 0 || it.tok0 < 0 || it.tok0 + it.count > kCommitBatchTokens || it.n16 < 0 ||
+            ((uintptr_t)it.src & 15) || ((uintptr_t)it.dst & 15))
+            return hipErrorInvalidValue;
+        most = std::max(most, it.n16);
+    }
+    const unsigned gy = (unsigned)std::min<int64_t>(16, (most + 255) / 256);
+    hipLaunchKernelGGL(k_commit_batch, dim3(a.n, gy), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_gather_rows(uint4* dst, const uint64_t* src, size_t row_words) {
     const int row = blockIdx.x;
     const uint4* s = (const uint4*)src[row];

@@ -191,6 +191,23 @@ struct CommitArgs {
     int32_t tokens[kCommitTokens];
 };
 
+// Commits of several sessions in one launch: item i writes its tokens
+// tokens[tok0 .. tok0+count) to hist[(slot0 + j) mod 512] and copies n16
+// 16-byte units from src to dst.  Everything rides in the kernel arguments.
+constexpr int kCommitItems = 32, kCommitBatchTokens = 512;
+struct CommitItemArgs {
+    int32_t* hist;
+    const uint4* src;
+    uint4* dst;
+    int64_t n16;
+    int32_t slot0, tok0, count, pad;
+};
+struct CommitBatchArgs {
+    int32_t n, pad;
+    CommitItemArgs item[kCommitItems];
+    int32_t tokens[kCommitBatchTokens];
+};
+
 // launchers (return hipError_t of the launch)
 // tag 1 launches a separate instantiation (the unembedding) so that profilers
 // can tell it apart from the per-layer GEMMs
@@ -198,6 +215,7 @@ struct CommitArgs {
 hipError_t gemm(GemmArgs a, bool bf16, size_t part_cap_floats, int num_cus, hipStream_t st, int tag = 0,
                 int* splits_out = nullptr);
 hipError_t rmsnorm(const NormArgs& a, hipStream_t st);
+hipError_t commit_batch(const CommitBatchArgs& a, hipStream_t st);
 hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st);
 hipError_t embed(const EmbedArgs& a, hipStream_t st);
 hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st);

@@ -184,6 +184,28 @@ class Session:
             check(self.lib, self.lib.dflash_session_close(h))
 
 
+def committed_batch(sessions: Sequence[Session], runs: Sequence, features: Sequence[torch.Tensor],
+                    positions: Sequence[int]) -> None:
+    """dflash_committed_batch: session k commits tokens runs[k] with feature
+    rows features[k] (device, [T_k, taps*Ht]) at positions[k]."""
+    d = sessions[0].d
+    n = len(sessions)
+    toks = [np.asarray(r, dtype=np.int32).reshape(-1) for r in runs]
+    offs = np.zeros(n + 1, dtype=np.int32)
+    offs[1:] = np.cumsum([len(t) for t in toks])
+    flat = np.ascontiguousarray(np.concatenate(toks) if offs[-1] else np.zeros(1, dtype=np.int32))
+    ptrs = (c_void_p * n)()
+    for k, (t, f) in enumerate(zip(toks, features)):
+        if len(t) and (f.dtype != d.feature_dtype or not f.is_contiguous() or f.shape[0] < len(t)
+                       or f.device.type != "cuda"):
+            raise ValueError("features must be contiguous device tensors [T, taps*Ht] of the drafter dtype")
+        ptrs[k] = f.data_ptr() if len(t) else None
+    hs = (c_void_p * n)(*[s.h for s in sessions])
+    pos = (c_int32 * n)(*[int(p) for p in positions])
+    check(d.lib, d.lib.dflash_committed_batch(hs, n, flat.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                              offs.ctypes.data_as(ctypes.POINTER(c_int32)), ptrs, pos))
+
+
 def flush_batch(sessions: Sequence[Session]) -> None:
     """dflash_flush_batch: every session's pending rows in one context pass."""
     d = sessions[0].d

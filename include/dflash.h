@@ -195,6 +195,21 @@ int dflash_committed(dflash_session* s, const int32_t* tokens_host, const void* 
  * per-row locality makes equal to one pass). */
 int dflash_flush(dflash_session* s);
 
+/* dflash_committed for `count` sessions in one call (a server commits the
+ * accepted run of every session after a batched round; dflash.go committed,
+ * once per session).  Session k's run is tokens_host[token_offsets[k] ..
+ * token_offsets[k+1]) (host) with feature rows features_dev[k] (device,
+ * [T_k, taps*Ht], config dtype) starting at positions[k].  Every run is
+ * checked before anything happens: a gap (E_CONTEXT_GAP), capacity
+ * (E_CAPACITY) or argument error (E_ARG: null pointers, negative lengths, a
+ * session twice, sessions on different contexts or streams) leaves every
+ * session unchanged.  The result equals calling dflash_committed on the
+ * sessions in order; runs that stay below the flush threshold are written in
+ * one or two launches for all sessions together. */
+int dflash_committed_batch(dflash_session* const* sessions, int32_t count, const int32_t* tokens_host,
+                           const int32_t* token_offsets, const void* const* features_dev,
+                           const int32_t* positions);
+
 /* dflash_flush over `count` sessions in one context forward (the flush of
  * dflash.go, once per session, with every session's pending rows gathered
  * into one pass as the Batch of dflash.go gathers its sequences).  Each

@@ -394,3 +394,68 @@ def test_flush_batch_rejects_bad_batches(host):
     assert host.dflash_flush_batch(hs, 2) == abi.E_ARG            # another workspace
     assert host.dflash_flush_batch(hs, 0) == abi.E_ARG
     assert a.state() == before                                    # state unchanged on every error
+
+
+def _commit_batch(host, sessions, runs, positions):
+    n = len(sessions)
+    toks = [np.asarray(r, dtype=np.int32) for r in runs]
+    offs = np.zeros(n + 1, dtype=np.int32)
+    offs[1:] = np.cumsum([len(t) for t in toks])
+    flat = np.ascontiguousarray(np.concatenate(toks) if offs[-1] else np.zeros(1, dtype=np.int32))
+    hs = (c_void_p * n)(*[s.h for s in sessions])
+    feats = (c_void_p * n)(*[s.feat.ctypes.data for s in sessions])
+    pos = (c_int32 * n)(*positions)
+    return host.dflash_committed_batch(hs, n, flat.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                       offs.ctypes.data_as(ctypes.POINTER(c_int32)), feats, pos)
+
+
+def test_committed_batch_equals_single_commits(host):
+    """dflash_committed_batch leaves every session as dflash_committed on each
+    would, with the same history writes, row copies and context passes:
+    a plain run, a run that repeats committed positions (skipped), a run that
+    reaches the flush threshold (flushes), and a history ring that wraps."""
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    assert rc == 0
+    one = _shared_sessions(host, ctx, 4, capacity=2048)
+    many = _shared_sessions(host, ctx, 4, capacity=2048)
+    for group in (one, many):
+        group[1].committed(np.arange(6), None, 0)
+        for p in range(0, 505, 5):              # session 3: 505 history tokens, 1 pending row short of a flush
+            group[3].committed(np.arange(5) + p, None, p)
+    _trace(host)
+    runs = [np.arange(4) + 100, np.arange(8) + 200, np.arange(20) + 300, np.arange(9) + 400]
+    positions = [0, 3, 0, 505]                  # session 1 repeats positions 3..5
+    for s, r, p in zip(one, runs, positions):
+        s.committed(r, None, p)
+    t_one = _trace(host)
+    abi.check(host, _commit_batch(host, many, runs, positions))
+    t_many = _trace(host)
+    assert [s.state() for s in many] == [s.state() for s in one]
+    assert [s.rows_written for s in many] == [s.rows_written for s in one]
+    # the same history writes, row copies and context rows (a single-session
+    # call names its session 0, so session indices are dropped)
+    def planned(trace):
+        return sorted(re.sub(r" sess=\d+", "", ln) for ln in trace)
+    assert planned(t_many) == planned(t_one)
+    st = [s.state() for s in many]
+    assert st[0] == (0, 4, 0, 0) and st[1][:2] == (0, 11)    # 6 pending + the 5 rows past them
+    assert st[2][:2] == (20, 0)                 # reached flush_rows = 16: flushed
+
+
+def test_committed_batch_rejects_any_bad_run(host):
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    ss = _shared_sessions(host, ctx, 3, capacity=64)
+    ss[0].committed(np.arange(3), None, 0)
+    before = [s.state() for s in ss]
+    _trace(host)
+    # session 2's run starts past its frontier: the whole batch is refused
+    rc = _commit_batch(host, ss, [np.arange(2), np.arange(2), np.arange(2)], [3, 0, 5])
+    assert rc == abi.E_CONTEXT_GAP
+    assert [s.state() for s in ss] == before and _trace(host) == []
+    rc = _commit_batch(host, [ss[0], ss[0]], [np.arange(2), np.arange(2)], [3, 5])
+    assert rc == abi.E_ARG                      # a session twice
+    rc = _commit_batch(host, ss[:1], [np.arange(70)], [3])
+    assert rc == abi.E_CAPACITY                 # 73 + block > capacity 64
+    assert [s.state() for s in ss] == before

@@ -188,7 +188,7 @@ def test_batched_propose_matches_oracle(cuda, case):
     """dflash_propose_batch over sessions of ragged context (one with none)
     equals each session's own oracle propose; one batched sample call draws
     every row with per-session penalties."""
-    from block_diffusion_drafter_fwd_amd import propose_batch, sample
+    from block_diffusion_drafter_fwd_amd import committed_batch, propose_batch, sample
     from oracle.sampler import sample_row
     vocab, lens, mts = BATCHED[case][:3]
     rounds = BATCHED[case][3] if len(BATCHED[case]) > 3 else 3
@@ -236,12 +236,22 @@ def test_batched_propose_matches_oracle(cuda, case):
                 rep.note("probs/bound", e / pt)
                 assert e < pt, (k, i, e, pt)
         check_ids(ids, ref, rep)
+        # every session's accepted run in one dflash_committed_batch call; the
+        # oracle commits session by session
+        bs, runs, fts, poss = [], [], [], []
         for k, pr in enumerate(pairs):
             pr.commit_block()
             F = pr.o[0].ctx_offset + pr.o[0].pending_count
             if F:
                 toks = np.array([cur[k], 7], dtype=np.int32)
-                pr.committed(toks, srcs[k].features(F, 2), F)
+                for o in pr.o:
+                    o.committed(toks, srcs[k].features(F, 2), F)
+                bs.append(pr.g)
+                runs.append(toks)
+                fts.append(feats_dev(cfg, srcs[k].features(F, 2)))
+                poss.append(F)
+        if bs:
+            committed_batch(bs, runs, fts, poss)
     say(f"[parity] batched worst {rep.worst} ids {rep.ids_compared}/{rep.ids_skipped}")
     for pr in pairs:
         pr.flush()
