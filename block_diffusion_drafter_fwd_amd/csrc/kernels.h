@@ -15,7 +15,7 @@ namespace kern {
 constexpr int kMaxSeg = 32;        // column segments of one GEMM launch
 constexpr int kMaxOut = 16;        // outputs of one norm launch
 constexpr int kMaxL = 16;          // layers of one head-finish launch
-constexpr int kUploadWords = 480;  // 1920-byte payload of one upload launch
+constexpr int kUploadWords = 960;  // 3840-byte payload of one upload launch (kernel arguments: 4 KiB)
 
 // One sequence (session) of a batched call.
 struct SeqDesc {
