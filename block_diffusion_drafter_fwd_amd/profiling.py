@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the measurement record.
 
     python -m block_diffusion_drafter_fwd_amd.profiling stats KERNEL_STATS_CSV [--trace KERNEL_TRACE_CSV]
-        [--command "..."] [--top N]
+        [--marker REGEX] [--command "..."] [--top N]
     python -m block_diffusion_drafter_fwd_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV
         --kernel REGEX [--command "..."] [--source FILE] [--out JSON]
 
@@ -112,6 +112,8 @@ def main(argv=None):
     s.add_argument("--trace")
     s.add_argument("--command", default="")
     s.add_argument("--top", type=int, default=25)
+    s.add_argument("--marker", default=r"k_gemm_skinny_p<4, 1",
+                   help="regex of the kernel launched once per round (the unembedding)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -128,7 +130,7 @@ def main(argv=None):
         text.append(stats(a.csv, a.top))
         if a.trace:
             text.append("")
-            text.append(per_round(a.trace))
+            text.append(per_round(a.trace, a.marker))
         print("\n".join(text))
     else:
         d = traffic(a.fetch, a.write, a.kernel, a.source, a.copy_kernel)
