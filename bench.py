@@ -105,8 +105,8 @@ def mfma_line(flops, avg_s, **extra):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
-                                   "not an implemented path", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the drafter runs on one GPU only; sharding across GPUs is described, "
+                                   "not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 
