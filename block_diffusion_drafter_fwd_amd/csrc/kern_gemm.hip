@@ -204,11 +204,15 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GA a) {
 // per-tile kernel when N is large (the unembedding reads 622 MB of weights
 // against 64 KB of activations).
 // ---------------------------------------------------------------------------
-template <int STEPS, int TAG, class GA>
+template <int STEPS, int TAG, class GA, int TPI>
 __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
-    __shared__ float red[kSkWaves][64 * 4];
+    // TPI adjacent 16-column tiles per iteration (2: the plain store form,
+    // e.g. the unembedding; the reduction and its barriers then serve twice
+    // the bytes); the paired SwiGLU form takes one
+    static_assert(TPI == 1 || TPI == 2, "tiles per iteration");
+    __shared__ float red[kSkWaves][TPI][64 * 4];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const bool pair = a.mode == kSwiGLU;
+    const bool pair = TPI == 1 && a.mode == kSwiGLU;
     const int nw = pair ? kSkWaves / 2 : kSkWaves;
     const int wv = pair ? (wave & (kSkWaves / 2 - 1)) : wave;
     const int r = lane & 15, q = lane >> 4;
@@ -229,49 +233,74 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
         for (int j = 0; j < 2 * STEPS; ++j) av[j] = aval ? av[j] : zero;
     }
     const int t = threadIdx.x;
-    for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        const GemmSeg g = pair ? a.seg[wave / (kSkWaves / 2)] : a.seg[find_seg(a, tile)];
-        const int n0 = (tile - g.tile0) * 16;
-        const bool bval = n0 + r < g.N;
-        const uint16_t* Bp = (const uint16_t*)g.B + (size_t)(bval ? n0 + r : 0) * g.ldb + q * 16;
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    for (int tile0 = blockIdx.x * TPI; tile0 < a.ntiles; tile0 += gridDim.x * TPI) {
+        const uint16_t* Bp[TPI];
+        bool bval[TPI];
+        int n0[TPI];
+        GemmSeg gs[TPI];
+#pragma unroll
+        for (int i = 0; i < TPI; ++i) {
+            const int tile = min(tile0 + i, a.ntiles - 1);
+            gs[i] = pair ? a.seg[wave / (kSkWaves / 2)] : a.seg[find_seg(a, tile)];
+            n0[i] = (tile - gs[i].tile0) * 16;
+            bval[i] = tile0 + i < a.ntiles && n0[i] + r < gs[i].N;
+            Bp[i] = (const uint16_t*)gs[i].B + (size_t)(bval[i] ? n0[i] + r : 0) * gs[i].ldb + q * 16;
+        }
+        f32x4_t acc0[TPI], acc1[TPI];
+#pragma unroll
+        for (int i = 0; i < TPI; ++i) acc0[i] = acc1[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j0 = 0; j0 < STEPS; j0 += 4) {
-            u32x4_t bv[8];
+            u32x4_t bv[TPI][8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int k = (wv + (j0 + u) * nw) << 6;
-                bv[2 * u] = *(const u32x4_t*)(Bp + k);
-                bv[2 * u + 1] = *(const u32x4_t*)(Bp + k + 8);
-            }
+            for (int i = 0; i < TPI; ++i)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) bv[u] = bval ? bv[u] : zero;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u & 1) {
-                    acc1 = mfma32(av[2 * (j0 + u)], bv[2 * u], acc1);
-                    acc1 = mfma32(av[2 * (j0 + u) + 1], bv[2 * u + 1], acc1);
-                } else {
-                    acc0 = mfma32(av[2 * (j0 + u)], bv[2 * u], acc0);
-                    acc0 = mfma32(av[2 * (j0 + u) + 1], bv[2 * u + 1], acc0);
+                for (int u = 0; u < 4; ++u) {
+                    const int k = (wv + (j0 + u) * nw) << 6;
+                    bv[i][2 * u] = *(const u32x4_t*)(Bp[i] + k);
+                    bv[i][2 * u + 1] = *(const u32x4_t*)(Bp[i] + k + 8);
                 }
-            }
-        }
-        const f32x4_t acc = acc0 + acc1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave][lane * 4 + e] = acc[e];
+            for (int i = 0; i < TPI; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) bv[i][u] = bval[i] ? bv[i][u] : zero;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < TPI; ++i) {
+                    if (u & 1) {
+                        acc1[i] = mfma32(av[2 * (j0 + u)], bv[i][2 * u], acc1[i]);
+                        acc1[i] = mfma32(av[2 * (j0 + u) + 1], bv[i][2 * u + 1], acc1[i]);
+                    } else {
+                        acc0[i] = mfma32(av[2 * (j0 + u)], bv[i][2 * u], acc0[i]);
+                        acc0[i] = mfma32(av[2 * (j0 + u) + 1], bv[i][2 * u + 1], acc0[i]);
+                    }
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < TPI; ++i) {
+            const f32x4_t acc = acc0[i] + acc1[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[wave][i][lane * 4 + e] = acc[e];
+        }
         __syncthreads();
-        const int m = t >> 4, nn = t & 15;
-        if (t < 256 && m < a.M) {
+        // threads 256 i .. 256 i + 255 finish tile i of the iteration
+        const int i = t >> 8, m = (t & 255) >> 4, nn = t & 15;
+        if (i < TPI && m < a.M && tile0 + i < a.ntiles) {
+            // (selects, not a runtime index into the per-tile arrays, which
+            // would put them in scratch memory)
+            const int gN = (TPI == 2 && i) ? gs[TPI - 1].N : gs[0].N;
+            const int gcol = (TPI == 2 && i) ? gs[TPI - 1].c_col0 : gs[0].c_col0;
+            const int ni = (TPI == 2 && i) ? n0[TPI - 1] : n0[0];
             const int idx = (nn + 16 * (m >> 2)) * 4 + (m & 3);
             float s0 = 0.f;
-            for (int w = 0; w < nw; ++w) s0 += red[w][idx];
+            for (int w = 0; w < nw; ++w) s0 += red[w][i][idx];
             if (pair) {
-                if (n0 + nn < a.seg[0].N) {
+                if (n0[0] + nn < a.seg[0].N) {
                     float s1 = 0.f;
-                    for (int w = nw; w < kSkWaves; ++w) s1 += red[w][idx];
+                    for (int w = nw; w < kSkWaves; ++w) s1 += red[w][0][idx];
                     const float v = s0 / (1.f + __expf(-s0)) * s1;
-                    const size_t o = (size_t)m * a.ldo + n0 + nn;
+                    const size_t o = (size_t)m * a.ldo + n0[0] + nn;
                     if (a.out_bf16) {
                         uint32_t u = __float_as_uint(v);
                         u += 0x7FFFu + ((u >> 16) & 1u);
@@ -280,8 +309,8 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
                         ((float*)a.out)[o] = v;
                     }
                 }
-            } else if (n0 + nn < g.N) {
-                float* p = a.C + (size_t)m * a.ldc + g.c_col0 + n0 + nn;   // kPartial: split 0 of 1
+            } else if (ni + nn < gN) {
+                float* p = a.C + (size_t)m * a.ldc + gcol + ni + nn;   // kPartial: split 0 of 1
                 *p = a.mode == kAccumulate ? *p + s0 : s0;
             }
         }
@@ -929,12 +958,20 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         // per-tile kernel, with more workgroups in flight, is faster)
         if (shared_a && (steps == 4 || steps == 8) && ntiles >= 2 * grid) {
             if (splits_out) *splits_out = 1;
-            if (steps == 4) {
-                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1, GA>), dim3(grid), dim3(512), 0, st, a);
-                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA>), dim3(grid), dim3(512), 0, st, a);
+            // four k steps per wave: two tiles per iteration (measured on the
+            // 151936-token unembedding: 124.4 -> 122.0 us); at eight steps the
+            // second tile's registers (172 VGPRs) cost the CU its second
+            // workgroup and the single-tile form is faster (372 vs 400 us);
+            // the paired SwiGLU form takes one tile
+            const dim3 g2((unsigned)std::min(2 * num_cus, (ntiles + 1) / 2));
+            if (steps == 4 && !swiglu) {
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1, GA, 2>), g2, dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 2>), g2, dim3(512), 0, st, a);
+            } else if (steps == 4) {
+                hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 1>), dim3(grid), dim3(512), 0, st, a);
             } else {
-                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<8, 1, GA>), dim3(grid), dim3(512), 0, st, a);
-                else hipLaunchKernelGGL((k_gemm_skinny_p<8, 0, GA>), dim3(grid), dim3(512), 0, st, a);
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<8, 1, GA, 1>), dim3(grid), dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<8, 0, GA, 1>), dim3(grid), dim3(512), 0, st, a);
             }
             return hipGetLastError();
         }
