@@ -204,17 +204,18 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GA a) {
 // per-tile kernel when N is large (the unembedding reads 622 MB of weights
 // against 64 KB of activations).
 // ---------------------------------------------------------------------------
-template <int STEPS, int TAG, class GA, int TPI>
-__global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
+template <int STEPS, int TAG, class GA, int TPI, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_skinny_p(GA a) {
     // TPI adjacent 16-column tiles per iteration (2: the plain store form,
     // e.g. the unembedding; the reduction and its barriers then serve twice
     // the bytes); the paired SwiGLU form takes one
     static_assert(TPI == 1 || TPI == 2, "tiles per iteration");
-    __shared__ float red[kSkWaves][TPI][64 * 4];
+    static_assert(NW == 8 || NW == 16, "waves");
+    __shared__ float red[NW][TPI][64 * 4];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const bool pair = TPI == 1 && a.mode == kSwiGLU;
-    const int nw = pair ? kSkWaves / 2 : kSkWaves;
-    const int wv = pair ? (wave & (kSkWaves / 2 - 1)) : wave;
+    const bool pair = TPI == 1 && NW == kSkWaves && a.mode == kSwiGLU;
+    const int nw = pair ? NW / 2 : NW;
+    const int wv = pair ? (wave & (NW / 2 - 1)) : wave;
     const int r = lane & 15, q = lane >> 4;
     const bool aval = r < a.M;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
 #pragma unroll
         for (int i = 0; i < TPI; ++i) {
             const int tile = min(tile0 + i, a.ntiles - 1);
-            gs[i] = pair ? a.seg[wave / (kSkWaves / 2)] : a.seg[find_seg(a, tile)];
+            gs[i] = pair ? a.seg[wave / (NW / 2)] : a.seg[find_seg(a, tile)];
             n0[i] = (tile - gs[i].tile0) * 16;
             bval[i] = tile0 + i < a.ntiles && n0[i] + r < gs[i].N;
             Bp[i] = (const uint16_t*)gs[i].B + (size_t)(bval[i] ? n0[i] + r : 0) * gs[i].ldb + q * 16;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(512) void k_gemm_skinny_p(GA a) {
             if (pair) {
                 if (n0[0] + nn < a.seg[0].N) {
                     float s1 = 0.f;
-                    for (int w = nw; w < kSkWaves; ++w) s1 += red[w][0][idx];
+                    for (int w = nw; w < NW; ++w) s1 += red[w][0][idx];
                     const float v = s0 / (1.f + __expf(-s0)) * s1;
                     const size_t o = (size_t)m * a.ldo + n0[0] + nn;
                     if (a.out_bf16) {
@@ -958,20 +959,25 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         // per-tile kernel, with more workgroups in flight, is faster)
         if (shared_a && (steps == 4 || steps == 8) && ntiles >= 2 * grid) {
             if (splits_out) *splits_out = 1;
-            // four k steps per wave: two tiles per iteration (measured on the
-            // 151936-token unembedding: 124.4 -> 122.0 us); at eight steps the
-            // second tile's registers (172 VGPRs) cost the CU its second
-            // workgroup and the single-tile form is faster (372 vs 400 us);
-            // the paired SwiGLU form takes one tile
-            const dim3 g2((unsigned)std::min(2 * num_cus, (ntiles + 1) / 2));
+            // two tiles per iteration (the reduction and its barriers serve
+            // twice the bytes): four k steps per wave on 8 waves (K = 2048:
+            // the 151936-token unembedding 124.2 -> 122.1 us); at K = 4096 the
+            // 8-wave form would need eight steps (172 VGPRs with two tiles, one
+            // workgroup per CU), so 16 waves of four steps, one workgroup per
+            // CU resident at once (the 262144-token unembedding 369 -> 345 us);
+            // the paired SwiGLU form takes one tile on 8 waves
             if (steps == 4 && !swiglu) {
-                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1, GA, 2>), g2, dim3(512), 0, st, a);
-                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 2>), g2, dim3(512), 0, st, a);
+                const dim3 g2((unsigned)std::min(2 * num_cus, (ntiles + 1) / 2));
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1, GA, 2, 8>), g2, dim3(512), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 2, 8>), g2, dim3(512), 0, st, a);
             } else if (steps == 4) {
-                hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 1>), dim3(grid), dim3(512), 0, st, a);
+                hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 1, 8>), dim3(grid), dim3(512), 0, st, a);
+            } else if (!swiglu) {
+                const dim3 g16((unsigned)std::min(num_cus, (ntiles + 1) / 2));
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<4, 1, GA, 2, 16>), g16, dim3(1024), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_skinny_p<4, 0, GA, 2, 16>), g16, dim3(1024), 0, st, a);
             } else {
-                if (tag == 1) hipLaunchKernelGGL((k_gemm_skinny_p<8, 1, GA, 1>), dim3(grid), dim3(512), 0, st, a);
-                else hipLaunchKernelGGL((k_gemm_skinny_p<8, 0, GA, 1>), dim3(grid), dim3(512), 0, st, a);
+                hipLaunchKernelGGL((k_gemm_skinny_p<8, 0, GA, 1, 8>), dim3(grid), dim3(512), 0, st, a);
             }
             return hipGetLastError();
         }
