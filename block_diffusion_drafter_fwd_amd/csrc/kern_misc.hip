@@ -401,7 +401,8 @@ hipError_t cache_read(const void* cache, int32_t cap, int32_t ring, int32_t Hkv,
 // Sampler.  Penalties (CTRL repetition penalty over the distinct tokens of the
 // session's committed history) -> temperature -> softmax probabilities and a
 // Gumbel-max draw, u from Philox4x64-10 (Salmon et al., SC'11) at counter
-// (t div 4, row, round, 0) under key (seed, stream), word t mod 4, top 23 bits.
+// (t div 8, row, round, 0) under key (seed, stream), word (t mod 8) div 2,
+// bits 63..41 for even t and 40..18 for odd t.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
     const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
@@ -487,9 +488,9 @@ __device__ __forceinline__ float gumbel(float u) {
 }
 
 // Per (row, vocabulary chunk): max and sum-exp of z'/T (online), and the
-// Gumbel-max candidate (or the argmax when greedy).  Four consecutive tokens
-// per thread: one 16-byte logits load, one history-bitmap word, one Philox
-// call whose four words are the tokens' draws.
+// Gumbel-max candidate (or the argmax when greedy).  Eight consecutive tokens
+// per thread: two 16-byte logits loads, one history-bitmap word, one Philox
+// call whose four words carry the eight draws (two 23-bit fields a word).
 __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int c = blockIdx.x, r = blockIdx.y;
     const RowInfo ri = a.rows[r];
@@ -499,42 +500,46 @@ __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     const bool greedy = a.temperature == 0.f;
     const float inv_t = greedy ? 0.f : 1.f / a.temperature;
-    const bool vec = (a.V & 3) == 0;
+    const bool vec = (a.V & 7) == 0;
     const float* zr = a.logits + (size_t)r * a.V;
-    for (int qd = (t_lo >> 2) + threadIdx.x; qd * 4 < t_hi; qd += 256) {
-        const int t0 = qd * 4;
-        float z[4];
-        if (vec) {   // t0 + 3 < V: V and the chunk bounds are multiples of 4
-            const float4 v = *(const float4*)(zr + t0);
-            z[0] = v.x;
-            z[1] = v.y;
-            z[2] = v.z;
-            z[3] = v.w;
+    for (int oc = (t_lo >> 3) + threadIdx.x; oc * 8 < t_hi; oc += 256) {
+        const int t0 = oc * 8;
+        float z[8];
+        if (vec) {   // t0 + 7 < V: V and the chunk bounds are multiples of 8
+            const float4 v0 = *(const float4*)(zr + t0), v1 = *(const float4*)(zr + t0 + 4);
+            z[0] = v0.x;
+            z[1] = v0.y;
+            z[2] = v0.z;
+            z[3] = v0.w;
+            z[4] = v1.x;
+            z[5] = v1.y;
+            z[6] = v1.z;
+            z[7] = v1.w;
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) z[j] = t0 + j < t_hi ? zr[t0 + j] : -INFINITY;
+            for (int j = 0; j < 8; ++j) z[j] = t0 + j < t_hi ? zr[t0 + j] : -INFINITY;
         }
         if (a.use_penalty) {
-            const uint32_t word = bm[t0 >> 5] >> (t0 & 31);   // the four tokens share one word
+            const uint32_t word = bm[t0 >> 5] >> (t0 & 31);   // the eight tokens share one word
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j)
                 if ((word >> j) & 1u) z[j] = z[j] > 0.f ? z[j] / a.rho : z[j] * a.rho;
         }
         if (greedy) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j)
                 if (t0 + j < t_hi && (z[j] > s.best || (z[j] == s.best && t0 + j < s.idx))) {
                     s.best = z[j];
                     s.idx = t0 + j;
                 }
             continue;
         }
-        uint64_t w[4] = {(uint64_t)qd, (uint64_t)ri.pos, (uint64_t)a.round, 0};
+        uint64_t w[4] = {(uint64_t)oc, (uint64_t)ri.pos, (uint64_t)a.round, 0};
         philox4x64_10(w, sd.seed, sd.stream);
-        float sv[4];
+        float sv[8];
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
             sv[j] = t0 + j < t_hi ? z[j] * inv_t : -INFINITY;
             mx = fmaxf(mx, sv[j]);
         }
@@ -543,10 +548,12 @@ __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
             s.m = mx;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
             if (t0 + j >= t_hi) break;
             s.l += __expf(sv[j] - s.m);
-            const float u = ((float)(w[j] >> 41) + 0.5f) * 0x1p-23f;
+            const uint64_t wj = w[j >> 1];
+            const uint32_t bits = (j & 1) ? (uint32_t)((wj >> 18) & 0x7FFFFFu) : (uint32_t)(wj >> 41);
+            const float u = ((float)bits + 0.5f) * 0x1p-23f;
             const float key = sv[j] + gumbel(u);
             if (key > s.best || (key == s.best && t0 + j < s.idx)) {
                 s.best = key;

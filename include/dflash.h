@@ -250,7 +250,8 @@ int dflash_propose_batch(dflash_session* const* sessions, int32_t count, const i
  * session's committed history only.  ids_out: device int32 [R]; probs_out:
  * device fp32 [R, V] or NULL (ignored when greedy).  The draw of row r of
  * session k is keyed by (seed, stream_id) of the session and counter
- * (t div 4, r - row_offsets[k], round, 0).  Errors: E_ARG. */
+ * (t div 8, r - row_offsets[k], round, 0): word (t mod 8) div 2, bits 63..41
+ * for even t and 40..18 for odd t.  Errors: E_ARG. */
 int dflash_sample(dflash_session* const* sessions, int32_t count, const int32_t* row_offsets,
                   const float* logits, const dflash_sample_params* params, int32_t* ids_out,
                   float* probs_out);

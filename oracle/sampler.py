@@ -11,9 +11,10 @@ the readings taken here are:
 * temperature T: scores z'/T; probabilities softmax(z'/T); T == 0 is greedy
   (argmax of z', lowest index on an exact tie) and returns no probabilities;
 * the draw is Gumbel-max: id = argmax_t (z'_t/T + g_t), g_t = -log(-log u_t),
-  u_t = (top 23 bits of word (t mod 4) of Philox4x64-10 at counter
-  (t div 4, row, round, 0) under key (seed, stream)) + 1/2, times 2**-23,
-  a value exactly representable in float32.
+  u_t = (b_t + 1/2) * 2**-23, a value exactly representable in float32, where
+  b_t is a 23-bit field of word ((t mod 8) div 2) of Philox4x64-10 at counter
+  (t div 8, row, round, 0) under key (seed, stream): bits 63..41 of the word
+  for even t, bits 40..18 for odd t (one generator call serves eight tokens).
 
 Philox4x64-10 is written from its published definition (Salmon, Moraes, Dror,
 Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds of
@@ -64,12 +65,14 @@ def philox4x64_10(ctr, key):
 def uniforms(seed: int, stream: int, rnd: int, row: int, vocab: int) -> np.ndarray:
     """u_t in (0, 1) for t in 0..vocab-1 (exact float32 values, returned float64)."""
     t = np.arange(vocab, dtype=np.uint64)
-    q = t >> np.uint64(2)
-    words = philox4x64_10((q, np.full_like(q, row), np.full_like(q, rnd), np.zeros_like(q)),
+    o = t >> np.uint64(3)
+    words = philox4x64_10((o, np.full_like(o, row), np.full_like(o, rnd), np.zeros_like(o)),
                           (seed, stream))
-    w = np.stack(words, axis=0)[(t & np.uint64(3)).astype(np.int64), np.arange(vocab)]
-    top = (w >> np.uint64(41)).astype(np.float64)
-    return (top + 0.5) * 2.0 ** -23
+    w = np.stack(words, axis=0)[((t >> np.uint64(1)) & np.uint64(3)).astype(np.int64), np.arange(vocab)]
+    hi = w >> np.uint64(41)
+    lo = (w >> np.uint64(18)) & np.uint64(0x7FFFFF)
+    bits = np.where((t & np.uint64(1)) == 0, hi, lo).astype(np.float64)
+    return (bits + 0.5) * 2.0 ** -23
 
 
 def penalize(z: np.ndarray, history: Sequence[int], rho: float) -> np.ndarray:

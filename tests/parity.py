@@ -152,12 +152,32 @@ class Pair:
                 assert ek < tol(self.cfg) and ev < tol(self.cfg), (l, ek, ev)
 
 
+def id_margin(cfg, z_gpu, z_ref, temperature: float, rho: float = 1.0) -> float:
+    """Gap above which the GPU must return the oracle's id.  Greedy rows: the
+    tie margin (one bf16 ulp of the top logit).  Sampled rows: that margin
+    over T, or twice the row's measured logit deviation in score units when
+    larger — both sides score token t as z'_t/T + g_t with the same g_t, z'
+    moves by at most rho times the logit deviation (the penalty), and two
+    score vectors within d of each other per token agree on the argmax
+    whenever the oracle's top-1/top-2 gap exceeds 2d."""
+    zr = np.asarray(z_ref, dtype=np.float64)
+    m = margin(cfg, float(np.max(np.abs(zr))), temperature)
+    if temperature <= 0:
+        return m
+    d = float(np.max(np.abs(np.asarray(z_gpu, dtype=np.float64) - zr))) * max(1.0, rho) / temperature
+    return max(m, 2.0 * d + 1e-4)
+
+
 def check_ids(gpu_ids, ref_rows, rep: Report):
-    """ref_rows: (oracle id, oracle scores, tie margin) per row."""
+    """ref_rows: (oracle id, oracle scores, margin) per row."""
     for gid, (oid, scores, tau) in zip(gpu_ids, ref_rows):
         if top2_gap(scores) > tau:
             rep.ids_compared += 1
-            assert int(gid) == int(oid), f"id {gid} != oracle {oid} (gap {top2_gap(scores)}, margin {tau})"
+            if int(gid) != int(oid):
+                sc = np.asarray(scores, dtype=np.float64)
+                rank = int(np.sum(sc > sc[int(gid)]))
+                raise AssertionError(f"id {gid} != oracle {oid} (gap {top2_gap(scores)}, margin {tau}; the "
+                                     f"GPU's id is the oracle's rank {rank}, {sc[int(oid)] - sc[int(gid)]} below)")
         else:
             rep.ids_skipped += 1
 
@@ -193,8 +213,8 @@ def run_session_script(drafter, cfg, wl: synth.Workload, weights_np, capacity, r
             for i in range(n):
                 oid, oprob, score = sample_row(out["logits"][i], o.history[-wl.history:] if wl.history else [],
                                                wl.temperature, wl.rep_penalty, pr.seed, pr.sid, r, i)
-                zmax = float(np.max(np.abs(out["logits"][i])))
-                ref.append((oid, score, margin(cfg, zmax, wl.temperature)))
+                ref.append((oid, score, id_margin(cfg, logits[i].double().cpu().numpy(), out["logits"][i],
+                                                  wl.temperature, wl.rep_penalty)))
                 if probs is not None:
                     e = rel_err(probs[i].double().cpu().numpy(), oprob)
                     pt = probs_tol(logits[i].double().cpu().numpy(), out["logits"][i], wl.temperature)

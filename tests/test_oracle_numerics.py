@@ -106,8 +106,10 @@ def test_uniforms_are_exact_float32_in_open_interval():
     # 23-bit grid with a half-step offset
     k = u * 2 ** 23 - 0.5
     np.testing.assert_array_equal(k, np.round(k))
-    # word t mod 4 of the counter block t div 4
+    # tokens 8..15 read the four words of counter block 1: bits 63..41 of word
+    # j for token 8 + 2j, bits 40..18 for token 8 + 2j + 1
     w = philox4x64_10((np.array([1], dtype=np.uint64), np.array([2], dtype=np.uint64),
                        np.array([11], dtype=np.uint64), np.array([0], dtype=np.uint64)), (7, 3))
     for j in range(4):
-        assert u[4 + j] == ((int(w[j][0]) >> 41) + 0.5) * 2.0 ** -23
+        assert u[8 + 2 * j] == ((int(w[j][0]) >> 41) + 0.5) * 2.0 ** -23
+        assert u[8 + 2 * j + 1] == (((int(w[j][0]) >> 18) & 0x7FFFFF) + 0.5) * 2.0 ** -23

@@ -56,3 +56,15 @@ def test_draws_depend_on_every_key_and_counter_field():
     base = uniforms(1, 2, 3, 4, 64)
     for args in [(9, 2, 3, 4), (1, 9, 3, 4), (1, 2, 9, 4), (1, 2, 3, 9)]:
         assert not np.array_equal(base, uniforms(*args, 64))
+
+
+def test_both_fields_of_a_word_are_independent_uniforms():
+    """Tokens 2i and 2i + 1 take disjoint bit fields of one generator word:
+    each marginal is uniform on (0, 1) and the pair is uncorrelated (a field
+    taken twice, or overlapping fields, would fail one of these)."""
+    from scipy.stats import kstest
+    u = np.concatenate([uniforms(3, 1, r, 0, 4096) for r in range(8)])
+    even, odd = u[0::2], u[1::2]
+    assert kstest(even, "uniform").pvalue > 1e-3 and kstest(odd, "uniform").pvalue > 1e-3
+    assert abs(np.corrcoef(even, odd)[0, 1]) < 0.02
+    assert not np.array_equal(even, odd)
