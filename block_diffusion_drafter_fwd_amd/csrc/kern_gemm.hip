@@ -1048,35 +1048,65 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             ntiles += (a.seg[s].N + NT - 1) / NT;
         }
         a.ntiles = ntiles;
-        const int mt4 = (a.M + W8<4>::BM - 1) / W8<4>::BM;
-        bool w8 = pipelined && ntiles * mt4 * 2 >= num_cus;
-        const bool w8big = w8 && a.M > W8<4>::BM && a.M <= W8<8>::BM && ntiles >= 2 * num_cus;
-        // 256-row tiles also for M > 128 when K splits (any count within the
-        // partial slices the consumer sums, each >= 512 k-values) fill at
-        // least 7/8 of the CUs: measured on the 256-row flush shapes (context
-        // k|v 24.3 vs 26.5 us, 4096-wide fc 66 vs 70 us); where they cannot,
-        // 128 x 128 tiles with power-of-two splits
-        int w4_splits = 0;
-        if (pipelined && !w8 && a.M > kMtBM && a.mode == kPartial) {
-            int s = std::min(a.max_splits, num_cus / (ntiles * mt4));
-            while (s > 1 && a.K / s < 512) --s;
-            if (s >= 1 && ntiles * mt4 * s * 8 >= 7 * num_cus) {
-                w8 = true;
-                w4_splits = s;
+        const bool w8big = pipelined && a.M > W8<4>::BM && a.M <= W8<8>::BM && ntiles >= 2 * num_cus;
+        const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
+        const int max_s = a.mode == kPartial ? a.max_splits : 1 << 30;
+        // power-of-two K splits while the grid stays within one workgroup per
+        // CU and a split keeps >= 512 k-values, within the partial slices
+        auto pow2_splits = [&](int base) {
+            int sp = 1;
+            while (base * sp * 2 <= num_cus && a.K / (sp * 2) >= 512) sp *= 2;
+            while (sp > 1 && ((size_t)sp * a.M * a.ldc > cap || sp > max_s)) sp /= 2;
+            return sp;
+        };
+        // the tile form: 128 x 128 (k_gemm_mt, 4 waves) or 256 x 128
+        // (k_gemm_w8, 8 waves; K slices of any count in kPartial mode) by a
+        // cost model that fits the measured shapes: one workgroup per CU is
+        // resident, so a launch takes rounds of resident workgroups x (a
+        // fixed start-up of ~1e7 multiply-adds' time + the multiply-adds of
+        // a workgroup), the 8-wave form ~7% faster per multiply-add.  It keeps
+        // 128-row tiles where 256-row ones would be mostly padding (a
+        // 551-row block: qkv 35.5 us on 256-row tiles) or too few, and takes
+        // 256-row tiles where K slices fill the CUs (the context k|v
+        // projection, 24.3 vs 26.5 us; the 4096-wide fc, 66 vs 70 us)
+        auto cost = [&](int BM, int sp, int kq_, double rate) {
+            const int kc_ = ((a.K + sp - 1) / sp + kq_ - 1) / kq_ * kq_;
+            const int n_sp = (a.K + kc_ - 1) / kc_;
+            const long wgs = (long)ntiles * ((a.M + BM - 1) / BM) * n_sp;
+            const long rounds = (wgs + num_cus - 1) / num_cus;
+            return (double)rounds * (1e7 + (double)BM * 128 * kc_ / rate);
+        };
+        bool w8 = false;
+        int MT, kq, splits;
+        if (w8big) {
+            MT = W8<8>::BM;
+            kq = 256;
+            splits = pow2_splits(ntiles * ((a.M + MT - 1) / MT));
+        } else if (!pipelined) {
+            MT = a.M <= 64 ? 64 : 128;
+            kq = 64;
+            splits = pow2_splits(ntiles * ((a.M + MT - 1) / MT));
+        } else {
+            MT = kMtBM;
+            kq = 256;
+            splits = pow2_splits(ntiles * ((a.M + kMtBM - 1) / kMtBM));
+            if (a.M > kMtBM) {
+                const int b8 = ntiles * ((a.M + W8<4>::BM - 1) / W8<4>::BM);
+                int s8 = pow2_splits(b8);
+                if (a.mode == kPartial) {
+                    s8 = std::max(1, std::min(a.max_splits, num_cus / b8));
+                    while (s8 > 1 && a.K / s8 < 512) --s8;
+                }
+                const double c_mt = cost(kMtBM, splits, 256, 1.0), c_w8 = cost(W8<4>::BM, s8, 128, 1.07);
+                if (c_w8 < c_mt || (c_w8 == c_mt && s8 <= splits)) {
+                    w8 = true;
+                    MT = W8<4>::BM;
+                    kq = 128;
+                    splits = s8;
+                }
             }
         }
-        const int MT = w8big ? W8<8>::BM : w8 ? W8<4>::BM : pipelined ? kMtBM : (a.M <= 64 ? 64 : 128);
-        const int kq = w4_splits ? 128 : pipelined ? 256 : 64;
         const int mtiles = (a.M + MT - 1) / MT;
-        const int base = ntiles * mtiles;
-        // split K while the grid stays within one workgroup per CU (128 KiB of
-        // LDS each) and a split keeps >= 512 k-values
-        int splits = 1;
-        while (base * splits * 2 <= num_cus && a.K / (splits * 2) >= 512) splits *= 2;
-        const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
-        while (splits > 1 && ((size_t)splits * a.M * a.ldc > cap || splits > (a.mode == kPartial ? a.max_splits : 1 << 30)))
-            splits /= 2;
-        if (w4_splits) splits = w4_splits;
         int kc = ((a.K + splits - 1) / splits + kq - 1) / kq * kq;
         splits = (a.K + kc - 1) / kc;
         a.splits = splits;
