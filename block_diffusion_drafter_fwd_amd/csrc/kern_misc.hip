@@ -167,16 +167,26 @@ hipError_t rmsnorm(const NormArgs& a, hipStream_t st) {
 // wave finishes one head (tasks: q heads, then k heads, then v heads).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
+    __shared__ float s_cos[64], s_sin[64];
     const int row = blockIdx.x, li = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nq = (a.q_col >= 0) ? a.Hq : 0;
     const int task = blockIdx.y * 4 + wave;
-    if (task >= nq + 2 * a.Hkv) return;
     const RowInfo ri = a.rows[row];
     const SeqDesc sd = a.seqs[ri.seq];
     const int pos = ri.pos;
-    const int slot = sd.ring ? pos % sd.cap : pos;
     const int half = a.D >> 1;
+    // the row's rotation angles once for the workgroup's four heads (fp64,
+    // rounded to fp32), not once per head
+    if (threadIdx.x < half) {
+        double sn_, cs_;
+        sincos((double)pos * a.inv_freq[threadIdx.x], &sn_, &cs_);
+        s_cos[threadIdx.x] = (float)cs_;
+        s_sin[threadIdx.x] = (float)sn_;
+    }
+    __syncthreads();
+    if (task >= nq + 2 * a.Hkv) return;
+    const int slot = sd.ring ? pos % sd.cap : pos;
     const bool act = lane < half;
     const int layer = a.layer[li];
     int kind, head, col;   // kind 0 q, 1 k, 2 v
@@ -212,9 +222,7 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
             }
         }
         if (act) {
-            double sd_, cd_;
-            sincos((double)pos * a.inv_freq[lane], &sd_, &cd_);
-            const float cs = (float)cd_, sn = (float)sd_;
+            const float cs = s_cos[lane], sn = s_sin[lane];
             const float y1 = x1 * cs - x2 * sn;
             const float y2 = x2 * cs + x1 * sn;
             x1 = y1;
