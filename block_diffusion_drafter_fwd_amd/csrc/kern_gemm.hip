@@ -389,7 +389,11 @@ __device__ __forceinline__ TileItem tile_item(int xcd_remap) {
     return TileItem{l - r * nx, r % ny, r / ny};
 }
 
-template <int TAG, class GA, int BK>
+// PAIR: the gate|up projection with its SwiGLU epilogue.  Tile t covers gate
+// columns [64 t, 64 t + 64) (segment 0, the waves with wn = 0) and the same
+// up columns (segment 1, wn = 1); the up products pass through LDS and the
+// gate waves store silu(gate) * up to the activation buffer.  One split.
+template <int TAG, class GA, int BK, bool PAIR = false>
 __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
     constexpr int KS = BK / 32;                         // 32-wide MFMA k steps per stage
     constexpr int NI = MtRows<BK>::kInst;
@@ -417,7 +421,14 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
             const int am = min(m0 + row, a.M - 1);
             const int ar = a.a_rows ? a.a_rows[am] : am;
             c.pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + lp * 8;
-            c.pb[i] = (const uint16_t*)g.B + (size_t)min(n0 + row, g.N - 1) * g.ldb + lp * 8;
+            if (PAIR) {   // rows 0..63 of the B tile: gate weights, 64..127: up weights
+                const bool up = row >= 64;
+                const uint16_t* Bb = (const uint16_t*)(up ? a.seg[1].B : a.seg[0].B);
+                const int ldb = up ? a.seg[1].ldb : a.seg[0].ldb, nb = up ? a.seg[1].N : a.seg[0].N;
+                c.pb[i] = Bb + (size_t)min(tile * 64 + (row & 63), nb - 1) * ldb + lp * 8;
+            } else {
+                c.pb[i] = (const uint16_t*)g.B + (size_t)min(n0 + row, g.N - 1) * g.ldb + lp * 8;
+            }
         }
     }
     const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
@@ -496,6 +507,46 @@ __global__ __launch_bounds__(256) void k_gemm_mt(GA a) {
         step(kt + 3, sA3, sB3, sA2, sB2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+    if constexpr (PAIR) {
+        // up products of wave (wm, 1) -> LDS (a finished stage per wm), then the
+        // gate wave (wm, 0) of the same rows and columns applies SwiGLU
+        __syncthreads();                                // every wave is done reading the stages
+        float* xs = (float*)(wm == 0 ? sA0 : sA1);      // 64 x 64 floats = one 16 KiB stage
+        if (wn == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xs[(i * 16 + 4 * q + e) * 64 + j * 16 + r] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (wn == 0) {
+            const int I = a.seg[0].N;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = tile * 64 + j * 16 + r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = m0 + wm * 64 + i * 16 + 4 * q + e;
+                        if (n >= I || m >= a.M) continue;
+                        const float gt = acc[i][j][e], up = xs[(i * 16 + 4 * q + e) * 64 + j * 16 + r];
+                        const float v = gt / (1.f + __expf(-gt)) * up;
+                        const size_t o = (size_t)m * a.ldo + n;
+                        if (a.out_bf16) {
+                            uint32_t u = __float_as_uint(v);
+                            u += 0x7FFFu + ((u >> 16) & 1u);
+                            ((uint16_t*)a.out)[o] = (uint16_t)(u >> 16);
+                        } else {
+                            ((float*)a.out)[o] = v;
+                        }
+                    }
+                }
+        }
+        return;
+    }
     // output (m, n) of MFMA tile (i, j): lane (r, q) holds rows 4 q + e of column r
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1048,6 +1099,24 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
             ntiles += (a.seg[s].N + NT - 1) / NT;
         }
         a.ntiles = ntiles;
+        // gate|up with SwiGLU: 128-row tiles pairing 64 gate and 64 up columns,
+        // the epilogue writing the activations (no fp32 gate|up round trip
+        // and no separate SwiGLU pass), when the pairs alone give at least one
+        // workgroup per CU (no K split)
+        if (swiglu && pipelined && a.nseg == 2 && a.seg[0].A == a.seg[1].A && a.seg[0].N == a.seg[1].N) {
+            const int pt = (a.seg[0].N + 63) / 64, mtl = (a.M + kMtBM - 1) / kMtBM;
+            if (pt * mtl >= num_cus) {
+                a.seg[0].tile0 = a.seg[1].tile0 = 0;
+                a.ntiles = pt;
+                a.splits = 1;
+                a.kc = a.K;
+                a.xcd_remap = 1;
+                const dim3 grid3(pt, mtl, 1);
+                if (tag == 1) hipLaunchKernelGGL((k_gemm_mt<1, GA, 64, true>), grid3, dim3(256), 0, st, a);
+                else hipLaunchKernelGGL((k_gemm_mt<0, GA, 64, true>), grid3, dim3(256), 0, st, a);
+                return hipGetLastError();
+            }
+        }
         const bool w8big = pipelined && a.M > W8<4>::BM && a.M <= W8<8>::BM && ntiles >= 2 * num_cus;
         const size_t cap = a.mode == kPartial ? (size_t)a.max_splits * a.M * a.ldc : part_cap_floats;
         const int max_s = a.mode == kPartial ? a.max_splits : 1 << 30;
