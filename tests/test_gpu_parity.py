@@ -261,6 +261,85 @@ def test_batched_propose_matches_oracle(cuda, case):
     assert rep.ids_compared > 0
 
 
+def test_batched_workload_at_full_size_sampled_sessions(cuda):
+    """The batched workload at full size, in the launch configuration the
+    bench times: 64 sessions with log-uniform prompts of 1050..15434 slots
+    (363424 in all) flushed in 256-row chunks, the 5-layer model and the
+    151936-token vocabulary, one batched propose with U{1..15} drafted rows
+    per session (the tiled block GEMMs and the paired SwiGLU epilogue, the
+    multi-round attention split over the host's largest-first order, the
+    256 x 256 unembedding tiles) and one batched sample with penalties and
+    probabilities.  A session's rows depend only on its own context, so the
+    oracle computes three of them on their own: the shortest, the median and
+    the longest.  Feature rows repeat with period 4096 (slot S carries the
+    seeded row S mod 4096, as in the bench)."""
+    from block_diffusion_drafter_fwd_amd import propose_batch, sample
+    from oracle.model import DraftModel
+    from oracle.sampler import sample_row
+    from oracle.session import OracleSession
+    wl = synth.WORKLOADS["batched"]
+    cfg = synth.config(wl.config)
+    B, S, period = cfg.block_size, wl.sessions, 4096
+    assert period % wl.commit_rows == 0
+    lens = synth.session_lengths(wl, 0)
+    say("[parity] batched full size: weights")
+    w = synth.make_weights(cfg, seed=2, gains="random")
+    d = _drafter(cfg, w, max_sessions=S)
+    fs = synth.FeatureSource(cfg, 0, 0)
+    toks, feats = fs.tokens(0, period), fs.features(0, period)
+    feats_d = feats_dev(cfg, feats)
+
+    def chunks(L):
+        for p in range(0, L, wl.commit_rows):
+            o = p % period
+            yield p, o, min(wl.commit_rows, L - p)
+
+    say(f"[parity] batched full size: {sum(lens)} prompt rows on the GPU")
+    sess = [d.session(L + 4 * B, seed=0, stream_id=k) for k, L in enumerate(lens)]
+    for k, s in enumerate(sess):
+        for p, o, T in chunks(lens[k]):
+            s.committed(toks[o:o + T], feats_d[o:o + T], p)
+        s.flush()
+    rng = np.random.default_rng(7)
+    cur = [int(x) for x in rng.integers(0, cfg.vocab, S)]
+    mts = [int(x) for x in rng.integers(1, B, S)]
+    offs, logits = propose_batch(sess, cur, mts)
+    ids, probs = sample(sess, offs, logits, wl.temperature, wl.rep_penalty, wl.history, 0, probs=True)
+    assert offs[S] == sum(mts)
+    ids = ids.cpu().numpy()
+    order = np.argsort(lens, kind="stable")
+    models = [DraftModel(cfg, w, emulate_bf16=e) for e in (False, True)]
+    rep = Report()
+    ref = []
+    for k in (int(order[0]), int(order[S // 2]), int(order[-1])):
+        say(f"[parity] batched full size: oracle session {k} ({lens[k]} slots, {mts[k]} rows)")
+        os_ = [OracleSession(m) for m in models]
+        for o in os_:
+            for p, q, T in chunks(lens[k]):
+                o.committed(toks[q:q + T], feats[q:q + T], p)
+            o.flush()
+        outs = [o.propose(cur[k], mts[k]) for o in os_]
+        assert offs[k + 1] - offs[k] == outs[0]["n"] == mts[k]
+        z_gpu = logits[offs[k]:offs[k + 1]].double().cpu().numpy()
+        for j, out in enumerate(outs):
+            e = rel_err(z_gpu, out["logits"])
+            rep.note(f"logits[{j}]", e)
+            assert e < tol(cfg), (k, j, e)
+        hist = os_[-1].history[-wl.history:]
+        for i in range(mts[k]):
+            z = outs[-1]["logits"][i]
+            oid, op, sc = sample_row(z, hist, wl.temperature, wl.rep_penalty, 0, k, 0, i)
+            ref.append((oid, sc, id_margin(cfg, z_gpu[i], z, wl.temperature, wl.rep_penalty)))
+            e = rel_err(probs[offs[k] + i].double().cpu().numpy(), op)
+            pt = probs_tol(z_gpu[i], z, wl.temperature)
+            rep.note("probs/bound", e / pt)
+            assert e < pt, (k, i, e, pt)
+        sel = slice(offs[k], offs[k + 1])
+        check_ids(ids[sel], ref[-mts[k]:], rep)
+    say(f"[parity] batched full size worst {rep.worst} ids {rep.ids_compared}/{rep.ids_skipped}")
+    assert rep.ids_compared > 0
+
+
 def test_long_context_cache_rows_at_full_length(cuda):
     """The long configuration's whole 131072-slot prompt through 256-row
     flushes, checked at sampled slots: a context row's K/V depend only on the
