@@ -284,15 +284,22 @@ static int write_context(dflash_session* s, const char* extra, int32_t extra_row
         int32_t rows = in_buf + take;
         if (rows > 0 && pos + rows - 1 >= lo) {
             const int32_t first = (int32_t)std::max<int64_t>(0, std::min<int64_t>((int64_t)lo - pos, rows));
-            // only rows at or past `first` are projected; copy those of the extra rows
+            // only rows at or past `first` are projected.  A chunk made only of
+            // the caller's rows is projected from them where they lie (the
+            // forward is enqueued now, so it reads them in stream order, as a
+            // copy would); otherwise the caller's rows are copied after the
+            // buffered ones
+            const char* direct = extra ? extra + (size_t)(used + first) * rb : nullptr;
+            const bool from_caller = in_buf == 0 && direct && ((uintptr_t)direct & 15) == 0;
             int32_t copy_from = std::max(first, in_buf);
-            if (copy_from < rows) {
+            if (!from_caller && copy_from < rows) {
                 int rc = ctx->engine->copy_rows(s->pending_buf() + (size_t)copy_from * rb,
                                                 extra + (size_t)(used + copy_from - in_buf) * rb,
                                                 (size_t)(rows - copy_from) * rb, s->stream);
                 if (rc) return rc;
             }
-            std::vector<CtxSeg> segs{{0, s->pending_buf() + (size_t)first * rb, rows - first, pos + first}};
+            const char* src = from_caller ? direct : s->pending_buf() + (size_t)first * rb;
+            std::vector<CtxSeg> segs{{0, src, rows - first, pos + first}};
             int rc = ctx->engine->ctx_forward(views, segs, s->ws, s->ws_sessions, s->stream);
             if (rc) return rc;
             written += rows - first;

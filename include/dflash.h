@@ -182,10 +182,13 @@ int dflash_session_close(dflash_session* s);
 /* A committed run (dflash.go committed): tokens_host[T] at positions
  * position..position+T-1 and their tap features features_dev, a device
  * [T, taps*Ht] array of the config dtype.  start = ctxOffset + pending -
- * position; start < 0 is E_CONTEXT_GAP (nothing changes); rows [start, T) are
- * copied into the pending buffer (the caller may free its buffer on return,
- * in stream order) and their tokens join the history; reaching flush_rows
- * pending rows flushes.  Errors: E_ARG, E_CONTEXT_GAP, E_CAPACITY. */
+ * position; start < 0 is E_CONTEXT_GAP (nothing changes); rows [start, T)
+ * join the pending rows and their tokens the history; reaching flush_rows
+ * pending rows flushes.  Rows that stay pending are copied into the pending
+ * buffer; a flushed chunk made only of this run's rows (16-byte aligned) is
+ * projected where it lies by the forward this call enqueues.  Either way the
+ * caller may free its buffer on return, in stream order.  Errors: E_ARG,
+ * E_CONTEXT_GAP, E_CAPACITY. */
 int dflash_committed(dflash_session* s, const int32_t* tokens_host, const void* features_dev,
                      int32_t T, int32_t position);
 
