@@ -189,6 +189,30 @@ def test_chunked_flush_plan(host):
     assert s.state() == (45, 0, 45, 0) and s.rows_written == 45
 
 
+def test_flushed_chunks_of_fresh_rows_are_read_in_place(host):
+    """A flushed chunk made only of the committed run's rows is projected
+    from the caller's buffer (no copy); rows joining buffered ones, rows that
+    stay pending and unaligned rows are copied into the pending buffer."""
+    fm = FakeModel(host, flush_rows=16)
+    rc, ctx = fm.create()
+    assert rc == 0
+    s = HostSession(host, ctx)
+
+    def commit(T, pos, offset=0):
+        t = np.arange(pos, pos + T, dtype=np.int32)
+        abi.check(host, host.dflash_committed(s.h, t.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                              s.feat.ctypes.data + offset, T, pos))
+        return [l for l in _trace(host) if l.startswith(("copy", "ctx"))]
+
+    assert s.feat.ctypes.data % 16 == 0
+    _trace(host)
+    assert commit(40, 0) == ["ctx sess=0 pos0=0 rows=16", "ctx sess=0 pos0=16 rows=16", "ctx sess=0 pos0=32 rows=8"]
+    assert commit(5, 40) == ["copy rows=5"]
+    assert commit(20, 45) == ["copy rows=11", "ctx sess=0 pos0=40 rows=16", "ctx sess=0 pos0=56 rows=9"]
+    assert commit(16, 65, offset=2) == ["copy rows=16", "ctx sess=0 pos0=65 rows=16"]
+    assert s.state() == (81, 0, 81, 0) and s.rows_written == 81
+
+
 def test_window_drop_plan_skips_old_chunks(host):
     fm = FakeModel(host, flush_rows=16, window=6, causal=0)
     rc, ctx = fm.create()
