@@ -331,14 +331,22 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
                 srcs.push_back((uint64_t)((const char*)g.rows + (size_t)r * rb));
             }
         }
-        Tables tb;
-        const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
-        const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
-        const size_t o_src = sj - si > 1 ? tb.add(srcs.data(), sizeof(uint64_t) * srcs.size()) : 0;
+        // one segment (a session's flush): its rows' positions and cache go
+        // to the head finish in the kernel arguments, and no table is uploaded
+        const bool one = sj - si == 1;
         char* tab = base + w.tables;
-        HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
-        const SeqDesc* d_desc = (const SeqDesc*)(tab + o_desc);
-        const RowInfo* d_info = (const RowInfo*)(tab + o_info);
+        const SeqDesc* d_desc = nullptr;
+        const RowInfo* d_info = nullptr;
+        size_t o_src = 0;
+        if (!one) {
+            Tables tb;
+            const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+            const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+            o_src = tb.add(srcs.data(), sizeof(uint64_t) * srcs.size());
+            HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+            d_desc = (const SeqDesc*)(tab + o_desc);
+            d_info = (const RowInfo*)(tab + o_info);
+        }
 
         // A operand of fc: the segment rows themselves, or gathered / aux-normed
         const void* A = segs[si].rows;
@@ -419,6 +427,12 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             h.src_stride = (int64_t)rows * ldkv;
             h.rows = d_info;
             h.seqs = d_desc;
+            if (one) {
+                h.pos0 = segs[si].pos0;
+                h.cache0 = descs[0].cache;
+                h.cap0 = descs[0].cap;
+                h.ring0 = descs[0].ring;
+            }
             h.ld = ldkv;
             h.nrows = rows;
             h.D = c.head_dim;

@@ -172,9 +172,21 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nq = (a.q_col >= 0) ? a.Hq : 0;
     const int task = blockIdx.y * 4 + wave;
-    const RowInfo ri = a.rows[row];
-    const SeqDesc sd = a.seqs[ri.seq];
-    const int pos = ri.pos;
+    int pos, cap, ring;
+    void* cache;
+    if (a.rows) {
+        const RowInfo ri = a.rows[row];
+        const SeqDesc sd = a.seqs[ri.seq];
+        pos = ri.pos;
+        cap = sd.cap;
+        ring = sd.ring;
+        cache = sd.cache;
+    } else {
+        pos = a.pos0 + row;
+        cap = a.cap0;
+        ring = a.ring0;
+        cache = a.cache0;
+    }
     const int half = a.D >> 1;
     // the row's rotation angles once for the workgroup's four heads (fp64,
     // rounded to fp32), not once per head
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
     }
     __syncthreads();
     if (task >= nq + 2 * a.Hkv) return;
-    const int slot = sd.ring ? pos % sd.cap : pos;
+    const int slot = ring ? pos % cap : pos;
     const bool act = lane < half;
     const int layer = a.layer[li];
     int kind, head, col;   // kind 0 q, 1 k, 2 v
@@ -235,9 +247,9 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
         st_any(a.q_out, o + lane, x1, a.q_bf16);
         st_any(a.q_out, o + lane + half, x2, a.q_bf16);
     } else {
-        const size_t o = ((((size_t)layer * 2 + (kind - 1)) * a.Hkv + head) * sd.cap + slot) * a.D;
-        st_any(sd.cache, o + lane, x1, a.cache_bf16);
-        st_any(sd.cache, o + lane + half, x2, a.cache_bf16);
+        const size_t o = ((((size_t)layer * 2 + (kind - 1)) * a.Hkv + head) * cap + slot) * a.D;
+        st_any(cache, o + lane, x1, a.cache_bf16);
+        st_any(cache, o + lane + half, x2, a.cache_bf16);
     }
 }
 

@@ -110,6 +110,11 @@ struct HeadArgs {
     int32_t nsplit, pad;
     int64_t src_stride;
     float eps;
+    // rows == nullptr: one run of rows, row r at position pos0 + r of the
+    // session whose cache, slot count and ring mode follow (no tables)
+    int32_t pos0;
+    void* cache0;
+    int32_t cap0, ring0;
     double inv_freq[64];      // theta^(-2d/D), d < D/2, computed on the host in fp64
 };
 
