@@ -60,6 +60,13 @@ struct dflash_session {
     bool outstanding;
     int64_t rows_written;
     int32_t hist_count, hist_head;
+    // history tokens of flushing commits reach the device ring only when it is
+    // next read or written (a sample, a verification, a one-step commit): the
+    // host keeps a copy of the ring, and the hist_dirty slots ending at
+    // hist_head are the ones not yet written (a long prompt's flushes would
+    // otherwise each pay a launch for tokens later ones overwrite)
+    std::vector<int32_t> hist_shadow;
+    int32_t hist_dirty = 0;
     ArenaLayout lay;
 
     SessView view() const {
@@ -316,24 +323,34 @@ static int write_context(dflash_session* s, const char* extra, int32_t extra_row
     return 0;
 }
 
-static int append_history(dflash_session* s, const int32_t* tokens, int32_t count) {
-    if (count <= 0) return 0;
+static void append_history(dflash_session* s, const int32_t* tokens, int32_t count) {
+    if (count <= 0) return;
     if (count > kHistory) {
         tokens += count - kHistory;
         s->hist_count += count - kHistory;
         count = kHistory;
     }
-    SessView v = s->view();
+    if (s->hist_shadow.empty()) s->hist_shadow.assign(kHistory, 0);
+    for (int32_t i = 0; i < count; ++i) s->hist_shadow[(s->hist_head + i) % kHistory] = tokens[i];
+    s->hist_head = (s->hist_head + count) % kHistory;
+    s->hist_count += count;
+    s->hist_dirty = std::min<int32_t>(kHistory, s->hist_dirty + count);
+}
+
+// writes the history slots not yet on the device (at most two ring runs)
+static int settle_history(dflash_session* s) {
+    if (s->hist_dirty == 0) return 0;
+    const SessView v = s->view();
+    const int32_t n = s->hist_dirty;
     int32_t done = 0;
-    while (done < count) {
-        int32_t slot = (s->hist_head + done) % kHistory;
-        int32_t run = std::min(count - done, kHistory - slot);
-        int rc = s->ctx->engine->write_history(v, slot, tokens + done, run, s->stream);
+    while (done < n) {
+        const int32_t slot = (s->hist_head - n + done + kHistory) % kHistory;
+        const int32_t run = std::min(n - done, kHistory - slot);
+        int rc = s->ctx->engine->write_history(v, slot, s->hist_shadow.data() + slot, run, s->stream);
         if (rc) return rc;
         done += run;
     }
-    s->hist_head = (s->hist_head + count) % kHistory;
-    s->hist_count += count;
+    s->hist_dirty = 0;
     return 0;
 }
 
@@ -357,6 +374,7 @@ extern "C" int dflash_committed(dflash_session* s, const int32_t* tokens_host, c
     const char* src = (const char*)features_dev + (size_t)start * s->row_bytes();
     if (s->pending + fresh < c.flush_rows && s->hist_head + fresh <= kHistory) {
         // the usual round: the history tokens and the rows in one step
+        if (int rc = settle_history(s)) return rc;
         int rc = s->ctx->engine->commit_rows(s->view(), s->hist_head, tokens_host + start, fresh,
                                              s->pending_buf() + (size_t)s->pending * s->row_bytes(), src,
                                              (size_t)fresh * s->row_bytes(), s->stream);
@@ -366,15 +384,18 @@ extern "C" int dflash_committed(dflash_session* s, const int32_t* tokens_host, c
         s->pending += fresh;
         return 0;
     }
-    int rc = append_history(s, tokens_host + start, fresh);
-    if (rc) return rc;
     if (s->pending + fresh < c.flush_rows) {
-        rc = s->ctx->engine->copy_rows(s->pending_buf() + (size_t)s->pending * s->row_bytes(), src,
+        // no flush (the history wraps the ring): both go out now
+        if (int rc = settle_history(s)) return rc;
+        append_history(s, tokens_host + start, fresh);
+        if (int rc = settle_history(s)) return rc;
+        int rc = s->ctx->engine->copy_rows(s->pending_buf() + (size_t)s->pending * s->row_bytes(), src,
                                        (size_t)fresh * s->row_bytes(), s->stream);
         if (rc) return rc;
         s->pending += fresh;
         return 0;
     }
+    append_history(s, tokens_host + start, fresh);
     commit_block(s);
     return write_context(s, src, fresh);
 }
@@ -417,6 +438,7 @@ extern "C" int dflash_committed_batch(dflash_session* const* ss, int32_t count, 
     for (int32_t k = 0; k < count; ++k) {
         dflash_session* s = ss[k];
         if (!fresh[k] || s->pending + fresh[k] >= c.flush_rows || fresh[k] > kHistory) continue;
+        if (int rc = settle_history(s)) return rc;
         const size_t rb = s->row_bytes();
         items.push_back({s->view().hist, s->hist_head, tokens_host + token_offsets[k] + start[k], fresh[k],
                          s->pending_buf() + (size_t)s->pending * rb,
@@ -612,6 +634,8 @@ extern "C" int dflash_sample(dflash_session* const* sessions, int32_t count, con
         views[k] = s->view();
     }
     if (row_offsets[count] == 0) return 0;
+    for (int32_t k = 0; k < count; ++k)
+        if (int rc = settle_history(sessions[k])) return rc;
     return s0->ctx->engine->sample(views, row_offsets, logits, *params, ids_out, probs_out, s0->ws,
                                    s0->ws_sessions, s0->stream);
 }

@@ -184,7 +184,8 @@ int dflash_session_close(dflash_session* s);
  * [T, taps*Ht] array of the config dtype.  start = ctxOffset + pending -
  * position; start < 0 is E_CONTEXT_GAP (nothing changes); rows [start, T)
  * join the pending rows and their tokens the history; reaching flush_rows
- * pending rows flushes.  Rows that stay pending are copied into the pending
+ * pending rows flushes (the history tokens of a flushing run are written to
+ * the device ring when a sample or a one-step commit next uses it).  Rows that stay pending are copied into the pending
  * buffer; a flushed chunk made only of this run's rows (16-byte aligned) is
  * projected where it lies by the forward this call enqueues.  Either way the
  * caller may free its buffer on return, in stream order.  Errors: E_ARG,

@@ -231,9 +231,9 @@ def test_history_ring_and_sample_plan(host):
     s = HostSession(host, ctx)
     _trace(host)
     s.committed(np.arange(600), None, 0)
-    hist = [l for l in _trace(host) if l.startswith("hist")]
-    toks = [int(x) for l in hist for x in l.split("tokens=")[1].split(",")]
-    assert toks == list(range(88, 600))             # only the last 512 are kept
+    # a flushing commit keeps its history tokens on the host until the ring
+    # is next read (the sample) or written (a one-step commit)
+    assert [l for l in _trace(host) if l.startswith("hist")] == []
     n = s.propose(3, 7)
     logits = np.zeros(16, dtype=np.float32)
     ids = np.zeros(16, dtype=np.int32)
@@ -241,8 +241,28 @@ def test_history_ring_and_sample_plan(host):
     hs = (c_void_p * 1)(s.h)
     p = abi.SampleParams(0.7, 1.1, 512, 4)
     abi.check(host, host.dflash_sample(hs, 1, offs, logits.ctypes.data, byref(p), ids.ctypes.data, None))
-    tr = [l for l in _trace(host) if l.startswith("sample")]
-    assert tr == ["sample rows=7 round=4 hist=600@0"]        # ring of 512 written from slot 0
+    tr = [l for l in _trace(host) if l.startswith(("hist", "sample"))]
+    toks = [int(x) for l in tr[:-1] for x in l.split("tokens=")[1].split(",")]
+    assert toks == list(range(88, 600))             # only the last 512 are kept, written before the sample
+    assert tr[0].startswith("hist slot=0 ")
+    assert tr[-1] == "sample rows=7 round=4 hist=600@0"      # ring of 512 written from slot 0
+    abi.check(host, host.dflash_sample(hs, 1, offs, logits.ctypes.data, byref(p), ids.ctypes.data, None))
+    assert [l for l in _trace(host) if l.startswith("hist")] == []   # written once
+
+
+def test_deferred_history_is_written_before_a_one_step_commit(host):
+    """A one-step commit writes its tokens to the device ring directly, so the
+    history a flushing commit left on the host goes out first (a later write
+    of the older tokens would overwrite the newer ones)."""
+    fm = FakeModel(host, flush_rows=16)
+    rc, ctx = fm.create()
+    s = HostSession(host, ctx)
+    _trace(host)
+    s.committed(np.arange(20), None, 0)              # flushes: 20 tokens kept on the host
+    s.committed(np.arange(20, 23), None, 20)         # one step: the 20 first, then these 3
+    tr = [l for l in _trace(host) if l.startswith(("hist", "copy"))]
+    assert tr == ["hist slot=0 tokens=" + ",".join(str(i) for i in range(20)), "hist slot=20 tokens=20,21,22",
+                  "copy rows=3"]
 
 
 @pytest.mark.parametrize("field,value", [("block_size", 1), ("block_size", 513), ("window", 1),
