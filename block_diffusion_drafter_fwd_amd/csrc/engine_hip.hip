@@ -788,15 +788,19 @@ int HipEngine::sample(const std::vector<SessView>& sess, const int32_t* row_offs
         any_hist |= descs[k].hist_n > 0;
         for (int32_t r = row_offsets[k]; r < row_offsets[k + 1]; ++r) info.push_back({k, r - row_offsets[k]});
     }
-    Tables tb;
-    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
-    const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
-    char* tab = base + w.tables;
-    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
     SampleArgs a{};
+    if (count == 1) {
+        a.seq0 = descs[0];    // rows and seqs stay null: no table upload
+    } else {
+        Tables tb;
+        const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+        const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+        char* tab = base + w.tables;
+        HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+        a.seqs = (const SeqDesc*)(tab + o_desc);
+        a.rows = (const RowInfo*)(tab + o_info);
+    }
     a.logits = logits;
-    a.seqs = (const SeqDesc*)(tab + o_desc);
-    a.rows = (const RowInfo*)(tab + o_info);
     a.bitmap = (uint32_t*)(base + w.bitmap);
     a.stats = (float*)(base + w.stats);
     a.ids = ids;

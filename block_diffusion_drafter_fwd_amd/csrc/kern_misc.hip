@@ -443,8 +443,16 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
     }
 }
 
+// one session's call passes its descriptor in the arguments and no tables
+__device__ __forceinline__ RowInfo sample_row(const SampleArgs& a, int r) {
+    return a.rows ? a.rows[r] : RowInfo{0, r};
+}
+__device__ __forceinline__ SeqDesc sample_seq(const SampleArgs& a, int k) {
+    return a.rows ? a.seqs[k] : a.seq0;
+}
+
 __global__ __launch_bounds__(256) void k_hist_bitmap(SampleArgs a) {
-    const SeqDesc sd = a.seqs[blockIdx.x];
+    const SeqDesc sd = sample_seq(a, blockIdx.x);
     uint32_t* bm = a.bitmap + (size_t)blockIdx.x * a.words;
     for (int i = threadIdx.x; i < a.words; i += 256) bm[i] = 0u;
     __syncthreads();
@@ -513,8 +521,8 @@ __device__ __forceinline__ float gumbel(float u) {
 // call whose four words carry the eight draws (two 23-bit fields a word).
 __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int c = blockIdx.x, r = blockIdx.y;
-    const RowInfo ri = a.rows[r];
-    const SeqDesc sd = a.seqs[ri.seq];
+    const RowInfo ri = sample_row(a, r);
+    const SeqDesc sd = sample_seq(a, ri.seq);
     const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
@@ -614,7 +622,7 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     if (!a.probs || a.temperature == 0.f) return;
     __syncthreads();
     const float M = tot[0], Z = tot[1];
-    const RowInfo ri = a.rows[r];
+    const RowInfo ri = sample_row(a, r);
     const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     const float inv_t = 1.f / a.temperature, inv_z = 1.f / Z;

@@ -159,6 +159,7 @@ struct SampleArgs {
     float* probs;
     int32_t V, R, nseq, words, chunk, nchunk, round, use_penalty;
     float temperature, rho;
+    SeqDesc seq0;             // rows == nullptr: one session, row r is its row r
 };
 
 // Speculative verification of drafted blocks: session k drafted
