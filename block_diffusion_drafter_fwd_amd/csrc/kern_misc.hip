@@ -443,16 +443,24 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
     }
 }
 
-// one session's call passes its descriptor in the arguments and no tables
+// ONE: a one-session call, whose descriptor rides in the arguments (no
+// tables; row r is the session's row r).  A compile-time switch: choosing
+// between the two sources at run time moved the descriptor (the Philox key)
+// into vector registers and cut the occupancy of the sampling kernel.
+template <bool ONE>
 __device__ __forceinline__ RowInfo sample_row(const SampleArgs& a, int r) {
-    return a.rows ? a.rows[r] : RowInfo{0, r};
+    if constexpr (ONE) return RowInfo{0, r};
+    else return a.rows[r];
 }
+template <bool ONE>
 __device__ __forceinline__ SeqDesc sample_seq(const SampleArgs& a, int k) {
-    return a.rows ? a.seqs[k] : a.seq0;
+    if constexpr (ONE) return a.seq0;
+    else return a.seqs[k];
 }
 
+template <bool ONE>
 __global__ __launch_bounds__(256) void k_hist_bitmap(SampleArgs a) {
-    const SeqDesc sd = sample_seq(a, blockIdx.x);
+    const SeqDesc sd = sample_seq<ONE>(a, blockIdx.x);
     uint32_t* bm = a.bitmap + (size_t)blockIdx.x * a.words;
     for (int i = threadIdx.x; i < a.words; i += 256) bm[i] = 0u;
     __syncthreads();
@@ -519,10 +527,11 @@ __device__ __forceinline__ float gumbel(float u) {
 // Gumbel-max candidate (or the argmax when greedy).  Eight consecutive tokens
 // per thread: two 16-byte logits loads, one history-bitmap word, one Philox
 // call whose four words carry the eight draws (two 23-bit fields a word).
+template <bool ONE>
 __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int c = blockIdx.x, r = blockIdx.y;
-    const RowInfo ri = sample_row(a, r);
-    const SeqDesc sd = sample_seq(a, ri.seq);
+    const RowInfo ri = sample_row<ONE>(a, r);
+    const SeqDesc sd = sample_seq<ONE>(a, ri.seq);
     const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
@@ -599,6 +608,7 @@ __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     }
 }
 
+template <bool ONE>
 __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     __shared__ float tot[4];
     const int c = blockIdx.x, r = blockIdx.y;
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     if (!a.probs || a.temperature == 0.f) return;
     __syncthreads();
     const float M = tot[0], Z = tot[1];
-    const RowInfo ri = sample_row(a, r);
+    const RowInfo ri = sample_row<ONE>(a, r);
     const uint32_t* bm = a.bitmap + (size_t)ri.seq * a.words;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     const float inv_t = 1.f / a.temperature, inv_z = 1.f / Z;
@@ -632,19 +642,25 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     }
 }
 
-hipError_t sample(const SampleArgs& a, hipStream_t st) {
-    if (a.R <= 0) return hipSuccess;
+template <bool ONE>
+static hipError_t sample_launch(const SampleArgs& a, hipStream_t st) {
     if (a.use_penalty) {
-        hipLaunchKernelGGL(k_hist_bitmap, dim3(a.nseq), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_hist_bitmap<ONE>, dim3(a.nseq), dim3(256), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_sample_stats, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_sample_stats<ONE>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool probs = a.probs && a.temperature != 0.f;
-    hipLaunchKernelGGL(k_sample_final, dim3(probs ? a.nchunk : 1, a.R), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_sample_final<ONE>, dim3(probs ? a.nchunk : 1, a.R), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+hipError_t sample(const SampleArgs& a, hipStream_t st) {
+    if (a.R <= 0) return hipSuccess;
+    if (!a.rows && a.nseq != 1) return hipErrorInvalidValue;   // no tables: exactly one session
+    return a.rows ? sample_launch<false>(a, st) : sample_launch<true>(a, st);
 }
 
 // ---------------------------------------------------------------------------
