@@ -744,6 +744,9 @@ int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_of
     const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
     const size_t o_offs = tb.add(draft_offsets, sizeof(int32_t) * (size_t)(count + 1));
     char* tab = base + w.tables;
+    // the stage timer brackets the whole call's GPU work, its table upload
+    // included (a bracket opened after the upload caught a varying share of it)
+    Timed tm(this, "verify", st);
     HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
     VerifyArgs a{};
     a.target = target;
@@ -763,7 +766,6 @@ int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_of
     a.nchunk = w.nchunk_max;
     a.round = p.round;
     a.temperature = p.temperature;
-    Timed tm(this, "verify", st);
     HIP_OK(kern::verify(a, st));
     return 0;
 }
