@@ -410,3 +410,39 @@ def test_flush_batch_matches_oracle(cuda, name):
             pr.check_state(f"flush_batch pass {r} session {k}")
             pr.check_cache(rep)
     say(f"[parity] flush_batch {name} worst {rep.worst}")
+
+
+def test_one_session_sample_equals_table_path_and_sees_deferred_history(cuda):
+    """A one-session sample call (its descriptor in the kernel arguments, no
+    tables) draws exactly what the same session draws inside a two-session
+    call (tables), and both see the prompt's history tokens, which a flushing
+    commit leaves on the host until the sample writes them to the ring: the
+    ids equal the oracle's draws with that history wherever the top-2 gap
+    exceeds the tie margin."""
+    from block_diffusion_drafter_fwd_amd import sample
+    from oracle.sampler import sample_row
+    cfg = synth.config("qwen", layers=1, vocab=3001)
+    w = synth.make_weights(cfg, seed=6, gains="random")
+    d = _drafter(cfg, w, max_sessions=2)
+    ss = [d.session(1024, seed=6, stream_id=k) for k in range(2)]
+    fs = synth.FeatureSource(cfg, 6, 0)
+    toks = (np.arange(300) * 7) % 50                 # history: ids 0..49, penalised
+    for s in ss:
+        s.committed(toks, feats_dev(cfg, fs.features(0, 300)), 0)   # 300 >= 256 rows: flushes
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    logits = torch.randn((30, cfg.vocab), generator=gen, device="cuda") * 2
+    logits[:, :50] += 3.0                            # the penalised ids would win without the penalty
+    rep = Report()
+    for rnd, (T, probs) in enumerate(((0.0, False), (0.7, True))):
+        ids1, p1 = sample([ss[0]], [0, 15], logits[:15], T, 1.3, 512, rnd, probs=probs)
+        ids2, p2 = sample(ss, [0, 15, 30], logits, T, 1.3, 512, rnd, probs=probs)
+        assert torch.equal(ids1.cpu(), ids2[:15].cpu())
+        if probs:
+            assert torch.equal(p1.cpu(), p2[:15].cpu())
+        z = logits.double().cpu().numpy()
+        ref = []
+        for i in range(15):
+            oid, _, sc = sample_row(z[i], list(toks), T, 1.3, 6, 0, rnd, i)
+            ref.append((oid, sc, id_margin(cfg, z[i], z[i], T, 1.3)))
+        check_ids(ids1.cpu().numpy(), ref, rep)
+    assert rep.ids_compared >= 25
