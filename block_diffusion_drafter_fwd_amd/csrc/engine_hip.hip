@@ -739,22 +739,27 @@ int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_of
         descs[k] = desc_of(sess[k]);
         for (int32_t i = 0; i <= draft_offsets[k + 1] - draft_offsets[k]; ++i) info.push_back({k, i});
     }
-    Tables tb;
-    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
-    const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
-    const size_t o_offs = tb.add(draft_offsets, sizeof(int32_t) * (size_t)(count + 1));
-    char* tab = base + w.tables;
     // the stage timer brackets the whole call's GPU work, its table upload
     // included (a bracket opened after the upload caught a varying share of it)
     Timed tm(this, "verify", st);
-    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
     VerifyArgs a{};
+    if (count == 1) {
+        a.seq0 = descs[0];    // rows, seqs and offs stay null: no table upload
+        a.n0 = draft_offsets[1];
+    } else {
+        Tables tb;
+        const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+        const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+        const size_t o_offs = tb.add(draft_offsets, sizeof(int32_t) * (size_t)(count + 1));
+        char* tab = base + w.tables;
+        HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+        a.seqs = (const SeqDesc*)(tab + o_desc);
+        a.rows = (const RowInfo*)(tab + o_info);
+        a.offs = (const int32_t*)(tab + o_offs);
+    }
     a.target = target;
     a.draft_ids = draft_ids;
     a.draft_probs = draft_probs;
-    a.seqs = (const SeqDesc*)(tab + o_desc);
-    a.rows = (const RowInfo*)(tab + o_info);
-    a.offs = (const int32_t*)(tab + o_offs);
     a.stats = (float*)(base + w.stats);
     a.stats2 = (float*)(base + w.stats2);
     a.accepted = accepted;

@@ -723,6 +723,25 @@ __device__ Stat row_stat(const float* stats, int nchunk, int r) {
     return s;
 }
 
+// ONE: a one-session call (descriptor and draft count in the arguments, no
+// tables), chosen at compile time as for the sampler
+template <bool ONE>
+__device__ __forceinline__ RowInfo verify_row(const VerifyArgs& a, int r) {
+    if constexpr (ONE) return RowInfo{0, r};
+    else return a.rows[r];
+}
+template <bool ONE>
+__device__ __forceinline__ int verify_off(const VerifyArgs& a, int k) {
+    if constexpr (ONE) return k == 0 ? 0 : a.n0;
+    else return a.offs[k];
+}
+template <bool ONE>
+__device__ __forceinline__ SeqDesc verify_seq(const VerifyArgs& a, int k) {
+    if constexpr (ONE) return a.seq0;
+    else return a.seqs[k];
+}
+
+template <bool ONE>
 __global__ __launch_bounds__(256) void k_verify_next(VerifyArgs a) {
     __shared__ float tot[2];
     const int c = blockIdx.x, r = blockIdx.y;
@@ -735,12 +754,12 @@ __global__ __launch_bounds__(256) void k_verify_next(VerifyArgs a) {
     }
     __syncthreads();
     const float M = tot[0], inv_z = 1.f / tot[1], inv_t = 1.f / a.temperature;
-    const RowInfo ri = a.rows[r];
-    const SeqDesc sd = a.seqs[ri.seq];
-    const int n = a.offs[ri.seq + 1] - a.offs[ri.seq];
+    const RowInfo ri = verify_row<ONE>(a, r);
+    const SeqDesc sd = verify_seq<ONE>(a, ri.seq);
+    const int n = verify_off<ONE>(a, ri.seq + 1) - verify_off<ONE>(a, ri.seq);
     const int i = ri.pos;                      // row within the block: i < n drafted, i == n bonus
     const float* z = a.target + (size_t)r * a.V;
-    const float* q = i < n ? a.draft_probs + (size_t)(a.offs[ri.seq] + i) * a.V : nullptr;
+    const float* q = i < n ? a.draft_probs + (size_t)(verify_off<ONE>(a, ri.seq) + i) * a.V : nullptr;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     for (int qd = (t_lo >> 2) + threadIdx.x; qd * 4 < t_hi; qd += 256) {
@@ -775,10 +794,11 @@ __global__ __launch_bounds__(256) void k_verify_next(VerifyArgs a) {
     }
 }
 
+template <bool ONE>
 __global__ __launch_bounds__(64) void k_verify_final(VerifyArgs a) {
     const int k = blockIdx.x;
-    const int off = a.offs[k], n = a.offs[k + 1] - off, r0 = off + k;
-    const SeqDesc sd = a.seqs[k];
+    const int off = verify_off<ONE>(a, k), n = verify_off<ONE>(a, k + 1) - off, r0 = off + k;
+    const SeqDesc sd = verify_seq<ONE>(a, k);
     int acc = 0;
     for (; acc < n; ++acc) {
         const Stat s = row_stat(a.stats, a.nchunk, r0 + acc);
@@ -802,18 +822,24 @@ __global__ __launch_bounds__(64) void k_verify_final(VerifyArgs a) {
     }
 }
 
-hipError_t verify(const VerifyArgs& a, hipStream_t st) {
-    if (a.nseq <= 0) return hipSuccess;
+template <bool ONE>
+static hipError_t verify_launch(const VerifyArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_verify_stats, dim3(a.nchunk, a.Rt), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.temperature > 0.f) {
-        hipLaunchKernelGGL(k_verify_next, dim3(a.nchunk, a.Rt), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_verify_next<ONE>, dim3(a.nchunk, a.Rt), dim3(256), 0, st, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_verify_final, dim3(a.nseq), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_verify_final<ONE>, dim3(a.nseq), dim3(64), 0, st, a);
     return hipGetLastError();
+}
+
+hipError_t verify(const VerifyArgs& a, hipStream_t st) {
+    if (a.nseq <= 0) return hipSuccess;
+    if (!a.rows && a.nseq != 1) return hipErrorInvalidValue;   // no tables: exactly one session
+    return a.rows ? verify_launch<false>(a, st) : verify_launch<true>(a, st);
 }
 
 }  // namespace kern

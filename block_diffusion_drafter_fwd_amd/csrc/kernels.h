@@ -178,6 +178,8 @@ struct VerifyArgs {
     int32_t* next;            // [nseq]
     int32_t V, Rt, nseq, chunk, nchunk, round;
     float temperature;
+    int32_t n0;               // rows == nullptr: one session with n0 drafts,
+    SeqDesc seq0;             // its descriptor (no tables)
 };
 
 struct UploadArgs {
