@@ -30,6 +30,9 @@ Pins: every function is checked in ``tests/test_oracle_*.py`` against
 something other than itself (transformers' Qwen3 attention and MLP, torch's
 ``rms_norm`` and ``scaled_dot_product_attention``, numpy's Philox, closed
 forms and invariants the pages state; verification against the
-rejection-sampling theorem it exists to satisfy).  The window/gate/aux-norm variant is
-pinned only by invariants (no library implements it); see the test headers.
+rejection-sampling theorem it exists to satisfy).  The Laguna variant (aux
+norms, context input norm, fused qkv, gate, window) is pinned against a
+forward assembled from transformers' Qwen3 modules plus those steps written in
+torch, with planted mistakes showing each pin discriminates; see the test
+headers.
 """

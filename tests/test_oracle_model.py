@@ -17,8 +17,8 @@
 3. Closed form: with o_proj = down_proj = 0 every layer is the identity, so the
    rows 1..n logits are lm_head @ RMSNorm(E[mask]) and row 0 is dropped.
 
-The window/gate/aux-norm arm has no library counterpart: it is pinned by the
-invariants in (2) only.
+The Laguna arm (aux norms, context input norm, gate, window) is pinned
+against an assembled torch forward in ``test_oracle_laguna.py``.
 """
 import numpy as np
 import pytest
