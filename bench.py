@@ -1,10 +1,12 @@
 """Throughput of the DFlash drafter forward on one MI355X.
 
-Workload (default, ``--config qwen``): the Qwen3.5-style bf16 drafter (hidden
-2048, 5 layers, 32 q / 8 kv heads x 128, fc 10240 -> 2048, vocab 151936,
-blockSize 16), seeded N(0, 0.02) weights with unit norm gains, N(0, 1) tap
-features, a 4096-slot context written by 256-row flushes, then drafting
-rounds at n = 15.
+Workload (default, ``--config long``): the long-context, flush-heavy bf16
+drafter (hidden 4096, 5 layers, 32 q / 8 kv heads x 128, fc 20480 -> 4096,
+vocab 262144, blockSize 8), seeded N(0, 0.02) weights with unit norm gains,
+N(0, 1) tap features, a 131072-slot prompt written by 256-row flushes, then
+drafting rounds at the fixed depth 7 with temperature-1 sampling that returns
+the full per-row probability vectors.  It is the largest configuration that
+fits one GPU.
 
 A step is one round of the whole hot path: rewind the outstanding block,
 commit the accepted run (anchor + a drafted rows, a ~ U{0..n}; its feature
@@ -12,23 +14,24 @@ rows ride in the next propose's context pass), propose (pending rows ->
 context K/V; anchor + n mask rows through every layer; rows 1..n
 unembedded) and sample the rows.  value = drafted blocks/s (for the batched
 workload one block per session per batched call).  The prompt phase is timed
-separately and reported as flushed context rows/s (at least 32768 rows: the
-4096-slot prompt is written into eight fresh sessions back to back).  All
-inputs (weights, feature rows, tokens, accept lengths) are resident on the
-device or host before the timed region, and Python's cyclic garbage
+separately and reported as flushed context rows/s (at least 32768 rows).
+All inputs (weights, feature rows, tokens, accept lengths) are resident on
+the device or host before the timed region, and Python's cyclic garbage
 collector is paused inside every timed region.
 
-Other workloads (``--config``): laguna (windowed, fused QKV, gate; 32768-slot
-prompt of which 511 stay), long (hidden 4096, vocab 262144, 131072-slot
-context, T = 1 with probabilities returned), batched (64 sessions with
-log-uniform 1k..16k contexts, U{1..15} rows each, T = 0.7, repetition
-penalty 1.1).  Their feature rows repeat with a period of 4096 slots (values
-do not change the work).
+Other workloads (``--config``): qwen (hidden 2048, vocab 151936, 4096-slot
+context, n = 15, greedy), laguna (windowed, fused QKV, gate; 32768-slot
+prompt of which 511 stay), batched (64 sessions with log-uniform 1k..16k
+contexts, U{1..15} rows each, T = 0.7, repetition penalty 1.1).  Feature rows
+of the long, laguna and batched prompts repeat with a period of 4096 slots
+(values do not change the work).  The default run also times the batched
+workload after the long one and reports it under ``kernels.batched``
+(``--no-secondary`` skips it).
 
-The JSON line carries the roofline of the dominant kernel, timed with HIP
-events on its stream inside the timed region, per-stage rooflines from the
-same hooks (``kernels``), and the CPU oracle's rate on a bounded sample of
-the same workload.
+The JSON line carries the roofline of the dominant kernel (the one with the
+most time per round), timed with HIP events on its stream inside the timed
+region, per-stage rooflines from the same hooks (``kernels``), and the CPU
+oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -46,8 +49,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
-PMC_FILE = os.path.join(ROOT, "profiles", "unembed_qwen_pmc.json")
+PROFILES = os.path.join(ROOT, "profiles")
 POOL_ROWS = 4096
+# the kernel timed live inside the timed region: the one with the most time
+# per round (the attention partials of five layers on the long workload, the
+# unembedding elsewhere)
+DOMINANT = {"long": "attention_partial", "qwen": "unembed", "laguna": "unembed", "tiny": "unembed"}
+KERNEL_NAMES = {"unembed": "k_gemm_skinny_p (lm_head)", "attention_partial": "k_attn_partial",
+                "attention": "k_attn_partial + k_attn_combine"}
 
 
 def gc_pause() -> None:
@@ -59,9 +68,20 @@ def gc_pause() -> None:
     gc.disable()
 
 
-def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "block_diffusion_drafter_fwd_amd", "csrc", "kern_gemm.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def pmc_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none or
+    the kernel's source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    pmc = json.load(open(path))
+    src = os.path.join(ROOT, pmc.get("source", ""))
+    if not os.path.isfile(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != pmc.get("kernel_source_sha256_16"):
+        return None
+    return pmc.get("hbm_bytes_per_launch")
 
 
 def parse():
@@ -69,11 +89,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed rounds (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="qwen", choices=["qwen", "laguna", "long", "batched", "tiny"])
+    ap.add_argument("--config", default="long", choices=["qwen", "laguna", "long", "batched", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="context rows of the oracle sample")
-    ap.add_argument("--cpu-rounds", type=int, default=8, help="propose + sample rounds of the oracle sample")
-    ap.add_argument("--stages", action="store_true", help="also time the attention, sampler and flush stages")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="context rows of the oracle sample")
+    ap.add_argument("--cpu-rounds", type=int, default=None, help="propose + sample rounds of the oracle sample")
+    ap.add_argument("--no-stages", action="store_true",
+                    help="time only the dominant kernel (skip the attention, sampler, verify and flush stages)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="default run: skip the batched workload timed after the long one")
     ap.add_argument("--no-width-sweep", action="store_true",
                     help="skip the propose-time-vs-n sweep and the truncated-block comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -135,31 +158,54 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    wl = synth.WORKLOADS[args.config]
+    out = run_workload(args, args.config, torch, synth, dev)
+    if args.config == "long" and not args.no_secondary:
+        # the batched workload (64 sessions, config 2's shape) as a secondary
+        # entry; the long run's device memory is released first
+        gc.collect()
+        torch.cuda.empty_cache()
+        sec = run_workload(args, "batched", torch, synth, dev, secondary=True)
+        out["kernels"]["batched"] = {k: sec[k] for k in ("value", "unit", "ms_per_step", "steps",
+                                                          "flushed_ctx_rows_per_s", "config", "kernels")}
+    print(json.dumps(out), flush=True)
+
+
+def run_workload(args, name, torch, synth, dev, secondary=False):
+    wl = synth.WORKLOADS[name]
     cfg = synth.config(wl.config)
-    steps = args.steps if args.steps is not None else min(wl.rounds, 200)
+    steps = args.steps if (args.steps is not None and not secondary) else min(wl.rounds, 200)
+    warmup = args.warmup if not secondary else 10
     bf16 = cfg.dtype == "bf16"
     dt = torch.bfloat16 if bf16 else torch.float32
+    want_cpu = not args.no_cpu_baseline and not secondary
     t0 = time.time()
     w_np = synth.make_weights(cfg, seed=0, gains="unit")
     w_dev = {}
     for k in list(w_np):
         w_dev[k] = torch.from_numpy(w_np[k]).to(dev).to(dt)
-        if args.no_cpu_baseline or args.config != "qwen":
+        if not want_cpu:
             del w_np[k]
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
     if wl.sessions > 1:
-        out = bench_batched(args, cfg, wl, w_dev, steps, torch, synth)
+        out = bench_batched(args, cfg, wl, w_dev, steps, warmup, torch, synth)
     else:
-        out = bench_single(args, cfg, wl, w_dev, steps, torch, synth)
-    if not args.no_cpu_baseline and args.config == "qwen":
-        out["cpu_baseline"] = cpu_baseline(cfg, wl, w_np, args.cpu_rows, args.cpu_rounds)
+        out = bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth)
+    del w_dev
+    if want_cpu:
+        rows, rounds = CPU_SAMPLE.get(name, (2048, 4))
+        out["cpu_baseline"] = cpu_baseline(cfg, wl, w_np, args.cpu_rows or rows, args.cpu_rounds or rounds)
     else:
         out.setdefault("cpu_baseline", None)
+    del w_np
     out["setup_s"] = round(gen_s, 1)
-    print(json.dumps(out), flush=True)
+    return out
+
+
+# bounded oracle samples (context rows flushed, propose + sample rounds),
+# each about 10-30 s of CPU work
+CPU_SAMPLE = {"long": (2048, 3), "qwen": (4096, 4), "laguna": (2048, 6), "batched": (2048, 4), "tiny": (48, 20)}
 
 
 class FeaturePool:
@@ -179,7 +225,7 @@ class FeaturePool:
         return self.toks[o:o + T], self.feats[o:o + T]
 
 
-def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
+def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
     import numpy as np
 
     from block_diffusion_drafter_fwd_amd import Drafter, sample
@@ -189,14 +235,14 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
     d = Drafter(cfg, w_dev)
     st = Stage(d.lib, d.ctx)
     B = cfg.block_size
-    n_rounds = args.warmup + steps
-    extra = 20                                   # rounds run after the timed ones (stage passes)
+    n_rounds = warmup + steps
+    extra = 64                                   # rounds run after the timed ones (stage passes)
     capacity = wl.context + (n_rounds + extra) * B + 64
     if cfg.window:
         capacity = cfg.window + B - 1
     rs = synth.RoundScript(cfg, wl, 0, 0)
     total_rows = wl.context + (n_rounds + extra) * B
-    pool = FeaturePool(cfg, total_rows, dev, dt, torch, synth, full=args.config == "qwen")
+    pool = FeaturePool(cfg, total_rows, dev, dt, torch, synth, full=wl.name == "qwen")
     n = min(rs.max_tokens, B - 1)
     plan = [(rs.accept(n), rs.bonus()) for _ in range(n_rounds + extra)]
     current0 = rs.first_anchor()
@@ -220,8 +266,6 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
     passes = max(1, -(-32768 // wl.context))
     fresh = [d.session(capacity) for _ in range(passes)]
     torch.cuda.synchronize()
-    if args.stages:
-        st.begin("flush_fc")
     gc_pause()
     t = time.perf_counter()
     for f in fresh:
@@ -229,7 +273,6 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
     torch.cuda.synchronize()
     flush_s = time.perf_counter() - t
     gc.enable()
-    fc_stage = st.end() if args.stages else None
     flush_rows_per_s = passes * wl.context / flush_s
     s = fresh[-1]
     for f in fresh[:-1]:
@@ -254,10 +297,11 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
         state["current"] = bonus
         state["r"] = r + 1
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     F_seen.clear()
-    st.begin("unembed")
+    dom = DOMINANT[wl.name] if cfg.dtype == "bf16" else "unembed"
+    st.begin(dom)
     torch.cuda.synchronize()
     gc_pause()
     t = time.perf_counter()
@@ -266,39 +310,44 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t
     gc.enable()
-    ms, launches = st.end()
+    dom_ms, dom_launches = st.end()
     blocks_per_s = steps / elapsed
 
     elem = 2 if cfg.dtype == "bf16" else 4
-    alg_bytes = cfg.vocab * cfg.hidden * elem + n * cfg.hidden * elem + n * cfg.vocab * 4
-    avg_s = ms / 1e3 / max(1, launches)
-    traffic = None
-    if os.path.exists(PMC_FILE) and args.config == "qwen":
-        pmc = json.load(open(PMC_FILE))
-        if pmc.get("kernel_source_sha256_16") == kernel_source_hash():
-            traffic = pmc.get("hbm_bytes_per_launch")
-    roofline = hbm_line(alg_bytes, avg_s, traffic=traffic, kernel="k_gemm_skinny_p<4,1> (lm_head)",
-                        alg_bytes_per_launch=alg_bytes, avg_launch_us=round(avg_s * 1e6, 2), launches=launches)
-    kernels = {"unembed": roofline}
+    # attention: one launch (pair) per layer; its KV bytes over the visible keys
+    F_mean = float(np.mean(F_seen)) if F_seen else float(wl.context)
+    vis = min(F_mean, cfg.window - 1) + n + 1 if cfg.window else F_mean + n + 1
+    kv_bytes = int(2 * cfg.kv_heads * vis * cfg.head_dim * elem)
+    unembed_bytes = cfg.vocab * cfg.hidden * elem + n * cfg.hidden * elem + n * cfg.vocab * 4
+    alg = {"unembed": unembed_bytes, "attention": kv_bytes, "attention_partial": kv_bytes}
 
-    if args.stages:
-        # attention: one launch pair per layer; its KV bytes over the visible keys
-        F_mean = float(np.mean(F_seen)) if F_seen else float(wl.context)
-        vis = min(F_mean, cfg.window - 1) + n + 1 if cfg.window else F_mean + n + 1
-        kv_bytes = 2 * cfg.kv_heads * vis * cfg.head_dim * elem
-        for name in ("attention", "sampler"):
+    def line(stage, ms_, launches_, rounds_):
+        avg = ms_ / 1e3 / max(1, launches_)
+        return hbm_line(alg[stage], avg, traffic=pmc_traffic(stage, wl.name), kernel=KERNEL_NAMES[stage],
+                        alg_bytes_per_launch=alg[stage], avg_launch_us=round(avg * 1e6, 2), launches=launches_,
+                        us_per_round=round(ms_ * 1e3 / rounds_, 1))
+
+    roofline = line(dom, dom_ms, dom_launches, steps)
+    kernels = {dom: roofline}
+    stage_rounds = 16
+    if not args.no_stages:
+        for name in ("unembed", "attention_partial", "attention", "sampler"):
+            if name in kernels or (name == "attention_partial" and cfg.dtype != "bf16"):
+                continue
             st.begin(name)
-            for _ in range(8):
+            for _ in range(stage_rounds):
                 step()
             ms_s, l_s = st.end()
             avg = ms_s / 1e3 / max(1, l_s)
-            if name == "attention":
-                kernels[name] = hbm_line(kv_bytes, avg, alg_bytes_per_launch=int(kv_bytes),
-                                         avg_launch_us=round(avg * 1e6, 2), launches=l_s)
-            else:
+            if name == "sampler":
                 sb = n * cfg.vocab * 4 * (2 if wl.probs and wl.temperature > 0 else 1)
                 kernels[name] = hbm_line(sb, avg, alg_bytes_per_launch=sb, avg_launch_us=round(avg * 1e6, 2),
                                          launches=l_s)
+            else:
+                kernels[name] = line(name, ms_s, l_s, stage_rounds)
+        per_round = {k: v.get("us_per_round", 0) for k, v in kernels.items() if k in ("unembed", "attention_partial")}
+        if per_round:
+            roofline["dominant_by_time_per_round"] = max(per_round, key=per_round.get)
         # verification of one block against synthetic target logits (n drafts,
         # n + 1 target rows; with the draft probabilities when sampling)
         from block_diffusion_drafter_fwd_amd import verify
@@ -318,22 +367,22 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
             vb = (n + 1) * cfg.vocab * 4 + (n * cfg.vocab * 4 if T > 0 else 0)
             kernels["verify"] = hbm_line(vb, avg, alg_bytes_per_launch=vb, avg_launch_us=round(avg * 1e6, 2),
                                          launches=l_v)
-        if fc_stage and fc_stage[1]:
-            avg = fc_stage[0] / 1e3 / fc_stage[1]
-            rows = wl.commit_rows
-            kernels["flush_fc"] = mfma_line(2.0 * rows * cfg.fc_in * cfg.hidden, avg, rows=rows,
-                                            avg_launch_us=round(avg * 1e6, 2), launches=fc_stage[1])
-        s2 = d.session(capacity)
-        st.begin("flush_kv")
-        prompt(s2)
-        torch.cuda.synchronize()
-        ms_k, l_k = st.end()
-        s2.close()
-        if l_k:
-            avg = ms_k / 1e3 / l_k
-            kvn = cfg.layers * 2 * cfg.kv_heads * cfg.head_dim
-            kernels["flush_kv"] = mfma_line(2.0 * wl.commit_rows * cfg.hidden * kvn, avg, rows=wl.commit_rows,
-                                            avg_launch_us=round(avg * 1e6, 2), launches=l_k)
+        # the context-path GEMMs over one more prompt each (fresh sessions)
+        rows = wl.commit_rows
+        flops = {"flush_fc": 2.0 * rows * cfg.fc_in * cfg.hidden,
+                 "flush_kv": 2.0 * rows * cfg.hidden * cfg.layers * 2 * cfg.kv_heads * cfg.head_dim}
+        for name in ("flush_fc", "flush_kv"):
+            s2 = d.session(capacity)
+            torch.cuda.synchronize()
+            st.begin(name)
+            prompt(s2)
+            torch.cuda.synchronize()
+            ms_k, l_k = st.end()
+            s2.close()
+            if l_k:
+                avg = ms_k / 1e3 / l_k
+                kernels[name] = mfma_line(flops[name], avg, rows=rows, avg_launch_us=round(avg * 1e6, 2),
+                                          launches=l_k, target_frac=0.5)
 
     sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
 
@@ -343,7 +392,7 @@ def bench_single(args, cfg, wl, w_dev, steps, torch, synth):
         "unit": "blocks/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -409,7 +458,7 @@ def width_sweep(s, cfg, current, logits, torch, np, reps=20):
             "truncation": trunc}
 
 
-def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
+def bench_batched(args, cfg, wl, w_dev, steps, warmup, torch, synth):
     """64 sessions, one batched propose + one batched sample per round."""
     import numpy as np
 
@@ -420,12 +469,12 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
     S = wl.sessions
     B = cfg.block_size
     lens = synth.session_lengths(wl, 0)
-    n_rounds = args.warmup + steps
+    n_rounds = warmup + steps
     d = Drafter(cfg, w_dev, max_sessions=S)
     st = Stage(d.lib, d.ctx)
     pool = FeaturePool(cfg, POOL_ROWS, dev, dt, torch, synth, full=False)
     scripts = [synth.RoundScript(cfg, wl, 0, k) for k in range(S)]
-    caps = [L + (n_rounds + 12) * B + 64 for L in lens]
+    caps = [L + (n_rounds + 16) * B + 64 for L in lens]
     logits = torch.empty((S * (B - 1), cfg.vocab), dtype=torch.float32, device=dev)
 
     def prompt(sessions):
@@ -474,10 +523,10 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
         committed_batch(sess, runs, fts, poss)
         state["r"] = r + 1
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     state["rows"].clear()
-    st.begin("attention")
+    st.begin("attention_partial")
     torch.cuda.synchronize()
     gc_pause()
     t = time.perf_counter()
@@ -493,10 +542,11 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
     ctx_now = [sess[k].state()[0] for k in range(S)]
     kv_bytes_layer = sum(2 * cfg.kv_heads * (c + B) * cfg.head_dim * elem for c in ctx_now)
     avg_a = ms_a / 1e3 / max(1, l_a)
-    attn = hbm_line(kv_bytes_layer, avg_a, kernel="k_attn_partial + k_attn_combine (all sessions, one layer)",
-                    alg_bytes_per_launch=int(kv_bytes_layer), avg_launch_us=round(avg_a * 1e6, 2), launches=l_a)
-    kernels = {"attention": attn}
-    for name in ("unembed", "sampler"):
+    attn = hbm_line(kv_bytes_layer, avg_a, traffic=pmc_traffic("attention_partial", wl.name),
+                    kernel="k_attn_partial (all sessions, one layer)", alg_bytes_per_launch=int(kv_bytes_layer),
+                    avg_launch_us=round(avg_a * 1e6, 2), launches=l_a, us_per_round=round(ms_a * 1e3 / steps, 1))
+    kernels = {"attention_partial": attn}
+    for name in ("attention", "unembed", "sampler"):
         st.begin(name)
         for _ in range(4):
             step()
@@ -504,7 +554,11 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
         avg = ms_s / 1e3 / max(1, l_s)
         if name == "unembed":
             kernels[name] = mfma_line(2.0 * R * cfg.hidden * cfg.vocab, avg, rows=round(R, 1),
-                                      avg_launch_us=round(avg * 1e6, 2), launches=l_s)
+                                      avg_launch_us=round(avg * 1e6, 2), launches=l_s, target_frac=0.5)
+        elif name == "attention":
+            kernels[name] = hbm_line(kv_bytes_layer, avg, kernel="k_attn_partial + k_attn_combine",
+                                     alg_bytes_per_launch=int(kv_bytes_layer), avg_launch_us=round(avg * 1e6, 2),
+                                     launches=l_s)
         else:
             sb = R * cfg.vocab * 4
             kernels[name] = hbm_line(sb, avg, alg_bytes_per_launch=int(sb), avg_launch_us=round(avg * 1e6, 2),
@@ -517,7 +571,7 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
         "unit": "blocks/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -535,10 +589,23 @@ def bench_batched(args, cfg, wl, w_dev, steps, torch, synth):
     }
 
 
-def cpu_baseline(cfg, wl, w_np, rows, rounds=8):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, wl, w_np, rows, rounds):
     """The float64 oracle on a bounded sample of the same workload: `rows`
     context rows flushed in 256-row chunks, then `rounds` rounds of propose +
-    sample over that context.  Reported per unit (blocks/s)."""
+    sample over that context at the workload's width, temperature and
+    penalty.  Reported per unit (blocks/s; flushed rows/s).  Its flush rate
+    does not depend on the context length (rows are independent); its round
+    rate over a context shorter than the workload's is an upper bound."""
     import numpy as np
 
     import synth
@@ -552,15 +619,17 @@ def cpu_baseline(cfg, wl, w_np, rows, rounds=8):
         cores = len(os.sched_getaffinity(0))
     fs = synth.FeatureSource(cfg, 0, 0)
     o = OracleSession(DraftModel(cfg, w_np))
+    n = cfg.block_size - 1 if wl.max_tokens <= 0 else min(wl.max_tokens, cfg.block_size - 1)
     t = time.perf_counter()
-    for p in range(0, rows, 256):
-        o.committed(fs.tokens(p, 256), fs.features(p, 256), p)
+    for p in range(0, rows, wl.commit_rows):
+        T = min(wl.commit_rows, rows - p)
+        o.committed(fs.tokens(p, T), fs.features(p, T), p)
     o.flush()
     t_flush = time.perf_counter() - t
     t = time.perf_counter()
     cur = 5
     for r in range(rounds):
-        out = o.propose(cur, cfg.block_size - 1)
+        out = o.propose(cur, n)
         for i in range(out["n"]):
             sample_row(out["logits"][i], o.history[-wl.history:], wl.temperature, wl.rep_penalty, 0, 0, r, i)
         o.commit_block()
@@ -569,10 +638,12 @@ def cpu_baseline(cfg, wl, w_np, rows, rounds=8):
         cur = 7
     t_rounds = time.perf_counter() - t
     return {"value": round(rounds / t_rounds, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
-            "flushed_ctx_rows_per_s": round(rows / t_flush, 2),
-            "sample": f"float64 NumPy oracle on the same config: {rows} context rows flushed in 256-row chunks "
-                      f"({t_flush:.1f} s), then {rounds} rounds of propose + sample over a {rows}-slot context "
-                      f"({t_rounds:.1f} s)"}
+            "cpu_model": cpu_model(), "flushed_ctx_rows_per_s": round(rows / t_flush, 2),
+            "sample": f"float64 NumPy oracle (BLAS threads = cores) on the same configuration: {rows} context "
+                      f"rows flushed in {wl.commit_rows}-row chunks ({t_flush:.1f} s), then {rounds} rounds of "
+                      f"propose (n={n}) + sample (T={wl.temperature}, penalty {wl.rep_penalty}) over a "
+                      f"{rows}-slot context ({t_rounds:.1f} s); the workload's context is {wl.context or 'per session'}"
+                      f" slots, so the round rate is an upper bound of the oracle's there"}
 
 
 if __name__ == "__main__":

@@ -55,7 +55,7 @@ def build_hip(verbose: bool = False) -> str:
                 print(out)
     objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + HOST_SOURCES]
     lib = os.path.join(HERE, "libdflash.so")
-    tmp = lib + ".tmp"
+    tmp = lib + f".tmp{os.getpid()}"
     # -z defs: an unresolved symbol (say, a kernel stub the host pass failed to
     # emit) fails the build instead of the first dlopen
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,-z,defs", *objs, "-o", tmp])
@@ -66,7 +66,7 @@ def build_hip(verbose: bool = False) -> str:
 def build_host(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     lib = os.path.join(HERE, "libdflash_host.so")
-    tmp = lib + ".tmp"
+    tmp = lib + f".tmp{os.getpid()}"
     out = _run(["g++", *CXX_FLAGS, "-shared", os.path.join(CSRC, "api.cpp"),
                 os.path.join(CSRC, "engine_trace.cpp"), "-o", tmp])
     if verbose and out.strip():

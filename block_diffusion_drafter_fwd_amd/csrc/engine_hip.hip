@@ -662,7 +662,15 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             a.out_bf16 = bf16();
             a.scale = 1.f / sqrtf((float)c.head_dim);
             Timed tm(this, "attention", st);
-            HIP_OK(attention(a, bf16(), st));
+            if (bf16() && stage_ == "attention_partial") {
+                {
+                    Timed tp(this, "attention_partial", st);
+                    HIP_OK(attention(a, true, st, 1));
+                }
+                HIP_OK(attention(a, true, st, 2));
+            } else {
+                HIP_OK(attention(a, bf16(), st));
+            }
         }
         int o_slices = 1;
         {

@@ -426,15 +426,18 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     ((float*)a.out)[(size_t)brow * a.Hq * D + (size_t)hq * D + t] = out;
 }
 
-hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st) {
+hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st, int part) {
     if (a.nrows <= 0) return hipSuccess;
     if (!bf16) {
+        if (part == 2) return hipSuccess;
         hipLaunchKernelGGL(k_attn_f32, dim3(a.nrows, a.Hq), dim3(64), 0, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items * a.Hkv), dim3(kAttnThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (part != 2) {
+        hipLaunchKernelGGL(k_attn_partial, dim3(a.total_items * a.Hkv), dim3(kAttnThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || part == 1) return e;
+    }
     hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, (a.Hq + kCombHeads - 1) / kCombHeads), dim3(32 * kCombHeads),
                        0, st, a);
     return hipGetLastError();

@@ -226,7 +226,8 @@ hipError_t rmsnorm(const NormArgs& a, hipStream_t st);
 hipError_t commit_batch(const CommitBatchArgs& a, hipStream_t st);
 hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st);
 hipError_t embed(const EmbedArgs& a, hipStream_t st);
-hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st);
+// part: 0 both launches, 1 the partials only, 2 the combine only (bf16 path)
+hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st, int part = 0);
 hipError_t sample(const SampleArgs& a, hipStream_t st);
 hipError_t verify(const VerifyArgs& a, hipStream_t st);
 hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st);

@@ -100,6 +100,7 @@ def traffic(fetch: str, write: str, kernel: str, source: str = None, copy_kernel
          "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
          "hbm_bytes_per_launch": int(round(fk * 1024 * f_scale + wk * 1024 * w_scale))}
     if source:
+        d["source"] = source
         d["kernel_source_sha256_16"] = hashlib.sha256(open(source, "rb").read()).hexdigest()[:16]
     return d
 
