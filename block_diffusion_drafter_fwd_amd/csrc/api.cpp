@@ -61,10 +61,10 @@ struct dflash_session {
     int64_t rows_written;
     int32_t hist_count, hist_head;
     // history tokens of flushing commits reach the device ring only when it is
-    // next read or written (a sample, a verification, a one-step commit): the
-    // host keeps a copy of the ring, and the hist_dirty slots ending at
-    // hist_head are the ones not yet written (a long prompt's flushes would
-    // otherwise each pay a launch for tokens later ones overwrite)
+    // next read or written (a sample or a one-step commit): the host keeps a
+    // full copy of the ring, and the hist_dirty slots ending at hist_head are
+    // the ones not yet written (a long prompt's flushes would otherwise each
+    // pay a launch for tokens later ones overwrite)
     std::vector<int32_t> hist_shadow;
     int32_t hist_dirty = 0;
     ArenaLayout lay;
@@ -255,6 +255,7 @@ extern "C" int dflash_session_open(dflash_ctx* ctx, void* arena, size_t arena_by
     s->stream_id = stream_id;
     s->ctx_offset = s->cache_len = restored_offset;
     s->lay = lay;
+    s->hist_shadow.assign(kHistory, 0);
     *out = s;
     return 0;
 }
@@ -262,6 +263,63 @@ extern "C" int dflash_session_open(dflash_ctx* ctx, void* arena, size_t arena_by
 // ---------------------------------------------------------------------------
 // state machine
 // ---------------------------------------------------------------------------
+
+// Host-side state of the sessions a call changes, saved on entry: a failure
+// after the first change (an enqueue that the HIP runtime refuses) puts every
+// session back, so host state never runs ahead of what was enqueued.  The
+// failed call may have written some slots of the device history ring, so
+// the whole ring window is written again from the host copy at its next use.
+// Cache rows it may have written lie at or past the restored frontier
+// (outstanding block and pending rows), which nothing reads before they are
+// written again -- except in a windowed ring, whose partial writes can land
+// on visible slots; after DFLASH_E_HIP the session should be closed.
+class StateGuard {
+public:
+    // history: the call may change the token history (commits), so the ring's
+    // host copy is saved too
+    StateGuard(dflash_session* const* ss, int32_t n, bool history) : history_(history) {
+        for (int32_t k = 0; k < n; ++k) {
+            const dflash_session* s = ss[k];
+            saved_.push_back({ss[k], s->ctx_offset, s->pending, s->cache_len, s->hist_count, s->hist_head,
+                              s->hist_dirty, s->outstanding, s->rows_written,
+                              history ? s->hist_shadow : std::vector<int32_t>()});
+        }
+    }
+    // restores every session and passes the error code through
+    int restore(int rc) {
+        for (const Saved& v : saved_) {
+            dflash_session* s = v.s;
+            s->ctx_offset = v.ctx_offset;
+            s->pending = v.pending;
+            s->cache_len = v.cache_len;
+            s->hist_count = v.hist_count;
+            s->hist_head = v.hist_head;
+            s->outstanding = v.outstanding;
+            s->rows_written = v.rows_written;
+            if (history_) {
+                s->hist_shadow = v.shadow;
+                s->hist_dirty = std::min<int32_t>(kHistory, std::max(v.hist_dirty, v.hist_count));
+            }
+        }
+        return rc;
+    }
+
+private:
+    struct Saved {
+        dflash_session* s;
+        int32_t ctx_offset, pending, cache_len, hist_count, hist_head, hist_dirty;
+        bool outstanding;
+        int64_t rows_written;
+        std::vector<int32_t> shadow;
+    };
+    std::vector<Saved> saved_;
+    bool history_;
+};
+
+// keeps the host copy of the ring equal to what the device ring will hold
+static void shadow_write(dflash_session* s, int32_t slot0, const int32_t* tokens, int32_t count) {
+    for (int32_t i = 0; i < count; ++i) s->hist_shadow[(slot0 + i) % kHistory] = tokens[i];
+}
 
 static void commit_block(dflash_session* s) {
     if (!s->outstanding) return;
@@ -330,8 +388,7 @@ static void append_history(dflash_session* s, const int32_t* tokens, int32_t cou
         s->hist_count += count - kHistory;
         count = kHistory;
     }
-    if (s->hist_shadow.empty()) s->hist_shadow.assign(kHistory, 0);
-    for (int32_t i = 0; i < count; ++i) s->hist_shadow[(s->hist_head + i) % kHistory] = tokens[i];
+    shadow_write(s, s->hist_head, tokens, count);
     s->hist_head = (s->hist_head + count) % kHistory;
     s->hist_count += count;
     s->hist_dirty = std::min<int32_t>(kHistory, s->hist_dirty + count);
@@ -372,13 +429,15 @@ extern "C" int dflash_committed(dflash_session* s, const int32_t* tokens_host, c
     if (!s->ring && frontier + c.block_size > s->cap)
         return fail(DFLASH_E_CAPACITY, "cache capacity exceeded");
     const char* src = (const char*)features_dev + (size_t)start * s->row_bytes();
+    StateGuard guard(&s, 1, true);
     if (s->pending + fresh < c.flush_rows && s->hist_head + fresh <= kHistory) {
         // the usual round: the history tokens and the rows in one step
-        if (int rc = settle_history(s)) return rc;
+        if (int rc = settle_history(s)) return guard.restore(rc);
         int rc = s->ctx->engine->commit_rows(s->view(), s->hist_head, tokens_host + start, fresh,
                                              s->pending_buf() + (size_t)s->pending * s->row_bytes(), src,
                                              (size_t)fresh * s->row_bytes(), s->stream);
-        if (rc) return rc;
+        if (rc) return guard.restore(rc);
+        shadow_write(s, s->hist_head, tokens_host + start, fresh);
         s->hist_head = (s->hist_head + fresh) % kHistory;
         s->hist_count += fresh;
         s->pending += fresh;
@@ -386,18 +445,19 @@ extern "C" int dflash_committed(dflash_session* s, const int32_t* tokens_host, c
     }
     if (s->pending + fresh < c.flush_rows) {
         // no flush (the history wraps the ring): both go out now
-        if (int rc = settle_history(s)) return rc;
+        if (int rc = settle_history(s)) return guard.restore(rc);
         append_history(s, tokens_host + start, fresh);
-        if (int rc = settle_history(s)) return rc;
+        if (int rc = settle_history(s)) return guard.restore(rc);
         int rc = s->ctx->engine->copy_rows(s->pending_buf() + (size_t)s->pending * s->row_bytes(), src,
                                        (size_t)fresh * s->row_bytes(), s->stream);
-        if (rc) return rc;
+        if (rc) return guard.restore(rc);
         s->pending += fresh;
         return 0;
     }
     append_history(s, tokens_host + start, fresh);
     commit_block(s);
-    return write_context(s, src, fresh);
+    if (int rc = write_context(s, src, fresh)) return guard.restore(rc);
+    return 0;
 }
 
 // dflash_committed for several sessions.  Every run is checked first (any
@@ -434,30 +494,32 @@ extern "C" int dflash_committed_batch(dflash_session* const* ss, int32_t count, 
         start[k] = (int32_t)st;
         fresh[k] = T - (int32_t)st;
     }
+    StateGuard guard(ss, count, true);
     std::vector<CommitItem> items;
     for (int32_t k = 0; k < count; ++k) {
         dflash_session* s = ss[k];
         if (!fresh[k] || s->pending + fresh[k] >= c.flush_rows || fresh[k] > kHistory) continue;
-        if (int rc = settle_history(s)) return rc;
+        if (int rc = settle_history(s)) return guard.restore(rc);
         const size_t rb = s->row_bytes();
         items.push_back({s->view().hist, s->hist_head, tokens_host + token_offsets[k] + start[k], fresh[k],
                          s->pending_buf() + (size_t)s->pending * rb,
                          (const char*)features_dev[k] + (size_t)start[k] * rb, (size_t)fresh[k] * rb});
     }
     if (!items.empty()) {
-        if (int rc = ctx->engine->commit_many(items, ss[0]->stream)) return rc;
+        if (int rc = ctx->engine->commit_many(items, ss[0]->stream)) return guard.restore(rc);
     }
     for (int32_t k = 0; k < count; ++k) {
         dflash_session* s = ss[k];
         if (!fresh[k]) continue;
         if (s->pending + fresh[k] < c.flush_rows && fresh[k] <= kHistory) {
+            shadow_write(s, s->hist_head, tokens_host + token_offsets[k] + start[k], fresh[k]);
             s->hist_head = (s->hist_head + fresh[k]) % kHistory;
             s->hist_count += fresh[k];
             s->pending += fresh[k];
         } else {
             const int32_t T = token_offsets[k + 1] - token_offsets[k];
             if (int rc = dflash_committed(s, tokens_host + token_offsets[k], features_dev[k], T, positions[k]))
-                return rc;
+                return guard.restore(rc);
         }
     }
     return 0;
@@ -465,8 +527,10 @@ extern "C" int dflash_committed_batch(dflash_session* const* ss, int32_t count, 
 
 extern "C" int dflash_flush(dflash_session* s) {
     if (!s) return fail(DFLASH_E_ARG, "null session");
+    StateGuard guard(&s, 1, false);
     commit_block(s);
-    return write_context(s, nullptr, 0);
+    if (int rc = write_context(s, nullptr, 0)) return guard.restore(rc);
+    return 0;
 }
 
 // dflash_flush over several sessions: each rewinds, and every session's
@@ -486,6 +550,7 @@ extern "C" int dflash_flush_batch(dflash_session* const* ss, int32_t count) {
         for (int32_t j = 0; j < k; ++j)
             if (ss[j] == s) return fail(DFLASH_E_ARG, "a session appears twice in one batch");
     }
+    StateGuard guard(ss, count, false);
     std::vector<SessView> views(count);
     std::vector<CtxSeg> segs;
     std::vector<int32_t> kept(count, 0);
@@ -504,7 +569,7 @@ extern "C" int dflash_flush_batch(dflash_session* const* ss, int32_t count) {
     }
     if (!segs.empty()) {
         int rc = ctx->engine->ctx_forward(views, segs, ss[0]->ws, ss[0]->ws_sessions, ss[0]->stream);
-        if (rc) return rc;
+        if (rc) return guard.restore(rc);
     }
     for (int32_t k = 0; k < count; ++k) {
         dflash_session* s = ss[k];
@@ -555,6 +620,7 @@ static int propose_many(dflash_session* const* ss, int32_t count, const int32_t*
     }
     // Rewind, then gather every proposing session's pending rows into one
     // context pass (rows ride in the same forward as the blocks).
+    StateGuard guard(ss, count, false);
     std::vector<SessView> views(count);
     std::vector<CtxSeg> segs;
     std::vector<BlockSeq> seqs;
@@ -581,7 +647,7 @@ static int propose_many(dflash_session* const* ss, int32_t count, const int32_t*
     dflash_session* s0 = ss[0];
     if (!segs.empty()) {
         int rc = ctx->engine->ctx_forward(views, segs, s0->ws, s0->ws_sessions, s0->stream);
-        if (rc) return rc;
+        if (rc) return guard.restore(rc);
     }
     for (int32_t k = 0; k < count; ++k) {
         if (!n[k]) continue;
@@ -593,7 +659,9 @@ static int propose_many(dflash_session* const* ss, int32_t count, const int32_t*
         s->outstanding = true;
         views[k] = s->view();
     }
-    return ctx->engine->block_forward(views, seqs, logits, hidden, s0->ws, s0->ws_sessions, s0->stream);
+    if (int rc = ctx->engine->block_forward(views, seqs, logits, hidden, s0->ws, s0->ws_sessions, s0->stream))
+        return guard.restore(rc);
+    return 0;
 }
 
 extern "C" int dflash_propose(dflash_session* s, int32_t current, int32_t max_tokens, float* logits_out,

@@ -15,6 +15,14 @@ namespace {
 
 std::mutex g_mu;
 std::vector<std::string> g_log;
+int g_fail_in = 0;     // > 0: the g_fail_in-th device step from now fails (E_HIP)
+
+// a device step that the test asked to fail, as a refused HIP enqueue would
+int injected() {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_fail_in > 0 && --g_fail_in == 0) return fail(DFLASH_E_HIP, "injected device failure");
+    return 0;
+}
 
 void log_line(const std::string& s) {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -26,10 +34,12 @@ public:
     explicit TraceEngine(const Model& m) : m_(m) {}
     size_t workspace_bytes(int32_t max_sessions) const override { return 256 * (size_t)max_sessions; }
     int copy_rows(void*, const void*, size_t bytes, void*) override {
+        if (int rc = injected()) return rc;
         log_line("copy rows=" + std::to_string(bytes / ((size_t)m_.fc_in * m_.elem)));
         return 0;
     }
     int write_history(const SessView&, int32_t slot0, const int32_t* t, int32_t count, void*) override {
+        if (int rc = injected()) return rc;
         std::string s = "hist slot=" + std::to_string(slot0) + " tokens=";
         for (int32_t i = 0; i < count; ++i) s += (i ? "," : "") + std::to_string(t[i]);
         log_line(s);
@@ -37,6 +47,7 @@ public:
     }
     int ctx_forward(const std::vector<SessView>&, const std::vector<CtxSeg>& segs, void*, int32_t,
                     void*) override {
+        if (int rc = injected()) return rc;
         for (const CtxSeg& g : segs)
             log_line("ctx sess=" + std::to_string(g.sess) + " pos0=" + std::to_string(g.pos0) +
                      " rows=" + std::to_string(g.nrows));
@@ -44,6 +55,7 @@ public:
     }
     int block_forward(const std::vector<SessView>&, const std::vector<BlockSeq>& seqs, float*, float*,
                       void*, int32_t, void*) override {
+        if (int rc = injected()) return rc;
         for (const BlockSeq& b : seqs)
             log_line("block sess=" + std::to_string(b.sess) + " F=" + std::to_string(b.F) +
                      " M=" + std::to_string(b.M) + " cur=" + std::to_string(b.current));
@@ -51,12 +63,14 @@ public:
     }
     int verify(const std::vector<SessView>& sess, const int32_t* offs, const float*, const int32_t*, const float*,
                const dflash_verify_params& p, int32_t*, int32_t*, void*, int32_t, void*) override {
+        if (int rc = injected()) return rc;
         log_line("verify drafts=" + std::to_string(offs[sess.size()]) + " sessions=" +
                  std::to_string(sess.size()) + " round=" + std::to_string(p.round));
         return 0;
     }
     int sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float*,
                const dflash_sample_params& p, int32_t*, float*, void*, int32_t, void*) override {
+        if (int rc = injected()) return rc;
         std::string s = "sample rows=" + std::to_string(row_offsets[sess.size()]) +
                         " round=" + std::to_string(p.round) + " hist=";
         for (size_t k = 0; k < sess.size(); ++k)
@@ -101,6 +115,12 @@ extern "C" int dflash_trace_line(int i, char* buf, int len) {
     if (i < 0 || i >= (int)dflash::g_log.size() || !buf || len <= 0) return -1;
     std::snprintf(buf, (size_t)len, "%s", dflash::g_log[i].c_str());
     return 0;
+}
+
+// the n-th device step from now returns DFLASH_E_HIP (0: none)
+extern "C" void dflash_trace_fail_in(int n) {
+    std::lock_guard<std::mutex> lk(dflash::g_mu);
+    dflash::g_fail_in = n;
 }
 
 extern "C" void dflash_trace_clear(void) {

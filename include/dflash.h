@@ -30,7 +30,14 @@
  *    are exact on return.
  *  - Return value 0 is success; a negative DFLASH_E_* code is an error, with a
  *    thread-local message from dflash_last_error().  A call that fails leaves
- *    every session state unchanged.
+ *    every session's state (offsets, pending rows, cache length, outstanding
+ *    block, committed-token history) as it was before the call.  Errors found
+ *    on the host (E_ARG, E_CONFIG, E_SHAPE, E_CONTEXT_GAP, E_CAPACITY) are
+ *    found before any device work is enqueued.  After E_HIP (the HIP runtime
+ *    refused an enqueue) the host state is put back the same way, but device
+ *    work enqueued earlier in the call may have written cache rows; a
+ *    windowed session's ring can then hold partial rows at visible slots, so
+ *    a session that saw E_HIP should be closed.
  *  - A session is not thread-safe.  Sessions that share a workspace must issue
  *    their calls on one stream (their calls are then serialized by it).
  *  - Linear weights are row-major [out_features, in_features]; all weights of

@@ -503,3 +503,111 @@ def test_committed_batch_rejects_any_bad_run(host):
     rc = _commit_batch(host, ss[:1], [np.arange(70)], [3])
     assert rc == abi.E_CAPACITY                 # 73 + block > capacity 64
     assert [s.state() for s in ss] == before
+
+
+# --------------------------------------------------------------------------
+# device failures (DFLASH_E_HIP injected by the trace backend)
+# --------------------------------------------------------------------------
+
+def _ring_from_trace(lines, ring):
+    """Replays the history writes of a trace onto a host model of the ring."""
+    for l in lines:
+        m = re.match(r"hist slot=(\d+) tokens=(.*)", l)
+        if m:
+            slot = int(m.group(1))
+            toks = [int(x) for x in m.group(2).split(",") if x]
+            ring[slot:slot + len(toks)] = toks
+    return ring
+
+
+def _sample(lib, s, history=512):
+    ids = np.zeros(8, dtype=np.int32)
+    logits = np.zeros(8, dtype=np.float32)
+    offs = (c_int32 * 2)(0, 1)
+    hs = (c_void_p * 1)(s.h)
+    p = abi.SampleParams(0.0, 1.1, history, 0)
+    abi.check(lib, lib.dflash_sample(hs, 1, offs, logits.ctypes.data, byref(p), ids.ctypes.data, None))
+
+
+def _drive(s, step):
+    """One call of the script: ('c', tokens, position), ('f',) or ('p', cur, n)."""
+    if step[0] == "c":
+        t = np.ascontiguousarray(np.asarray(step[1], dtype=np.int32))
+        return s.lib.dflash_committed(s.h, t.ctypes.data_as(ctypes.POINTER(c_int32)), s.feat.ctypes.data,
+                                      len(t), step[2])
+    if step[0] == "f":
+        return s.lib.dflash_flush(s.h)
+    n = c_int32()
+    logits = np.zeros(16, dtype=np.float32)
+    return s.lib.dflash_propose(s.h, step[1], step[2], logits.ctypes.data, None, byref(n))
+
+
+SCRIPT = [("c", list(range(100, 110)), 0), ("p", 3, 7), ("c", [3, 501, 502], 10),
+          ("c", list(range(200, 220)), 13), ("p", 9, 5), ("c", [9], 33), ("f",),
+          ("c", list(range(300, 800)), 34), ("p", 4, 7), ("c", [4, 7], 534)]
+
+
+def _sampled_window(lines, ring):
+    """(count, head) the sampler saw, from its trace line, and the ring slots
+    it reads: the last min(count, 512) ending at head."""
+    m = [re.search(r"hist=(\d+)@(\d+)", l) for l in lines if l.startswith("sample")]
+    count, head = int(m[-1].group(1)), int(m[-1].group(2))
+    hn = min(count, 512)
+    return count, head, [int(ring[(head - hn + i) % 512]) for i in range(hn)]
+
+
+def test_device_failure_leaves_host_state_unchanged(host):
+    """Every device step of every call of a script (one-step commits, flushing
+    commits, a 500-token run that wraps the history ring, proposes, a flush)
+    is made to fail in turn.  The failing call returns DFLASH_E_HIP and the
+    session's host state (offsets, pending rows, cache length, outstanding
+    block, rows written) is what it was before the call; retrying the call
+    then gives the states of a run that never failed, and the history window
+    the sampler reads holds the same tokens (the failed call's partial ring
+    writes are overwritten from the host copy)."""
+    fm = FakeModel(host, flush_rows=16)
+    rc, ctx = fm.create()
+    assert rc == 0
+    ref = HostSession(host, ctx, capacity=2048)
+    _trace(host)
+    ref_states, ref_windows = [], []
+    ref_ring = np.full(512, -1)
+    for step in SCRIPT:
+        assert _drive(ref, step) == 0
+        ref_states.append((ref.state(), ref.rows_written))
+        _sample(host, ref)
+        lines = _trace(host)
+        _ring_from_trace(lines, ref_ring)
+        ref_windows.append(_sampled_window(lines, ref_ring))
+    injected = 0
+    for k in range(len(SCRIPT)):
+        for fail_at in range(1, 16):
+            s = HostSession(host, ctx, capacity=2048)
+            for step in SCRIPT[:k]:
+                assert _drive(s, step) == 0
+            _sample(host, s)
+            lines = _trace(host)
+            ring = _ring_from_trace(lines, np.full(512, -1))
+            window = _sampled_window(lines, ring)
+            before = (s.state(), s.rows_written)
+            host.dflash_trace_fail_in(fail_at)
+            rc = _drive(s, SCRIPT[k])
+            host.dflash_trace_fail_in(0)
+            _ring_from_trace(_trace(host), ring)        # what the failed call did write
+            if rc == 0:                                  # the call has fewer device steps
+                break
+            injected += 1
+            assert rc == abi.E_HIP, (k, fail_at, rc)
+            assert (s.state(), s.rows_written) == before, (k, fail_at)
+            _sample(host, s)                             # the sampler still sees the old history
+            lines = _trace(host)
+            _ring_from_trace(lines, ring)
+            assert _sampled_window(lines, ring) == window, (k, fail_at)
+            assert _drive(s, SCRIPT[k]) == 0
+            assert (s.state(), s.rows_written) == ref_states[k], (k, fail_at)
+            _sample(host, s)
+            lines = _trace(host)
+            _ring_from_trace(lines, ring)
+            assert _sampled_window(lines, ring) == ref_windows[k], (k, fail_at)
+    assert injected >= len(SCRIPT)
+    host.dflash_destroy(ctx)
