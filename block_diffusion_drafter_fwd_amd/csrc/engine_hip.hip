@@ -34,6 +34,8 @@ using namespace kern;
 
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
+static_assert(kHistory == kHistRing, "the kernels index the history ring with kHistRing slots");
+
 constexpr int kSampleChunk = 4096;
 constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
 constexpr int kAttnShortChunk = 256;                 // below: one attention workgroup per CU

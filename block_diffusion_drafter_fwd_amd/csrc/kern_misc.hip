@@ -358,7 +358,7 @@ hipError_t commit_rows(int32_t* hist, const int32_t* tokens, int32_t count, void
 __global__ __launch_bounds__(256) void k_commit_batch(CommitBatchArgs a) {
     const CommitItemArgs& it = a.item[blockIdx.x];
     if (blockIdx.y == 0)
-        for (int j = threadIdx.x; j < it.count; j += 256) it.hist[(it.slot0 + j) % 512] = a.tokens[it.tok0 + j];
+        for (int j = threadIdx.x; j < it.count; j += 256) it.hist[(it.slot0 + j) % kHistRing] = a.tokens[it.tok0 + j];
     for (int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x; i < it.n16; i += (int64_t)gridDim.y * 256)
         it.dst[i] = it.src[i];
 }
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void k_hist_bitmap(SampleArgs a) {
     for (int i = threadIdx.x; i < a.words; i += 256) bm[i] = 0u;
     __syncthreads();
     for (int j = threadIdx.x; j < sd.hist_n; j += 256) {
-        const int tok = sd.hist[(sd.hist_head - sd.hist_n + j + 2 * 512) % 512];
+        const int tok = sd.hist[(sd.hist_head - sd.hist_n + j + 2 * kHistRing) % kHistRing];
         if (tok >= 0 && tok < a.V) atomicOr(&bm[tok >> 5], 1u << (tok & 31));
     }
 }

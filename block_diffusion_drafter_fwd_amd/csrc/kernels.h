@@ -16,6 +16,7 @@ constexpr int kMaxSeg = 32;        // column segments of one GEMM launch
 constexpr int kMaxOut = 16;        // outputs of one norm launch
 constexpr int kMaxL = 16;          // layers of one head-finish launch
 constexpr int kUploadWords = 960;  // 3840-byte payload of one upload launch (kernel arguments: 4 KiB)
+constexpr int kHistRing = 512;     // slots of a session's committed-token ring (penalty history)
 
 // One sequence (session) of a batched call.
 struct SeqDesc {
@@ -200,7 +201,7 @@ struct CommitArgs {
 };
 
 // Commits of several sessions in one launch: item i writes its tokens
-// tokens[tok0 .. tok0+count) to hist[(slot0 + j) mod 512] and copies n16
+// tokens[tok0 .. tok0+count) to hist[(slot0 + j) mod kHistRing] and copies n16
 // 16-byte units from src to dst.  Everything rides in the kernel arguments.
 constexpr int kCommitItems = 32, kCommitBatchTokens = 512;
 struct CommitItemArgs {
