@@ -66,19 +66,76 @@ class Report:
     ids_compared: int = 0
     ids_skipped: int = 0
     rounds: int = 0
+    greedy_compared: int = 0
+    greedy_skipped: int = 0
+    sampled_compared: int = 0
+    sampled_skipped: int = 0
+    sampled_expected_skips: float = 0.0   # sum over sampled rows of P(top-2 gap <= margin)
+    greedy_expected_skips: float = 0.0    # the same for greedy rows (spacing model of the top logits)
 
     def note(self, key, value):
         self.worst[key] = max(self.worst.get(key, 0.0), value)
+
+    def skip_bound_ok(self) -> bool:
+        """Skipped rows within their expected tie counts (plus Poisson slack):
+        sampled rows from the exact Gumbel-max tie probability, greedy rows
+        from the spacing model of the top logits."""
+        def ok(skipped, e):
+            return skipped <= e + 3.0 * math.sqrt(e) + 2.0
+        return ok(self.sampled_skipped, self.sampled_expected_skips) and \
+            ok(self.greedy_skipped, self.greedy_expected_skips)
+
+    def summary(self, name: str) -> dict:
+        return {"case": name, "rounds": self.rounds, "greedy_compared": self.greedy_compared,
+                "greedy_skipped": self.greedy_skipped, "sampled_compared": self.sampled_compared,
+                "sampled_skipped": self.sampled_skipped,
+                "sampled_expected_skips": round(self.sampled_expected_skips, 3),
+                "greedy_expected_skips": round(self.greedy_expected_skips, 3),
+                "worst": {k: float(f"{v:.3g}") for k, v in self.worst.items()}}
+
+
+def tie_probability(probs, tau: float) -> float:
+    """P(top-1 minus top-2 score <= tau) for Gumbel-max scores a_t + g_t with
+    softmax(a) = probs: token k wins by more than tau with probability
+    p_k e^-tau / (1 - p_k (1 - e^-tau)) (shift a_k down by tau and take the
+    Gumbel-max probability of k), summed over k."""
+    p = np.asarray(probs, dtype=np.float64)
+    e = math.exp(-tau)
+    return float(max(0.0, 1.0 - np.sum(p * e / (1.0 - p * (1.0 - e)))))
+
+
+def greedy_tie_probability(z, tau: float, k: int = 8) -> float:
+    """P(top-1 minus top-2 logit <= tau) for a row of many logits drawn from a
+    smooth distribution: near the top the spacings D_j between the j-th and
+    (j+1)-th largest values satisfy j D_j ~ Exp(b) (Renyi's representation
+    for distributions in the Gumbel domain), so the top gap is Exp(b) with b
+    estimated from the row's spacings 2..k+1 (the first is the one tested)."""
+    z = np.asarray(z, dtype=np.float64)
+    top = np.sort(np.partition(z, -(k + 2))[-(k + 2):])[::-1]
+    d = top[:-1] - top[1:]
+    b = float(np.mean((np.arange(1, d.size + 1) * d)[1:k + 1]))
+    return 1.0 - math.exp(-tau / b) if b > 0 else 1.0
+
+
+def log_summary(rep: Report, name: str) -> None:
+    """Appends the case's id coverage to $DFLASH_PARITY_LOG (JSON lines)."""
+    import json
+    import os
+    path = os.environ.get("DFLASH_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rep.summary(name)) + "\n")
 
 
 class Pair:
     """One GPU session and its two oracle twins (exact and bf16-emulating)."""
 
-    def __init__(self, drafter, cfg, weights_np, capacity, seed=0, sid=0, restored=0):
+    def __init__(self, drafter, cfg, weights_np, capacity, seed=0, sid=0, restored=0, twins=None):
         self.cfg = cfg
         self.g = drafter.session(capacity, seed=seed, stream_id=sid, restored_offset=restored)
-        self.o = [OracleSession(DraftModel(cfg, weights_np, emulate_bf16=e), restored)
-                  for e in ((False, True) if cfg.dtype == "bf16" else (False,))]
+        if twins is None:
+            twins = (False, True) if cfg.dtype == "bf16" else (False,)
+        self.o = [OracleSession(DraftModel(cfg, weights_np, emulate_bf16=e), restored) for e in twins]
         self.seed, self.sid = seed, sid
 
     def check_state(self, where=""):
@@ -168,35 +225,68 @@ def id_margin(cfg, z_gpu, z_ref, temperature: float, rho: float = 1.0) -> float:
     return max(m, 2.0 * d + 1e-4)
 
 
-def check_ids(gpu_ids, ref_rows, rep: Report):
-    """ref_rows: (oracle id, oracle scores, margin) per row."""
-    for gid, (oid, scores, tau) in zip(gpu_ids, ref_rows):
+def check_ids(gpu_ids, ref_rows, rep: Report, probs=None):
+    """ref_rows: (oracle id, oracle scores, margin) per row; probs: the
+    oracle's sampling distribution of each row (None for greedy rows).  Rows
+    whose top-2 gap exceeds the margin must agree; the others are ties both
+    answers are right for, and the GPU's id must then score within twice the
+    margin of the oracle's best."""
+    for r, (gid, (oid, scores, tau)) in enumerate(zip(gpu_ids, ref_rows)):
+        sampled = probs is not None and probs[r] is not None
+        if sampled:
+            rep.sampled_expected_skips += tie_probability(probs[r], tau)
+        else:
+            rep.greedy_expected_skips += greedy_tie_probability(scores, tau)
         if top2_gap(scores) > tau:
             rep.ids_compared += 1
+            if sampled:
+                rep.sampled_compared += 1
+            else:
+                rep.greedy_compared += 1
             if int(gid) != int(oid):
                 sc = np.asarray(scores, dtype=np.float64)
                 rank = int(np.sum(sc > sc[int(gid)]))
                 raise AssertionError(f"id {gid} != oracle {oid} (gap {top2_gap(scores)}, margin {tau}; the "
                                      f"GPU's id is the oracle's rank {rank}, {sc[int(oid)] - sc[int(gid)]} below)")
         else:
+            sc = np.asarray(scores, dtype=np.float64)
+            assert sc[int(gid)] >= sc.max() - 2.0 * tau, \
+                f"tie row: GPU id {gid} scores {sc.max() - sc[int(gid)]} below the best (margin {tau})"
             rep.ids_skipped += 1
+            if sampled:
+                rep.sampled_skipped += 1
+            else:
+                rep.greedy_skipped += 1
 
 
 def run_session_script(drafter, cfg, wl: synth.Workload, weights_np, capacity, rounds=None, seed=0, sid=0,
-                       sample=True, check_cache_every=0) -> Report:
+                       sample=True, check_cache_every=0, twins=None, cache_sample=None) -> Report:
     """The synthetic round driver (prompt in commit_rows pieces, then rounds
-    of propose -> sample -> accept -> rewind -> commit) on GPU and oracle."""
+    of propose -> sample -> accept -> rewind -> commit) on GPU and oracle.
+    twins: the oracle modes to run (default: exact and, for bf16, emulating);
+    cache_sample: when set, the prompt's and the final cache are checked at
+    that many seeded slots instead of every slot (long contexts)."""
     from block_diffusion_drafter_fwd_amd import sample as gpu_sample
     rep = Report()
     fs = synth.FeatureSource(cfg, seed, sid)
     rs = synth.RoundScript(cfg, wl, seed, sid)
-    pr = Pair(drafter, cfg, weights_np, capacity, seed, sid)
+    pr = Pair(drafter, cfg, weights_np, capacity, seed, sid, twins=twins)
     ctx_len = wl.context
+
+    def cache_positions():
+        if not cache_sample:
+            return None
+        ctx, _, cache_len, _ = pr.g.state()
+        lo = max(0, ctx - (cfg.window - 1)) if cfg.window else 0
+        pick = np.random.default_rng([seed, sid, cache_len]).integers(lo, cache_len, size=cache_sample)
+        return np.unique(np.concatenate([pick, [lo, cache_len - 1]]))
+
     for p in range(0, ctx_len, wl.commit_rows):
         T = min(wl.commit_rows, ctx_len - p)
         pr.committed(fs.tokens(p, T), fs.features(p, T), p)
-        pr.check_state(f"prompt commit at {p}")
-    pr.check_cache(rep)
+        if not cache_sample or p + T >= ctx_len:
+            pr.check_state(f"prompt commit at {p}")
+    pr.check_cache(rep, cache_positions())
     current = rs.first_anchor()
     for r in range(wl.rounds if rounds is None else rounds):
         if rs.flush_before:
@@ -209,19 +299,20 @@ def run_session_script(drafter, cfg, wl: synth.Workload, weights_np, capacity, r
                                     probs=wl.probs)
             ids = ids.cpu().numpy()
             o = pr.o[-1]
-            ref = []
+            ref, ref_probs = [], []
             for i in range(n):
                 oid, oprob, score = sample_row(out["logits"][i], o.history[-wl.history:] if wl.history else [],
                                                wl.temperature, wl.rep_penalty, pr.seed, pr.sid, r, i)
                 ref.append((oid, score, id_margin(cfg, logits[i].double().cpu().numpy(), out["logits"][i],
                                                   wl.temperature, wl.rep_penalty)))
+                ref_probs.append(oprob)
                 if probs is not None:
                     e = rel_err(probs[i].double().cpu().numpy(), oprob)
                     pt = probs_tol(logits[i].double().cpu().numpy(), out["logits"][i], wl.temperature)
                     rep.note("probs", e)
                     rep.note("probs/bound", e / pt)
                     assert e < pt, f"probs rel err {e} above the bound {pt} implied by the logits"
-            check_ids(ids, ref, rep)
+            check_ids(ids, ref, rep, ref_probs)
         n = res[0] if res is not None else 0
         a = rs.accept(n)
         pr.commit_block()
@@ -232,8 +323,8 @@ def run_session_script(drafter, cfg, wl: synth.Workload, weights_np, capacity, r
         current = rs.bonus()
         rep.rounds += 1
         if check_cache_every and (r + 1) % check_cache_every == 0:
-            pr.check_cache(rep)
+            pr.check_cache(rep, cache_positions())
     pr.flush()
     pr.check_state("final flush")
-    pr.check_cache(rep)
+    pr.check_cache(rep, cache_positions())
     return rep

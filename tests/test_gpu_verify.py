@@ -113,3 +113,57 @@ def test_verify_rejects_sampling_without_draft_probabilities(setup):
     ids = torch.zeros((int(offs[-1]),), dtype=torch.int32, device="cuda")
     with pytest.raises(DFlashError):
         verify(sessions, offs, target, ids, None, 0.5, 0)
+
+
+def _block(rng, n, temperature):
+    """Target rows (n + 1), draft ids and draft probabilities of one block:
+    greedy drafts follow the target's argmax up to a random break; sampled
+    drafts are drawn from a mix of the target's own p and unrelated q."""
+    target = rng.normal(scale=2.0, size=(n + 1, V)).astype(np.float32)
+    ids = np.zeros(max(1, n), np.int32)
+    q = np.zeros((max(1, n), V), np.float32)
+    brk = int(rng.integers(0, n + 1))
+    for i in range(n):
+        if temperature == 0.0:
+            am = int(np.argmax(target[i]))
+            ids[i] = am if i < brk else (am + 1 + int(rng.integers(0, V - 1))) % V
+        else:
+            qi = softmax(target[i], temperature) if rng.integers(0, 2) else softmax(rng.normal(scale=2.0, size=V), 1.0)
+            q[i] = qi.astype(np.float32)
+            qi64 = q[i].astype(np.float64)
+            ids[i] = int(rng.choice(V, p=qi64 / qi64.sum()))
+    return target, ids, q
+
+
+@pytest.mark.parametrize("n", [0, 3, 7])
+@pytest.mark.parametrize("temperature", [0.0, 0.7, 1.0])
+def test_one_session_verify_equals_batched_and_oracle(setup, n, temperature):
+    """A one-session call (its descriptor and draft count travel in the
+    kernel arguments; no tables are uploaded) gives the same (accepted, next)
+    as the same session inside a five-session call, and as the oracle; n = 0
+    (only the bonus row) and n = blockSize - 1 included."""
+    from block_diffusion_drafter_fwd_amd import verify
+    cfg, d, sessions = setup
+    rng = np.random.default_rng(100 + n + int(10 * temperature))
+    rnd = 5 + n
+    target, ids, q = _block(rng, n, temperature)
+    T = torch.from_numpy(target).cuda()
+    I = torch.from_numpy(ids).cuda()
+    Q = torch.from_numpy(q).cuda() if temperature > 0 else None
+    acc1, nxt1 = verify(sessions[:1], [0, n], T, I, Q, temperature, rnd)
+    # the same block as session 0 of a five-session call (the others draft 2 each)
+    others = [_block(rng, 2, temperature) for _ in range(4)]
+    tg = np.concatenate([target] + [o[0] for o in others])
+    ii = np.concatenate([ids[:n]] + [o[1][:2] for o in others]).astype(np.int32)
+    qq = np.concatenate([q[:n]] + [o[2][:2] for o in others]).astype(np.float32)
+    offs = np.array([0, n, n + 2, n + 4, n + 6, n + 8], np.int32)
+    accb, nxtb = verify(sessions, offs, torch.from_numpy(tg).cuda(), torch.from_numpy(ii).cuda(),
+                        torch.from_numpy(qq).cuda() if temperature > 0 else None, temperature, rnd)
+    one = (int(acc1.cpu()[0]), int(nxt1.cpu()[0]))
+    assert one == (int(accb.cpu()[0]), int(nxtb.cpu()[0]))
+    a, x, info = verify_block(target, ids[:n], q[:n] if temperature > 0 else None, temperature, 100, 0, rnd)
+    close = temperature > 0 and (any(abs(uq - p) <= 1e-5 * max(uq, p, 1e-30) for uq, p in info["tests"]) or
+                                 (lambda sc: sc.size > 1 and sc[-1] - sc[-2] < 1e-4)(
+                                     np.sort(info["scores"][np.isfinite(info["scores"])])))
+    if not close:
+        assert one == (a, x), (one, a, x)
