@@ -95,6 +95,7 @@ def parse():
     ap.add_argument("--cpu-rounds", type=int, default=None, help="propose + sample rounds of the oracle sample")
     ap.add_argument("--no-stages", action="store_true",
                     help="time only the dominant kernel (skip the attention, sampler, verify and flush stages)")
+    ap.add_argument("--no-spec-loop", action="store_true", help="skip the closed speculative round")
     ap.add_argument("--no-secondary", action="store_true",
                     help="default run: skip the batched workload timed after the long one")
     ap.add_argument("--no-width-sweep", action="store_true",
@@ -236,7 +237,7 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
     st = Stage(d.lib, d.ctx)
     B = cfg.block_size
     n_rounds = warmup + steps
-    extra = 64                                   # rounds run after the timed ones (stage passes)
+    extra = 64 + 80                              # rounds after the timed ones (stage passes, closed loop)
     capacity = wl.context + (n_rounds + extra) * B + 64
     if cfg.window:
         capacity = cfg.window + B - 1
@@ -385,6 +386,7 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
                                           launches=l_k, target_frac=0.5)
 
     sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
+    spec = None if args.no_spec_loop else spec_loop(s, cfg, wl, pool, n, state["current"], logits, torch, np)
 
     return {
         "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
@@ -409,7 +411,70 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
         "roofline": roofline,
         "kernels": kernels,
         **({"width_sweep": sweep} if sweep else {}),
+        **({"spec_round": spec} if spec else {}),
     }
+
+
+def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8, agree=0.7, boost=10.0):
+    """The closed speculative round on the GPU: propose -> sample (ids and,
+    when sampling, the proposal probabilities) -> verify against a seeded
+    synthetic target -> rewind and commit the anchor plus the accepted
+    drafts, the correction or bonus token becoming the next anchor.  The
+    target (no target model is here) is N(0, 1) noise per position with
+    +boost on one preferred token: the draft's own token with probability
+    `agree`, else a seeded token (the bonus row: always a seeded token); its
+    noise rows are drawn on the device before timing, the preference is
+    added in the round.  The one host synchronisation per round reads the
+    accepted count, the next token and the drafted ids, which the commit
+    needs on the host.  Reported: emitted tokens (accepted + 1) per second
+    of drafting, verification and commits, the target's own forward not
+    included."""
+    from block_diffusion_drafter_fwd_amd import sample, verify
+    dev = logits.device
+    V, T = cfg.vocab, wl.temperature
+    total = warm + rounds
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    base = torch.randn((total, n + 1, V), generator=gen, device=dev)
+    rng = np.random.default_rng(1234)
+    coins = torch.from_numpy(rng.uniform(size=(total, n)) < agree).to(dev)
+    toks = torch.from_numpy(rng.integers(0, V - 1, size=(total, n + 1))).to(dev)
+    rows = torch.arange(n, device=dev)
+    s.commit_block()
+    state = {"cur": current, "acc": []}
+
+    def rnd(r):
+        k, lg, _ = s.propose(state["cur"], n, logits=logits)
+        ids, probs = sample([s], [0, k], lg, T, wl.rep_penalty, wl.history, 10_000 + r, probs=T > 0)
+        tgt = base[r]
+        pref = torch.where(coins[r, :k], ids.long(), toks[r, :k])
+        tgt[rows[:k], pref] += boost
+        tgt[k, toks[r, k]] += boost
+        acc, nxt = verify([s], [0, k], tgt[:k + 1], ids, probs, T, 10_000 + r)
+        out = torch.cat([acc, nxt, ids]).cpu().numpy()          # the round's one synchronisation
+        a, x = int(out[0]), int(out[1])
+        s.commit_block()
+        F = s.state()[0]
+        _, ft = pool.at(F, a + 1)
+        s.committed(np.concatenate([[state["cur"]], out[2:2 + a]]).astype(np.int32), ft, F)
+        state["cur"] = x
+        return a
+
+    for r in range(warm):
+        rnd(r)
+    torch.cuda.synchronize()
+    gc_pause()
+    t = time.perf_counter()
+    for r in range(warm, total):
+        state["acc"].append(rnd(r))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t
+    gc.enable()
+    acc = state["acc"]
+    return {"rounds": rounds, "width": n, "temperature": T, "target_agree": agree,
+            "accepted_per_round": round(float(np.mean(acc)), 3),
+            "emitted_tokens_per_s": round((sum(acc) + rounds) / el, 1),
+            "ms_per_round": round(el / rounds * 1e3, 4),
+            "note": "drafter + verification + commit per round; the target's forward is synthetic and not timed"}
 
 
 def width_sweep(s, cfg, current, logits, torch, np, reps=20):

@@ -34,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "DraftConfig", "Workload", "CONFIGS", "WORKLOADS", "config", "weight_specs",
-    "make_weights", "bf16_bits", "FeatureSource", "RoundScript", "session_lengths",
+    "make_weights", "bf16_bits", "FeatureSource", "RoundScript", "SyntheticTarget", "session_lengths",
 ]
 
 _PIECE = 1 << 24          # elements per independently keyed weight piece
@@ -347,3 +347,44 @@ class RoundScript:
 
     def bonus(self) -> int:
         return int(self.rng.integers(0, self.cfg.vocab - 1))
+
+
+class SyntheticTarget:
+    """Stand-in for the target model of a verification round (no checkpoint is
+    here): the logits of the n + 1 positions that follow a drafted block.
+
+    Row i (the token after block position i; row n is the bonus position) is
+    N(0, sigma) noise drawn from ``default_rng([seed, 23, session, round])``
+    plus ``boost`` on one preferred token: for a row below n, with
+    probability ``agree`` (a seeded coin from the same stream) the token the
+    draft proposed there, else a seeded token; for row n always a seeded
+    token.  With boost well above the noise's maximum the preferred token is
+    the row's argmax, so a greedy round accepts the drafts up to the first
+    coin that came up "disagree" (expected accepted drafts
+    sum_{j<=n} agree^j), and a sampling round accepts a draft about as often.
+    It depends only on the seeds, the round and the drafted ids, so two
+    drafters that draft the same ids see the same target.
+    """
+
+    def __init__(self, vocab: int, seed: int = 0, session: int = 0, sigma: float = 1.0,
+                 boost: float = 10.0, agree: float = 0.7):
+        self.vocab, self.seed, self.session = vocab, seed, session
+        self.sigma, self.boost, self.agree = sigma, boost, agree
+
+    def draws(self, rnd: int, n: int):
+        """(noise [n+1, V], coins [n] (True: prefer the draft), random tokens [n+1])."""
+        rng = np.random.default_rng([self.seed, 23, self.session, rnd])
+        noise = rng.standard_normal((n + 1, self.vocab), dtype=np.float32) * np.float32(self.sigma)
+        coins = rng.uniform(size=n) < self.agree
+        toks = rng.integers(0, self.vocab - 1, size=n + 1)
+        return noise, coins, toks
+
+    def rows(self, rnd: int, drafted) -> np.ndarray:
+        """Target logits [n + 1, V] (float32) for the drafted ids of a round."""
+        drafted = np.asarray(drafted, dtype=np.int64).reshape(-1)
+        n = drafted.size
+        noise, coins, toks = self.draws(rnd, n)
+        pref = np.where(coins, drafted, toks[:n]) if n else np.zeros(0, np.int64)
+        noise[np.arange(n), pref] += np.float32(self.boost)
+        noise[n, toks[n]] += np.float32(self.boost)
+        return noise
