@@ -7,12 +7,13 @@ the library was not built.
 """
 from .abi import ContextGap, DFlashError  # noqa: F401
 
-__all__ = ["Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "verify", "WidthPolicy", "ContextGap",
-           "DFlashError"]
+__all__ = ["Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "verify",
+           "verify_noalloc", "WidthPolicy", "ContextGap", "DFlashError"]
 
 
 def __getattr__(name):
-    if name in ("Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "verify", "WidthPolicy"):
+    if name in ("Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "verify",
+                "verify_noalloc", "WidthPolicy"):
         from . import drafter
         return getattr(drafter, name)
     raise AttributeError(name)

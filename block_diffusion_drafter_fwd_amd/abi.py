@@ -73,6 +73,8 @@ SYMBOLS = {
                               POINTER(SampleParams), c_void_p, c_void_p]),
     "dflash_verify": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p,
                               POINTER(VerifyParams), c_void_p, c_void_p]),
+    "dflash_verify_noalloc": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p,
+                                      POINTER(VerifyParams), c_void_p, c_void_p]),
     "dflash_width_policy_create": (c_int, [c_int32, c_float, c_float, c_float, c_float, c_float,
                                            POINTER(c_void_p)]),
     "dflash_width_policy_observe": (c_int, [c_void_p, c_int32, c_int32]),

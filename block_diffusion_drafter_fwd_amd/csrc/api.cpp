@@ -708,31 +708,58 @@ extern "C" int dflash_sample(dflash_session* const* sessions, int32_t count, con
                                    s0->ws_sessions, s0->stream);
 }
 
-extern "C" int dflash_verify(dflash_session* const* sessions, int32_t count, const int32_t* draft_offsets,
-                             const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
-                             const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out) {
+// Checks shared by dflash_verify and dflash_verify_noalloc; fills the views.
+static int verify_checks(dflash_session* const* sessions, int32_t count, const int32_t* draft_offsets,
+                         const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
+                         const dflash_verify_params* params, const int32_t* accepted_out, const int32_t* next_out,
+                         std::vector<SessView>* views) {
     if (!sessions || count <= 0 || !draft_offsets || !target_logits || !params || !accepted_out || !next_out)
         return fail(DFLASH_E_ARG, "null argument");
     dflash_session* s0 = sessions[0];
     if (!s0) return fail(DFLASH_E_ARG, "null session");
-    if (count > s0->ws_sessions) return fail(DFLASH_E_CAPACITY, "more sessions than the workspace serves");
     if (!(params->temperature >= 0.f) || params->round < 0) return fail(DFLASH_E_ARG, "verify parameters out of range");
     if (draft_offsets[0] != 0) return fail(DFLASH_E_ARG, "draft_offsets[0] must be 0");
-    std::vector<SessView> views(count);
+    views->assign(count, SessView{});
     for (int32_t k = 0; k < count; ++k) {
         dflash_session* s = sessions[k];
-        if (!s || s->ctx != s0->ctx || s->ws != s0->ws || s->stream != s0->stream)
-            return fail(DFLASH_E_ARG, "sessions must share context, workspace and stream");
+        if (!s || s->ctx != s0->ctx || s->stream != s0->stream)
+            return fail(DFLASH_E_ARG, "sessions must share context and stream");
         if (draft_offsets[k + 1] < draft_offsets[k] ||
             draft_offsets[k + 1] - draft_offsets[k] > s0->ctx->model.cfg.block_size - 1)
             return fail(DFLASH_E_ARG, "draft_offsets must be non-decreasing with at most blockSize-1 drafts per session");
-        views[k] = s->view();
+        (*views)[k] = s->view();
     }
     if (draft_offsets[count] > 0 && !draft_ids) return fail(DFLASH_E_ARG, "null draft ids");
     if (draft_offsets[count] > 0 && params->temperature > 0.f && !draft_probs)
         return fail(DFLASH_E_ARG, "sampling verification needs the draft probabilities");
+    return 0;
+}
+
+extern "C" int dflash_verify(dflash_session* const* sessions, int32_t count, const int32_t* draft_offsets,
+                             const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
+                             const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out) {
+    std::vector<SessView> views;
+    if (int rc = verify_checks(sessions, count, draft_offsets, target_logits, draft_ids, draft_probs, params,
+                               accepted_out, next_out, &views))
+        return rc;
+    dflash_session* s0 = sessions[0];
+    if (count > s0->ws_sessions) return fail(DFLASH_E_CAPACITY, "more sessions than the workspace serves");
+    for (int32_t k = 0; k < count; ++k)
+        if (sessions[k]->ws != s0->ws) return fail(DFLASH_E_ARG, "sessions must share the workspace");
     return s0->ctx->engine->verify(views, draft_offsets, target_logits, draft_ids, draft_probs, *params,
                                    accepted_out, next_out, s0->ws, s0->ws_sessions, s0->stream);
+}
+
+extern "C" int dflash_verify_noalloc(dflash_session* const* sessions, int32_t count, const int32_t* draft_offsets,
+                                     const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
+                                     const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out) {
+    std::vector<SessView> views;
+    if (int rc = verify_checks(sessions, count, draft_offsets, target_logits, draft_ids, draft_probs, params,
+                               accepted_out, next_out, &views))
+        return rc;
+    dflash_session* s0 = sessions[0];
+    return s0->ctx->engine->verify_scratch(views, draft_offsets, target_logits, draft_ids, draft_probs, *params,
+                                           accepted_out, next_out, s0->stream);
 }
 
 extern "C" int dflash_session_state(const dflash_session* s, int32_t* ctx_offset, int32_t* pending,

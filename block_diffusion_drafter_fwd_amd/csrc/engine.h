@@ -119,6 +119,10 @@ public:
     virtual int verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
                        const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
                        int32_t* accepted, int32_t* next, void* ws, int32_t ws_sessions, void* stream) = 0;
+    // verify with the backend's own static scratch instead of a workspace
+    virtual int verify_scratch(const std::vector<SessView>& sess, const int32_t* draft_offsets,
+                               const float* target, const int32_t* draft_ids, const float* draft_probs,
+                               const dflash_verify_params& p, int32_t* accepted, int32_t* next, void* stream) = 0;
     virtual int cache_read(const SessView& s, int32_t layer, int32_t pos0, int32_t count,
                            float* k_out, float* v_out, void* stream) = 0;
     // event timing of one named stage (see dflash_profile_begin)

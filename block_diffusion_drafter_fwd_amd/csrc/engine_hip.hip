@@ -18,6 +18,7 @@
 // reduction pass is launched.
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <cmath>
 #include <cstring>
@@ -28,6 +29,11 @@
 #include "kernels.h"
 
 namespace dflash {
+
+// the static scratch array of dflash_verify_noalloc (4 MiB per GPU); see
+// scratch_address below for how host code obtains its device address
+static __device__ __align__(256) char scratch[size_t(4) << 20];
+
 namespace {
 
 using namespace kern;
@@ -35,6 +41,31 @@ using namespace kern;
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 static_assert(kHistory == kHistRing, "the kernels index the history ring with kHistRing slots");
+
+// Device memory for the calls that take no workspace (dflash_verify_noalloc):
+// one array per GPU for the process's lifetime.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): each device's address comes from hipGetSymbolAddress, resolved
+// once per device with that device current, and only that pointer is used.
+constexpr size_t kScratchBytes = sizeof(scratch);
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address (resolved on the first call per device)
+hipError_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 constexpr int kSampleChunk = 4096;
 constexpr int kAttnMinChunk = 64;                    // keys per attention work item, at least (one tile)
@@ -64,7 +95,7 @@ struct WsLayout {
 
 class HipEngine : public Engine {
 public:
-    HipEngine(const Model& m, int num_cus) : m_(m), cus_(num_cus) {}
+    HipEngine(const Model& m, int num_cus, void* scratch) : m_(m), cus_(num_cus), scratch_(scratch) {}
 
     WsLayout layout(int32_t ms) const {
         const dflash_config& c = m_.cfg;
@@ -182,6 +213,9 @@ public:
     int verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
                const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p, int32_t* accepted,
                int32_t* next, void* ws, int32_t ws_sessions, void* stream) override;
+    int verify_scratch(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+                       const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
+                       int32_t* accepted, int32_t* next, void* stream) override;
 
     int cache_read(const SessView& s, int32_t layer, int32_t pos0, int32_t count, float* k_out, float* v_out,
                    void* stream) override {
@@ -216,6 +250,12 @@ public:
     }
 
 private:
+    int verify_in(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+                  const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p, int32_t* accepted,
+                  int32_t* next, char* tab, float* stats, float* stats2, void* stream);
+    size_t verify_scratch_bytes(int32_t count, int32_t Rt) const;
+    size_t verify_table_bytes(int32_t count, int32_t Rt) const;
+
     // Brackets the launches of one stage with events while that stage is profiled.
     struct Timed {
         HipEngine* e;
@@ -297,6 +337,7 @@ private:
 
     Model m_;
     int cus_;
+    void* scratch_ = nullptr;    // this device's static scratch array (device address)
     std::string stage_;
     std::vector<hipEvent_t> ev_;
     size_t ev_used_ = 0;
@@ -736,13 +777,50 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
 int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
                       const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
                       int32_t* accepted, int32_t* next, void* ws, int32_t ws_sessions, void* stream) {
-    const dflash_config& c = m_.cfg;
     const WsLayout w = layout(ws_sessions);
-    hipStream_t st = (hipStream_t)stream;
-    char* base = (char*)ws;
     const int32_t count = (int32_t)sess.size();
     const int32_t Rt = draft_offsets[count] + count;     // target rows: n_k + 1 per session
     if (Rt > w.r_blk) return fail(DFLASH_E_CAPACITY, "verified rows exceed the workspace");
+    char* base = (char*)ws;
+    return verify_in(sess, draft_offsets, target, draft_ids, draft_probs, p, accepted, next, base + w.tables,
+                     (float*)(base + w.stats), (float*)(base + w.stats2), stream);
+}
+
+// The scratch a verification needs: its tables, then two [Rt][nchunk][4]
+// float statistics arrays (every element is written before it is read).
+size_t HipEngine::verify_scratch_bytes(int32_t count, int32_t Rt) const {
+    const size_t stats = 16 * (size_t)Rt * ((m_.cfg.vocab + kSampleChunk - 1) / kSampleChunk);
+    return al(verify_table_bytes(count, Rt)) + 2 * al(stats);
+}
+
+size_t HipEngine::verify_table_bytes(int32_t count, int32_t Rt) const {
+    return sizeof(SeqDesc) * (size_t)count + sizeof(RowInfo) * (size_t)Rt + sizeof(int32_t) * (count + 1) + 64;
+}
+
+int HipEngine::verify_scratch(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+                              const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
+                              int32_t* accepted, int32_t* next, void* stream) {
+    if (!scratch_) return fail(DFLASH_E_HIP, "no scratch array on this device");
+    const int32_t count = (int32_t)sess.size();
+    const int32_t Rt = draft_offsets[count] + count;
+    if (verify_scratch_bytes(count, Rt) > kScratchBytes)
+        return fail(DFLASH_E_CAPACITY, "verification exceeds the static scratch array (" +
+                                           std::to_string(kScratchBytes >> 20) + " MiB)");
+    const size_t stats = al(16 * (size_t)Rt * ((m_.cfg.vocab + kSampleChunk - 1) / kSampleChunk));
+    char* base = (char*)scratch_;
+    char* tab = base;
+    char* s1 = base + al(verify_table_bytes(count, Rt));
+    return verify_in(sess, draft_offsets, target, draft_ids, draft_probs, p, accepted, next, tab, (float*)s1,
+                     (float*)(s1 + stats), stream);
+}
+
+int HipEngine::verify_in(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
+                         const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
+                         int32_t* accepted, int32_t* next, char* tab, float* stats, float* stats2, void* stream) {
+    const dflash_config& c = m_.cfg;
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t count = (int32_t)sess.size();
+    const int32_t Rt = draft_offsets[count] + count;
     std::vector<SeqDesc> descs(count);
     std::vector<RowInfo> info;
     for (int32_t k = 0; k < count; ++k) {
@@ -761,7 +839,6 @@ int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_of
         const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
         const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
         const size_t o_offs = tb.add(draft_offsets, sizeof(int32_t) * (size_t)(count + 1));
-        char* tab = base + w.tables;
         HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
         a.seqs = (const SeqDesc*)(tab + o_desc);
         a.rows = (const RowInfo*)(tab + o_info);
@@ -770,15 +847,15 @@ int HipEngine::verify(const std::vector<SessView>& sess, const int32_t* draft_of
     a.target = target;
     a.draft_ids = draft_ids;
     a.draft_probs = draft_probs;
-    a.stats = (float*)(base + w.stats);
-    a.stats2 = (float*)(base + w.stats2);
+    a.stats = stats;
+    a.stats2 = stats2;
     a.accepted = accepted;
+    a.nchunk = (c.vocab + kSampleChunk - 1) / kSampleChunk;
     a.next = next;
     a.V = c.vocab;
     a.Rt = Rt;
     a.nseq = count;
     a.chunk = kSampleChunk;
-    a.nchunk = w.nchunk_max;
     a.round = p.round;
     a.temperature = p.temperature;
     HIP_OK(kern::verify(a, st));
@@ -852,7 +929,13 @@ Engine* make_engine(const Model& m, std::string* err) {
         *err = std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e);
         return nullptr;
     }
-    return new HipEngine(m, cus);
+    void* scratch_ptr = nullptr;
+    e = scratch_address(dev, &scratch_ptr);
+    if (e != hipSuccess) {
+        *err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+        return nullptr;
+    }
+    return new HipEngine(m, cus, scratch_ptr);
 }
 
 }  // namespace dflash

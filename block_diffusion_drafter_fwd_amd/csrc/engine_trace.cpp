@@ -68,6 +68,13 @@ public:
                  std::to_string(sess.size()) + " round=" + std::to_string(p.round));
         return 0;
     }
+    int verify_scratch(const std::vector<SessView>& sess, const int32_t* offs, const float*, const int32_t*,
+                       const float*, const dflash_verify_params& p, int32_t*, int32_t*, void*) override {
+        if (int rc = injected()) return rc;
+        log_line("verify_noalloc drafts=" + std::to_string(offs[sess.size()]) + " sessions=" +
+                 std::to_string(sess.size()) + " round=" + std::to_string(p.round));
+        return 0;
+    }
     int sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float*,
                const dflash_sample_params& p, int32_t*, float*, void*, int32_t, void*) override {
         if (int rc = injected()) return rc;

@@ -251,6 +251,29 @@ def verify(sessions: Sequence[Session], draft_offsets: Sequence[int], target_log
     return acc, nxt
 
 
+def verify_noalloc(sessions: Sequence[Session], draft_offsets: Sequence[int], target_logits: torch.Tensor,
+                   draft_ids: Optional[torch.Tensor], draft_probs: Optional[torch.Tensor], temperature: float,
+                   round: int, accepted_out: torch.Tensor, next_out: torch.Tensor) -> None:
+    """dflash_verify_noalloc: as ``verify`` into the caller's int32 device
+    outputs, with the library's static scratch array instead of a workspace
+    (nothing is allocated, here or in the library)."""
+    d = sessions[0].d
+    n = len(sessions)
+    for t, dt in ((target_logits, torch.float32), (draft_ids, torch.int32), (draft_probs, torch.float32),
+                  (accepted_out, torch.int32), (next_out, torch.int32)):
+        if t is not None and (not t.is_contiguous() or t.device.type != "cuda" or t.dtype != dt):
+            raise ValueError("verify operands: contiguous device tensors, fp32 logits / probabilities, int32 ids")
+    if accepted_out.numel() < n or next_out.numel() < n:
+        raise ValueError("outputs need one entry per session")
+    hs = (c_void_p * n)(*[s.h for s in sessions])
+    offs = (c_int32 * (n + 1))(*[int(x) for x in draft_offsets])
+    p = abi.VerifyParams(float(temperature), int(round))
+    check(d.lib, d.lib.dflash_verify_noalloc(hs, n, offs, target_logits.data_ptr(),
+                                             draft_ids.data_ptr() if draft_ids is not None else None,
+                                             draft_probs.data_ptr() if draft_probs is not None else None,
+                                             byref(p), accepted_out.data_ptr(), next_out.data_ptr()))
+
+
 def sample(sessions: Sequence[Session], row_offsets: Sequence[int], logits: torch.Tensor, temperature: float,
            rep_penalty: float = 1.0, history: int = 512, round: int = 0,
            probs: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:

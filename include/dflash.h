@@ -295,6 +295,21 @@ int dflash_verify(dflash_session* const* sessions, int32_t count, const int32_t*
                   const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
                   const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out);
 
+/* dflash_verify for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, results and errors, but the verification's tables and
+ * statistics live in a static 4 MiB device array of the library (one per
+ * GPU, held until the process ends) instead of the sessions' workspace, so
+ * the sessions need not share one.  The call allocates nothing.  It needs
+ * 32 bytes per target row and 4096-token vocabulary chunk (2 KiB per row at
+ * a 262144-token vocabulary: up to about 2000 target rows) plus its tables;
+ * a call needing more fails with E_CAPACITY and does nothing.  Every call on one GPU uses the same array: calls that overlap on
+ * one GPU (on different streams, or from several threads) race and must be
+ * ordered by the caller. */
+int dflash_verify_noalloc(dflash_session* const* sessions, int32_t count, const int32_t* draft_offsets,
+                          const float* target_logits, const int32_t* draft_ids, const float* draft_probs,
+                          const dflash_verify_params* params, int32_t* accepted_out, int32_t* next_out);
+
 /* Draft width controller (host only).  The pages: DFlash2 drafts a fixed
  * seven tokens per round instead of following Ollama's depth controller, whose
  * shallower picks lose more accepted tokens than they save in verify time.
