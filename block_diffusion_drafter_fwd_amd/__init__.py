@@ -7,12 +7,12 @@ the library was not built.
 """
 from .abi import ContextGap, DFlashError  # noqa: F401
 
-__all__ = ["Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "verify",
+__all__ = ["Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "select", "verify",
            "verify_noalloc", "WidthPolicy", "ContextGap", "DFlashError"]
 
 
 def __getattr__(name):
-    if name in ("Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "verify",
+    if name in ("Drafter", "Session", "committed_batch", "flush_batch", "propose_batch", "sample", "select", "verify",
                 "verify_noalloc", "WidthPolicy"):
         from . import drafter
         return getattr(drafter, name)

@@ -22,7 +22,7 @@ class Config(ctypes.Structure):
         "dtype", "hidden", "layers", "q_heads", "kv_heads", "head_dim", "taps", "target_hidden",
         "vocab", "block_size", "mask_id", "window", "intermediate", "causal", "qk_norm", "gate",
         "aux_norms", "ctx_input_norm", "fused_qkv", "attention_bias", "flush_rows")] + [
-        ("rope_theta", c_float), ("rms_eps", c_float)]
+        ("rope_theta", c_float), ("rms_eps", c_float), ("sel_candidates", c_int32), ("sel_dim", c_int32)]
 
 
 class Tensor(ctypes.Structure):
@@ -39,11 +39,16 @@ class LayerWeights(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [("embed", Tensor), ("lm_head", Tensor), ("fc", Tensor), ("hidden_norm", Tensor),
-                ("norm", Tensor), ("aux_norms", Tensor), ("layers", POINTER(LayerWeights))]
+                ("norm", Tensor), ("aux_norms", Tensor), ("layers", POINTER(LayerWeights)),
+                ("sel_prev", Tensor), ("sel_next", Tensor)]
 
 
 class SampleParams(ctypes.Structure):
     _fields_ = [("temperature", c_float), ("rep_penalty", c_float), ("history", c_int32), ("round", c_int32)]
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("round", c_int32)]
 
 
 class VerifyParams(ctypes.Structure):
@@ -71,6 +76,8 @@ SYMBOLS = {
                                      c_void_p, POINTER(c_int32)]),
     "dflash_sample": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p,
                               POINTER(SampleParams), c_void_p, c_void_p]),
+    "dflash_select": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, POINTER(c_int32),
+                              POINTER(SelectParams), c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_verify": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p,
                               POINTER(VerifyParams), c_void_p, c_void_p]),
     "dflash_verify_noalloc": (c_int, [POINTER(c_void_p), c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p,

@@ -108,6 +108,11 @@ static int check_config(const dflash_config& c) {
     if (c.flush_rows < 1 || c.flush_rows > 4096) return bad("flush_rows must lie in 1..4096");
     if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return bad("rms_eps and rope_theta must be positive");
     if (c.head_dim % 2) return bad("head_dim must be even");
+    if (c.sel_candidates < 0 || c.sel_candidates > 16 || c.sel_candidates > c.vocab)
+        return bad("sel_candidates must lie in 0..min(16, vocab)");
+    if (c.sel_candidates && (c.sel_dim < 1 || c.sel_dim > 256)) return bad("sel_dim must lie in 1..256");
+    if ((int64_t)c.sel_candidates * ((c.vocab + 4095) / 4096) > 1024)
+        return bad("sel_candidates x ceil(vocab / 4096) must be at most 1024");
     if (c.dtype == DFLASH_BF16) {
         if (c.head_dim != 128) return bad("bf16 path needs head_dim 128");
         if (c.hidden % 64 || c.intermediate % 64 || c.target_hidden % 64 ||
@@ -147,6 +152,11 @@ extern "C" int dflash_create(const dflash_config* cfg, const dflash_weights* w, 
         (rc = check_tensor(w->norm, "norm", H, -1)))
         return rc;
     if (c.aux_norms && (rc = check_tensor(w->aux_norms, "aux_norms", c.taps, c.target_hidden))) return rc;
+    if (c.sel_candidates && ((rc = check_tensor(w->sel_prev, "sel_prev", V, c.sel_dim)) ||
+                             (rc = check_tensor(w->sel_next, "sel_next", V, c.sel_dim))))
+        return rc;
+    m.sel_prev = c.sel_candidates ? w->sel_prev.data : nullptr;
+    m.sel_next = c.sel_candidates ? w->sel_next.data : nullptr;
     if (!w->layers) return fail(DFLASH_E_ARG, "layers array missing");
     m.embed = w->embed.data;
     m.lm_head = w->lm_head.data;
@@ -706,6 +716,34 @@ extern "C" int dflash_sample(dflash_session* const* sessions, int32_t count, con
         if (int rc = settle_history(sessions[k])) return rc;
     return s0->ctx->engine->sample(views, row_offsets, logits, *params, ids_out, probs_out, s0->ws,
                                    s0->ws_sessions, s0->stream);
+}
+
+extern "C" int dflash_select(dflash_session* const* sessions, int32_t count, const int32_t* row_offsets,
+                             const float* logits, const int32_t* current, const dflash_select_params* params,
+                             int32_t* tokens_out, int32_t* cand_ids_out, float* cand_probs_out,
+                             float* dense_probs_out) {
+    if (!sessions || count <= 0 || !row_offsets || !logits || !current || !params || !tokens_out || !cand_ids_out)
+        return fail(DFLASH_E_ARG, "null argument");
+    dflash_session* s0 = sessions[0];
+    if (!s0) return fail(DFLASH_E_ARG, "null session");
+    const dflash_config& c = s0->ctx->model.cfg;
+    if (!c.sel_candidates) return fail(DFLASH_E_STATE, "the drafter has no selector (sel_candidates = 0)");
+    if (count > s0->ws_sessions) return fail(DFLASH_E_CAPACITY, "more sessions than the workspace serves");
+    if (!(params->temperature >= 0.f) || params->round < 0) return fail(DFLASH_E_ARG, "selector parameters out of range");
+    if (row_offsets[0] != 0) return fail(DFLASH_E_ARG, "row_offsets[0] must be 0");
+    std::vector<SessView> views(count);
+    for (int32_t k = 0; k < count; ++k) {
+        dflash_session* s = sessions[k];
+        if (!s || s->ctx != s0->ctx || s->ws != s0->ws || s->stream != s0->stream)
+            return fail(DFLASH_E_ARG, "sessions must share context, workspace and stream");
+        if (row_offsets[k + 1] < row_offsets[k] || row_offsets[k + 1] - row_offsets[k] > c.block_size - 1)
+            return fail(DFLASH_E_ARG, "row_offsets must be non-decreasing with at most blockSize-1 rows per session");
+        if (current[k] < 0 || current[k] >= c.vocab) return fail(DFLASH_E_ARG, "anchor token outside the vocabulary");
+        views[k] = s->view();
+    }
+    if (row_offsets[count] == 0) return 0;
+    return s0->ctx->engine->select(views, row_offsets, logits, current, *params, tokens_out, cand_ids_out,
+                                   cand_probs_out, dense_probs_out, s0->ws, s0->ws_sessions, s0->stream);
 }
 
 // Checks shared by dflash_verify and dflash_verify_noalloc; fills the views.

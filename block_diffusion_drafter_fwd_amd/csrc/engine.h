@@ -27,6 +27,7 @@ struct LayerW {
 struct Model {
     dflash_config cfg;
     const void *embed, *lm_head, *fc, *hidden_norm, *norm, *aux_norms;
+    const void *sel_prev, *sel_next;     // DFlash2 selector tables [V, Ds] (sel_candidates > 0)
     LayerW layer[kMaxLayers];
     int qd, kd, fc_in;              // Hq*D, Hkv*D, taps*Ht
     size_t elem;                    // bytes per element of weights, cache and features
@@ -119,6 +120,9 @@ public:
     virtual int verify(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
                        const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
                        int32_t* accepted, int32_t* next, void* ws, int32_t ws_sessions, void* stream) = 0;
+    virtual int select(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
+                       const int32_t* current, const dflash_select_params& p, int32_t* tokens, int32_t* cand_ids,
+                       float* cand_probs, float* dense, void* ws, int32_t ws_sessions, void* stream) = 0;
     // verify with the backend's own static scratch instead of a workspace
     virtual int verify_scratch(const std::vector<SessView>& sess, const int32_t* draft_offsets,
                                const float* target, const int32_t* draft_ids, const float* draft_probs,

@@ -81,7 +81,7 @@ struct WsLayout {
     size_t tables;
     size_t ctx_stage, ctx_fc, ctx_c, ctx_x, ctx_kv;
     size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_part, blk_mlp, blk_act;
-    size_t attn_o, attn_ml, part, bitmap, stats, stats2;
+    size_t attn_o, attn_ml, part, bitmap, stats, stats2, sel;
     size_t total;
     int32_t r_ctx, r_blk, items_cap, nchunk_max, blk_slices;
 };
@@ -133,6 +133,7 @@ public:
         w.bitmap = put(4 * (size_t)ms * ((c.vocab + 31) / 32));
         w.stats = put(16 * (size_t)w.r_blk * w.nchunk_max);
         w.stats2 = put(16 * (size_t)w.r_blk * w.nchunk_max);   // verification's second pass
+        w.sel = put(c.sel_candidates ? 8 * (size_t)kSelMaxK * w.r_blk * w.nchunk_max : 0);
         w.total = o;
         return w;
     }
@@ -216,6 +217,9 @@ public:
     int verify_scratch(const std::vector<SessView>& sess, const int32_t* draft_offsets, const float* target,
                        const int32_t* draft_ids, const float* draft_probs, const dflash_verify_params& p,
                        int32_t* accepted, int32_t* next, void* stream) override;
+    int select(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
+               const int32_t* current, const dflash_select_params& p, int32_t* tokens, int32_t* cand_ids,
+               float* cand_probs, float* dense, void* ws, int32_t ws_sessions, void* stream) override;
 
     int cache_read(const SessView& s, int32_t layer, int32_t pos0, int32_t count, float* k_out, float* v_out,
                    void* stream) override {
@@ -859,6 +863,50 @@ int HipEngine::verify_in(const std::vector<SessView>& sess, const int32_t* draft
     a.round = p.round;
     a.temperature = p.temperature;
     HIP_OK(kern::verify(a, st));
+    return 0;
+}
+
+int HipEngine::select(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
+                      const int32_t* current, const dflash_select_params& p, int32_t* tokens, int32_t* cand_ids,
+                      float* cand_probs, float* dense, void* ws, int32_t ws_sessions, void* stream) {
+    const dflash_config& c = m_.cfg;
+    const WsLayout w = layout(ws_sessions);
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const int32_t count = (int32_t)sess.size();
+    const int32_t R = row_offsets[count];
+    if (R > w.r_blk) return fail(DFLASH_E_CAPACITY, "selected rows exceed the workspace");
+    std::vector<SeqDesc> descs(count);
+    for (int32_t k = 0; k < count; ++k) descs[k] = desc_of(sess[k]);
+    Tables tb;
+    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+    const size_t o_offs = tb.add(row_offsets, sizeof(int32_t) * (size_t)(count + 1));
+    const size_t o_anch = tb.add(current, sizeof(int32_t) * (size_t)count);
+    char* tab = base + w.tables;
+    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+    SelectArgs a{};
+    a.logits = logits;
+    a.P = m_.sel_prev;
+    a.Q = m_.sel_next;
+    a.seqs = (const SeqDesc*)(tab + o_desc);
+    a.offs = (const int32_t*)(tab + o_offs);
+    a.anchors = (const int32_t*)(tab + o_anch);
+    a.cand = (float*)(base + w.sel);
+    a.tokens = tokens;
+    a.cand_ids = cand_ids;
+    a.cand_probs = cand_probs;
+    a.dense = p.temperature > 0.f ? dense : nullptr;
+    a.V = c.vocab;
+    a.R = R;
+    a.nseq = count;
+    a.K = c.sel_candidates;
+    a.Ds = c.sel_dim;
+    a.chunk = kSampleChunk;
+    a.nchunk = w.nchunk_max;
+    a.round = p.round;
+    a.w_bf16 = bf16();
+    a.temperature = p.temperature;
+    HIP_OK(kern::select(a, st));
     return 0;
 }
 

@@ -68,6 +68,16 @@ public:
                  std::to_string(sess.size()) + " round=" + std::to_string(p.round));
         return 0;
     }
+    int select(const std::vector<SessView>& sess, const int32_t* row_offsets, const float*, const int32_t* current,
+               const dflash_select_params& p, int32_t*, int32_t*, float*, float* dense, void*, int32_t,
+               void*) override {
+        if (int rc = injected()) return rc;
+        std::string s = "select rows=" + std::to_string(row_offsets[sess.size()]) +
+                        " round=" + std::to_string(p.round) + " dense=" + std::to_string(dense != nullptr) + " anchors=";
+        for (size_t k = 0; k < sess.size(); ++k) s += (k ? "," : "") + std::to_string(current[k]);
+        log_line(s);
+        return 0;
+    }
     int verify_scratch(const std::vector<SessView>& sess, const int32_t* offs, const float*, const int32_t*,
                        const float*, const dflash_verify_params& p, int32_t*, int32_t*, void*) override {
         if (int rc = injected()) return rc;

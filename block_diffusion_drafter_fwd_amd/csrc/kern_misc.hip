@@ -1,6 +1,7 @@
 // Row-wise kernels of the drafter forward: RMSNorm, the per-head q/k norm +
 // RoPE + slot-indexed K/V cache writer, embedding gather, descriptor upload,
 // row gather, cache readback, and the batched sampler.
+#include <climits>
 #include <cmath>
 
 #include "kernels.h"
@@ -820,6 +821,197 @@ __global__ __launch_bounds__(64) void k_verify_final(VerifyArgs a) {
         a.accepted[k] = acc;
         a.next[k] = s.idx;
     }
+}
+
+// ---------------------------------------------------------------------------
+// DFlash2 candidate selector.  Pass 1, per (row, 4096-token chunk): the
+// chunk's K best logits (value descending, id ascending), by K rounds of a
+// workgroup argmax over the 16 values each thread holds; with dense output
+// the chunk of the row's dense distribution is zeroed on the way.  Pass 2,
+// one wave per session, its rows in order: merge the chunks' candidates into
+// the row's K best, score candidate c by z(c) + <P[prev], Q[c]> (prev: the
+// anchor, then the token chosen at the row before), softmax over the K
+// candidates at temperature T and a Gumbel-max draw (u of rank j from
+// Philox4x64-10 counter (j div 4, position, round, 3), word j mod 4), or the
+// best score when T = 0; the choice is the next row's prev.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+}
+
+template <bool DENSE>
+__global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+    const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
+    const float* z = a.logits + (size_t)r * a.V;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = t_lo + tid + 256 * j;
+        v[j] = t < t_hi ? z[t] : -INFINITY;
+        if (DENSE && t < t_hi) a.dense[(size_t)r * a.V + t] = 0.f;
+    }
+    for (int k = 0; k < a.K; ++k) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)                     // ids ascend with j: ties keep the lower id
+            if (v[j] > bv) {
+                bv = v[j];
+                bi = t_lo + tid + 256 * j;
+            }
+        wave_best(bv, bi);
+        if ((tid & 63) == 0) {
+            sv[wave] = bv;
+            si[wave] = bi;
+        }
+        __syncthreads();
+        float wv = sv[0];
+        int wi = si[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (better(sv[w], si[w], wv, wi)) {
+                wv = sv[w];
+                wi = si[w];
+            }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (wi == t_lo + tid + 256 * j) v[j] = -INFINITY;
+        if (tid == 0) {
+            float* o = a.cand + (((size_t)r * a.nchunk + c) * kSelMaxK + k) * 2;
+            o[0] = wv;
+            o[1] = __int_as_float(wi);
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) void k_sel_walk(SelectArgs a) {
+    const int k = blockIdx.x, lane = threadIdx.x;
+    const SeqDesc sd = a.seqs[k];
+    const int r0 = a.offs[k], n = a.offs[k + 1] - r0;
+    const int E = a.nchunk * a.K;                        // <= kSelMaxEntries: 16 entries per lane
+    const float inv_t = a.temperature > 0.f ? 1.f / a.temperature : 0.f;
+    int prev = a.anchors[k];
+    for (int i = 0; i < n; ++i) {
+        const int r = r0 + i;
+        const float* ent = a.cand + (size_t)r * a.nchunk * kSelMaxK * 2;
+        float ev[16];
+        int ei[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = lane + 64 * u;
+            if (e < E) {
+                const float* o = ent + ((size_t)(e / a.K) * kSelMaxK + e % a.K) * 2;
+                ev[u] = o[0];
+                ei[u] = __float_as_int(o[1]);
+            } else {
+                ev[u] = -INFINITY;
+                ei[u] = INT_MAX;
+            }
+        }
+        // the row's K best, rank j held by lane j
+        int cid = INT_MAX;
+        float cz = -INFINITY;
+        for (int j = 0; j < a.K; ++j) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (better(ev[u], ei[u], bv, bi)) {
+                    bv = ev[u];
+                    bi = ei[u];
+                }
+            wave_best(bv, bi);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (ei[u] == bi) {
+                    ev[u] = -INFINITY;
+                    ei[u] = INT_MAX;
+                }
+            if (lane == j) {
+                cid = bi;
+                cz = bv;
+            }
+        }
+        // bigram scores <P[prev], Q[c]>: lanes over the Ds dimensions, one
+        // sum per candidate
+        float acc[kSelMaxK];
+#pragma unroll
+        for (int j = 0; j < kSelMaxK; ++j) acc[j] = 0.f;
+        for (int d = lane; d < a.Ds; d += 64) {
+            const float pd = ld_any(a.P, (size_t)prev * a.Ds + d, a.w_bf16);
+#pragma unroll
+            for (int j = 0; j < kSelMaxK; ++j) {
+                const int cj = __shfl(cid, j);
+                if (j < a.K) acc[j] += pd * ld_any(a.Q, (size_t)cj * a.Ds + d, a.w_bf16);
+            }
+        }
+        float s = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kSelMaxK; ++j) {
+            float t = acc[j];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+            if (lane == j && j < a.K) s = cz + t;
+        }
+        float key = s, prob = 0.f;
+        if (a.temperature > 0.f) {
+            const float x = lane < a.K ? s * inv_t : -INFINITY;
+            float m = x;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+            const float e = lane < a.K ? __expf(x - m) : 0.f;
+            float sum = e;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+            prob = e / sum;
+            uint64_t w[4] = {(uint64_t)(lane >> 2), (uint64_t)(i + 1), (uint64_t)a.round, 3};
+            philox4x64_10(w, sd.seed, sd.stream);
+            const uint64_t wj = (lane & 3) == 0 ? w[0] : (lane & 3) == 1 ? w[1] : (lane & 3) == 2 ? w[2] : w[3];
+            key = lane < a.K ? x - logf(-logf(u23(wj))) : -INFINITY;
+        } else if (lane >= a.K) {
+            key = -INFINITY;
+        }
+        float bk = key;
+        int br = lane < a.K ? lane : INT_MAX;
+        wave_best(bk, br);                               // ties: the lower rank
+        const int tok = __shfl(cid, br);
+        if (lane < a.K) {
+            a.cand_ids[(size_t)r * a.K + lane] = cid;
+            if (a.cand_probs && a.temperature > 0.f) a.cand_probs[(size_t)r * a.K + lane] = prob;
+            if (a.dense && a.temperature > 0.f) a.dense[(size_t)r * a.V + cid] = prob;
+        }
+        if (lane == 0) a.tokens[r] = tok;
+        prev = tok;
+    }
+}
+
+hipError_t select(const SelectArgs& a, hipStream_t st) {
+    if (a.R <= 0 || a.nseq <= 0) return hipSuccess;
+    if (a.K < 1 || a.K > kSelMaxK || a.nchunk * a.K > kSelMaxEntries || a.chunk != 4096 || !a.seqs || !a.offs ||
+        !a.anchors)
+        return hipErrorInvalidValue;
+    if (a.dense) hipLaunchKernelGGL(k_sel_topk<true>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_sel_topk<false>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sel_walk, dim3(a.nseq), dim3(64), 0, st, a);
+    return hipGetLastError();
 }
 
 template <bool ONE>

@@ -183,6 +183,27 @@ struct VerifyArgs {
     SeqDesc seq0;             // its descriptor (no tables)
 };
 
+// DFlash2 candidate selector: per (row, 4096-token chunk) the chunk's top-K,
+// then per session a walk over its rows in order (merge to the row's top-K,
+// bigram scores against the previous choice, softmax / Gumbel-max).
+constexpr int kSelMaxK = 16;            // candidates per row, at most
+constexpr int kSelMaxEntries = 1024;    // chunk candidates merged per row (nchunk * K), at most
+struct SelectArgs {
+    const float* logits;      // [R][V]
+    const void* P;            // [V][Ds] predecessor table (bf16 or fp32)
+    const void* Q;            // [V][Ds] candidate table
+    const SeqDesc* seqs;      // [nseq]: seed, stream
+    const int32_t* offs;      // [nseq + 1] row offsets
+    const int32_t* anchors;   // [nseq]
+    float* cand;              // [R][nchunk][kSelMaxK][2]: chunk top-K (value, id bits)
+    int32_t* tokens;          // [R]
+    int32_t* cand_ids;        // [R][K]
+    float* cand_probs;        // [R][K] or null
+    float* dense;             // [R][V] or null: zeroed, then the candidates' probabilities
+    int32_t V, R, nseq, K, Ds, chunk, nchunk, round, w_bf16, pad;
+    float temperature;
+};
+
 struct UploadArgs {
     uint32_t* dst;
     int32_t nwords, pad;
@@ -231,6 +252,7 @@ hipError_t embed(const EmbedArgs& a, hipStream_t st);
 hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st, int part = 0);
 hipError_t sample(const SampleArgs& a, hipStream_t st);
 hipError_t verify(const VerifyArgs& a, hipStream_t st);
+hipError_t select(const SelectArgs& a, hipStream_t st);
 hipError_t gather_rows(void* dst, const uint64_t* src_ptrs, int32_t rows, size_t row_bytes, hipStream_t st);
 hipError_t upload(void* dst, const void* host, size_t bytes, hipStream_t st);
 // count <= kCommitTokens tokens to hist, then bytes from src to dst; returns

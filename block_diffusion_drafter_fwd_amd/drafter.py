@@ -19,6 +19,7 @@ from .abi import check
 
 _CFG_INT_FIELDS = ("hidden", "layers", "q_heads", "kv_heads", "head_dim", "taps", "target_hidden", "vocab",
                    "block_size", "mask_id", "window", "intermediate", "flush_rows")
+_CFG_OPT_FIELDS = ("sel_candidates", "sel_dim")
 _CFG_FLAG_FIELDS = ("causal", "qk_norm", "gate", "aux_norms", "ctx_input_norm", "fused_qkv", "attention_bias")
 
 
@@ -31,6 +32,8 @@ def make_config(cfg) -> abi.Config:
         setattr(c, n, int(getattr(cfg, n)))
     for n in _CFG_FLAG_FIELDS:
         setattr(c, n, int(bool(getattr(cfg, n, False))))
+    for n in _CFG_OPT_FIELDS:
+        setattr(c, n, int(getattr(cfg, n, 0)))
     c.rope_theta = float(cfg.rope_theta)
     c.rms_eps = float(cfg.rms_eps)
     return c
@@ -69,7 +72,7 @@ class Drafter:
         self._weights = weights
         self._c = make_config(cfg)
         W = abi.Weights()
-        for n in ("embed", "lm_head", "fc", "hidden_norm", "norm", "aux_norms"):
+        for n in ("embed", "lm_head", "fc", "hidden_norm", "norm", "aux_norms", "sel_prev", "sel_next"):
             setattr(W, n, _tensor(weights.get(n)))
         L = self._c.layers
         self._layers = (abi.LayerWeights * L)()
@@ -249,6 +252,34 @@ def verify(sessions: Sequence[Session], draft_offsets: Sequence[int], target_log
                                      draft_probs.data_ptr() if draft_probs is not None else None,
                                      byref(p), acc.data_ptr(), nxt.data_ptr()))
     return acc, nxt
+
+
+def select(sessions: Sequence[Session], row_offsets: Sequence[int], logits: torch.Tensor, current: Sequence[int],
+           temperature: float, round: int = 0, dense: bool = False):
+    """dflash_select (the DFlash2 candidate selector): per session, its rows'
+    tokens chosen in order, each conditioned on the one before (the anchor
+    first), with the candidates and their probabilities.  Returns (tokens
+    [R], candidate ids [R, K], candidate probabilities [R, K] or None, dense
+    probability rows [R, V] or None)."""
+    d = sessions[0].d
+    n = len(sessions)
+    K = d._c.sel_candidates
+    R = int(row_offsets[n])
+    tok = torch.empty((max(R, 1),), dtype=torch.int32, device=d.device)
+    cid = torch.empty((max(R, 1), max(K, 1)), dtype=torch.int32, device=d.device)
+    cpr = torch.empty((max(R, 1), max(K, 1)), dtype=torch.float32, device=d.device) if temperature > 0 else None
+    den = torch.empty((max(R, 1), d._c.vocab), dtype=torch.float32, device=d.device) if dense and temperature > 0 \
+        else None
+    if not logits.is_contiguous() or logits.dtype != torch.float32 or logits.device.type != "cuda":
+        raise ValueError("logits: contiguous fp32 device tensor [R, V]")
+    hs = (c_void_p * n)(*[s.h for s in sessions])
+    offs = (c_int32 * (n + 1))(*[int(x) for x in row_offsets])
+    cur = (c_int32 * n)(*[int(x) for x in current])
+    p = abi.SelectParams(float(temperature), int(round))
+    check(d.lib, d.lib.dflash_select(hs, n, offs, logits.data_ptr(), cur, byref(p), tok.data_ptr(), cid.data_ptr(),
+                                     cpr.data_ptr() if cpr is not None else None,
+                                     den.data_ptr() if den is not None else None))
+    return tok[:R], cid[:R], (cpr[:R] if cpr is not None else None), (den[:R] if den is not None else None)
 
 
 def verify_noalloc(sessions: Sequence[Session], draft_offsets: Sequence[int], target_logits: torch.Tensor,

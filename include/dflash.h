@@ -101,6 +101,8 @@ typedef struct {
     int32_t flush_rows;      /* pending bound; in [1, 4096] */
     float rope_theta;        /* RoPE base */
     float rms_eps;           /* RMSNorm epsilon */
+    int32_t sel_candidates;  /* DFlash2 selector: candidates per drafted row K (0: no selector; 1..16) */
+    int32_t sel_dim;         /* DFlash2 selector: width Ds of its two token tables (1..256) */
 } dflash_config;
 
 /* One weight: device pointer plus its shape (ndim 1 or 2). */
@@ -130,6 +132,8 @@ typedef struct {
     dflash_tensor norm;         /* [H], final norm before the unembedding */
     dflash_tensor aux_norms;    /* [taps, Ht] (aux_norms) */
     const dflash_layer_weights* layers;  /* host array of `layers` entries, copied */
+    dflash_tensor sel_prev;     /* [V, Ds] selector table of the predecessor (sel_candidates > 0) */
+    dflash_tensor sel_next;     /* [V, Ds] selector table of the candidate (sel_candidates > 0) */
 } dflash_weights;
 
 /* Sampler settings of one dflash_sample call.  temperature 0 is greedy
@@ -142,6 +146,13 @@ typedef struct {
     int32_t history;
     int32_t round;           /* Philox counter field: one value per round */
 } dflash_sample_params;
+
+/* Selector settings of one dflash_select call (temperature only, no
+ * penalties: the DFlash2 draft samples with the request's temperature). */
+typedef struct {
+    float temperature;       /* 0: the best-scoring candidate */
+    int32_t round;           /* Philox counter field: one value per round */
+} dflash_select_params;
 
 /* Verification settings of one dflash_verify call. */
 typedef struct {
@@ -266,6 +277,31 @@ int dflash_propose_batch(dflash_session* const* sessions, int32_t count, const i
 int dflash_sample(dflash_session* const* sessions, int32_t count, const int32_t* row_offsets,
                   const float* logits, const dflash_sample_params* params, int32_t* ids_out,
                   float* probs_out);
+
+/* DFlash2 candidate selector (Ollama dflash.go selectBlock, BlockSelector
+ * branch; DFlash2 commit note: the selector proposes each token conditioned
+ * on its predecessor and returns each position's candidate distribution,
+ * which verification uses to keep the output exact).  Rows [row_offsets[k],
+ * row_offsets[k+1]) of logits (device fp32 [R, V], as dflash_propose returns
+ * them) are session k's drafted rows 1..n_k and current[k] (host) its anchor.
+ * Position i's candidates are the K = sel_candidates highest logits of its
+ * row (ties to the lower id), ranked by logit; candidate c scores
+ * s_i(c) = z_i(c) + <sel_prev[t_{i-1}], sel_next[c]> with t_0 the anchor and
+ * t_{i-1} the token chosen at position i-1 (so the positions are chosen in
+ * order); the position's distribution is softmax over its candidates of
+ * s_i / T, and the token is the Gumbel-max draw (u of candidate rank j: top
+ * 23 bits of word j mod 4 of Philox4x64-10 at counter (j div 4, i, round, 3)
+ * under the session's (seed, stream_id), plus 1/2, times 2^-23), or the best
+ * score when T = 0 (the lower rank on a tie).  Outputs (device): tokens_out
+ * int32 [R]; cand_ids_out int32 [R, K]; cand_probs_out fp32 [R, K] (T > 0;
+ * may be NULL); dense_probs_out fp32 [R, V] or NULL: the candidate
+ * distribution as full rows, zero off the candidates, in the form
+ * dflash_verify takes as draft probabilities (T > 0).  Session state is not
+ * touched.  Sessions share context, workspace and stream.  Errors: E_ARG,
+ * E_STATE (the drafter has no selector), E_CAPACITY. */
+int dflash_select(dflash_session* const* sessions, int32_t count, const int32_t* row_offsets, const float* logits,
+                  const int32_t* current, const dflash_select_params* params, int32_t* tokens_out,
+                  int32_t* cand_ids_out, float* cand_probs_out, float* dense_probs_out);
 
 /* Speculative verification of drafted blocks against the target's logits
  * (the round loop's check of a draft; Ollama dflash.go propose: verification

@@ -76,6 +76,8 @@ class DraftConfig:
     flush_rows: int = 256
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
+    sel_candidates: int = 0        # DFlash2 selector: candidates per drafted row (0: none)
+    sel_dim: int = 0               # DFlash2 selector: width of its two token tables
 
     @property
     def mask_id(self) -> int:
@@ -177,6 +179,8 @@ def weight_specs(cfg: DraftConfig) -> List[Tuple[str, Tuple[int, ...], str]]:
     ]
     if cfg.aux_norms:
         specs.append(("aux_norms", (cfg.taps, cfg.target_hidden), "gain"))
+    if cfg.sel_candidates:
+        specs += [("sel_prev", (cfg.vocab, cfg.sel_dim), "normal"), ("sel_next", (cfg.vocab, cfg.sel_dim), "normal")]
     for l in range(cfg.layers):
         p = f"layers.{l}."
         specs += [(p + "input_layernorm", (H,), "gain"),

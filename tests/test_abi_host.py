@@ -611,3 +611,51 @@ def test_device_failure_leaves_host_state_unchanged(host):
             assert _sampled_window(lines, ring) == ref_windows[k], (k, fail_at)
     assert injected >= len(SCRIPT)
     host.dflash_destroy(ctx)
+
+
+# --------------------------------------------------------------------------
+# DFlash2 selector arguments
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k,ds", [(17, 8), (-1, 8), (33, 8), (4, 0), (4, 257)])
+def test_selector_config_bounds(host, k, ds):
+    """K in 1..min(16, V), Ds in 1..256 (the 32-token vocabulary of the fake
+    model bounds K too)."""
+    fm = FakeModel(host, sel_candidates=k, sel_dim=ds)
+    assert fm.create()[0] == abi.E_CONFIG, (k, ds)
+
+
+def test_selector_tables_and_state(host):
+    fm = FakeModel(host, sel_candidates=4, sel_dim=8)
+    rc, _ = fm.create()                                   # tables missing
+    assert rc == abi.E_SHAPE and b"sel_prev" in host.dflash_last_error()
+    fm.W.sel_prev = fm.t(32, 8)
+    fm.W.sel_next = fm.t(32, 7)
+    assert fm.create()[0] == abi.E_SHAPE and b"sel_next" in host.dflash_last_error()
+    fm.W.sel_next = fm.t(32, 8)
+    rc, ctx = fm.create()
+    assert rc == 0, host.dflash_last_error()
+    s = HostSession(host, ctx)
+    out = np.zeros(64, dtype=np.int32)
+    offs = (c_int32 * 2)(0, 3)
+    cur = (c_int32 * 1)(5)
+    hs = (c_void_p * 1)(s.h)
+    p = abi.SelectParams(0.5, 2)
+    _trace(host)
+    rc = host.dflash_select(hs, 1, offs, out.ctypes.data, cur, byref(p), out.ctypes.data, out.ctypes.data,
+                            out.ctypes.data, out.ctypes.data)
+    assert rc == 0 and _trace(host) == ["select rows=3 round=2 dense=1 anchors=5"]
+    bad = (c_int32 * 1)(32)                                # anchor outside the vocabulary
+    assert host.dflash_select(hs, 1, offs, out.ctypes.data, bad, byref(p), out.ctypes.data, out.ctypes.data,
+                              None, None) == abi.E_ARG
+    many = (c_int32 * 2)(0, 8)                             # more rows than blockSize - 1
+    assert host.dflash_select(hs, 1, many, out.ctypes.data, cur, byref(p), out.ctypes.data, out.ctypes.data,
+                              None, None) == abi.E_ARG
+    host.dflash_destroy(ctx)
+    plain = FakeModel(host)                                # no selector configured
+    rc, ctx2 = plain.create()
+    s2 = HostSession(host, ctx2)
+    hs2 = (c_void_p * 1)(s2.h)
+    assert host.dflash_select(hs2, 1, offs, out.ctypes.data, cur, byref(p), out.ctypes.data, out.ctypes.data,
+                              None, None) == abi.E_STATE
+    host.dflash_destroy(ctx2)
