@@ -387,6 +387,14 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
 
     sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
     spec = None if args.no_spec_loop else spec_loop(s, cfg, wl, pool, n, state["current"], logits, torch, np)
+    policy = None
+    if sweep:
+        v_ms = kernels["verify"]["avg_launch_us"] / 1e3 if "verify" in kernels else 0.0
+        policy = width_policy_compare(sweep["fixed_ms"], sweep["per_row_ms"], v_ms, n, np)
+        if spec and not args.no_spec_loop:
+            pol = width_policy_object(n, sweep["fixed_ms"], sweep["per_row_ms"], v_ms, 0.0)
+            spec["adaptive"] = spec_loop(s, cfg, wl, pool, n, spec_state_current(s), logits, torch, np,
+                                         policy=pol)
 
     return {
         "metric": "drafted blocks/s + flushed ctx rows/s at 1 GPU; % HBM / MFMA peak",
@@ -412,10 +420,58 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
         "kernels": kernels,
         **({"width_sweep": sweep} if sweep else {}),
         **({"spec_round": spec} if spec else {}),
+        **({"width_policy": policy} if policy else {}),
     }
 
 
-def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8, agree=0.7, boost=10.0):
+def spec_state_current(s):
+    """An anchor for a fresh closed loop (any token works: the loop's rounds
+    commit whatever the anchor is)."""
+    return 5
+
+
+def width_policy_object(max_width, draft_fixed, draft_per_row, verify_fixed, verify_per_row):
+    from block_diffusion_drafter_fwd_amd.drafter import WidthPolicy
+    return WidthPolicy(max_width, draft_fixed, draft_per_row, verify_fixed, verify_per_row, decay=0.95)
+
+
+def width_policy_compare(draft_fixed, draft_per_row, verify_ms, max_width, np, rounds=4000):
+    """Fixed depth (the full width, DFlash2's seven on this configuration)
+    against the adaptive width controller (dflash_width_policy_*), in expected
+    emitted tokens per millisecond of round time, on a seeded acceptance
+    model: draft position j is accepted with probability alpha while every
+    earlier one was.  The round costs the measured draft time (fixed + per
+    row, from the width sweep) plus a verification cost: the measured
+    verification kernels only (the target's forward is not here), or the
+    pages' GB10 fit of a Laguna target's verify round (72 ms + 3.55 ms per
+    verified row), where verify time, not drafting, decides the width."""
+    out = []
+    for label, v_fixed, v_row in (("verification kernels only", verify_ms, 0.0),
+                                  ("GB10 target verify fit: 72 ms + 3.55 ms/row", 72.0, 3.55)):
+        for alpha in (0.5, 0.7, 0.9):
+            rng = np.random.default_rng([int(alpha * 100), int(v_fixed)])
+            res = {}
+            for pol_name in ("fixed", "adaptive"):
+                pol = width_policy_object(max_width, draft_fixed, draft_per_row, v_fixed, v_row)
+                tokens = cost = widths = 0.0
+                for _ in range(rounds):
+                    w = max_width if pol_name == "fixed" else pol.choose()
+                    a = 0
+                    while a < w and rng.random() < alpha:
+                        a += 1
+                    pol.observe(w, a)
+                    tokens += a + 1
+                    cost += draft_fixed + draft_per_row * w + v_fixed + v_row * (w + 1)
+                    widths += w
+                pol.close()
+                res[pol_name] = {"tokens_per_ms": round(tokens / cost, 5), "mean_width": round(widths / rounds, 2)}
+            out.append({"cost_model": label, "alpha": alpha, **res,
+                        "adaptive_over_fixed": round(res["adaptive"]["tokens_per_ms"] / res["fixed"]["tokens_per_ms"], 4)})
+    return out
+
+
+def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8, agree=0.7, boost=10.0,
+              policy=None):
     """The closed speculative round on the GPU: propose -> sample (ids and,
     when sampling, the proposal probabilities) -> verify against a seeded
     synthetic target -> rewind and commit the anchor plus the accepted
@@ -428,7 +484,8 @@ def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8
     accepted count, the next token and the drafted ids, which the commit
     needs on the host.  Reported: emitted tokens (accepted + 1) per second
     of drafting, verification and commits, the target's own forward not
-    included."""
+    included.  With `policy` (a width controller) each round drafts the
+    width it chooses and reports the round's outcome to it."""
     from block_diffusion_drafter_fwd_amd import sample, verify
     dev = logits.device
     V, T = cfg.vocab, wl.temperature
@@ -443,7 +500,8 @@ def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8
     state = {"cur": current, "acc": []}
 
     def rnd(r):
-        k, lg, _ = s.propose(state["cur"], n, logits=logits)
+        width = policy.choose() if policy is not None else n
+        k, lg, _ = s.propose(state["cur"], width, logits=logits)
         ids, probs = sample([s], [0, k], lg, T, wl.rep_penalty, wl.history, 10_000 + r, probs=T > 0)
         tgt = base[r]
         pref = torch.where(coins[r, :k], ids.long(), toks[r, :k])
@@ -457,6 +515,9 @@ def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8
         _, ft = pool.at(F, a + 1)
         s.committed(np.concatenate([[state["cur"]], out[2:2 + a]]).astype(np.int32), ft, F)
         state["cur"] = x
+        if policy is not None:
+            policy.observe(k, a)
+            state.setdefault("widths", []).append(k)
         return a
 
     for r in range(warm):
@@ -470,7 +531,9 @@ def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8
     el = time.perf_counter() - t
     gc.enable()
     acc = state["acc"]
-    return {"rounds": rounds, "width": n, "temperature": T, "target_agree": agree,
+    extra = {"mean_width": round(float(np.mean(state["widths"][warm:])), 2)} if policy is not None else {}
+    return {"rounds": rounds, "width": n if policy is None else "adaptive", **extra, "temperature": T,
+            "target_agree": agree,
             "accepted_per_round": round(float(np.mean(acc)), 3),
             "emitted_tokens_per_s": round((sum(acc) + rounds) / el, 1),
             "ms_per_round": round(el / rounds * 1e3, 4),
