@@ -284,6 +284,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
 // those weights; chunks are taken kCombItems at a time with a running merge.
 constexpr int kCombItems = 1024;
 constexpr int kCombHeads = 4;
+#ifndef DFLASH_COMB_WIDE_BELOW
+#define DFLASH_COMB_WIDE_BELOW 512
+#endif
+constexpr int kCombWideBelow = DFLASH_COMB_WIDE_BELOW;   // workgroups of the form below under which the wide form runs
 
 __global__ __launch_bounds__(32 * kCombHeads) void k_attn_combine(AttnArgs a) {
     __shared__ float sw[kCombHeads][kCombItems], sl[kCombHeads][kCombItems];
@@ -369,6 +373,81 @@ __global__ __launch_bounds__(32 * kCombHeads) void k_attn_combine(AttnArgs a) {
     }
 }
 
+// The combine for launches with few rows (one session's block): one
+// workgroup per (block row, q head), 8 groups of 32 lanes (four dims per
+// lane); group j merges items j, j + 8, ... on the fly (all its loads issued
+// together), then group 0 merges the 8 groups through LDS.  The form above
+// gives such launches only a few dozen workgroups, each walking every item.
+constexpr int kCombGroups = 8;
+
+__global__ __launch_bounds__(32 * kCombGroups) void k_attn_combine_w(AttnArgs a) {
+    __shared__ float gm[kCombGroups], gl[kCombGroups];
+    __shared__ float4 go[kCombGroups][32];
+    const int brow = blockIdx.x, hq = blockIdx.y, t = threadIdx.x, grp = t >> 5, lane = t & 31;
+    const RowInfo ri = a.rows[brow];
+    const SeqDesc sd = a.seqs[ri.seq];
+    const int G = a.Hq / a.Hkv, g = hq / G;
+    const int row = (ri.pos - sd.F) * G + hq % G;
+    const size_t stride = (size_t)a.Hkv * 64;                    // between items
+    const size_t base0 = ((size_t)sd.item0 * a.Hkv + g) * 64 + row;
+    float gv = 0.f;
+    if (a.gate && grp == 0) {
+        const float* gs = a.gate_src + (size_t)brow * a.gate_ld + a.gate_col + hq;
+        for (int sp = 0; sp < a.gate_nsplit; ++sp) gv += gs[(size_t)sp * a.gate_stride];
+    }
+    float M = -INFINITY, L = 0.f;
+    float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = grp; c0 < sd.nitems; c0 += 4 * kCombGroups) {
+        float2 ml[4];
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {                            // the group's next four items, loads first
+            const int c = min(c0 + u * kCombGroups, sd.nitems - 1);
+            const size_t b = base0 + (size_t)c * stride;
+            ml[u] = *(const float2*)&a.part_ml[b * 2];
+            v[u] = *(const float4*)(a.part_o + b * kD + 4 * lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u * kCombGroups >= sd.nitems || ml[u].x == -INFINITY) continue;
+            const float mn = fmaxf(M, ml[u].x);
+            const float so = M == -INFINITY ? 0.f : __expf(M - mn), sn = __expf(ml[u].x - mn);
+            acc = float4{acc.x * so + v[u].x * sn, acc.y * so + v[u].y * sn, acc.z * so + v[u].z * sn,
+                         acc.w * so + v[u].w * sn};
+            L = L * so + ml[u].y * sn;
+            M = mn;
+        }
+    }
+    if (lane == 0) {
+        gm[grp] = M;
+        gl[grp] = L;
+    }
+    go[grp][lane] = acc;
+    __syncthreads();
+    if (grp != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kCombGroups; ++j) Mt = fmaxf(Mt, gm[j]);
+    float Lt = 0.f;
+    float4 out = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kCombGroups; ++j) {
+        if (gm[j] == -INFINITY) continue;
+        const float w = __expf(gm[j] - Mt);
+        Lt += gl[j] * w;
+        const float4 o = go[j][lane];
+        out = float4{out.x + o.x * w, out.y + o.y * w, out.z + o.z * w, out.w + o.w * w};
+    }
+    float f = 1.f / Lt;
+    if (a.gate) f *= 1.f / (1.f + __expf(-gv));
+    const size_t o = (size_t)brow * a.Hq * kD + (size_t)hq * kD + 4 * lane;
+    if (a.out_bf16) {
+        *(uint2*)((uint16_t*)a.out + o) = uint2{pack_bf16(out.x * f, out.y * f), pack_bf16(out.z * f, out.w * f)};
+    } else {
+        *(float4*)((float*)a.out + o) = float4{out.x * f, out.y * f, out.z * f, out.w * f};
+    }
+}
+
 // fp32: one workgroup of 64 threads per (block row, q head); D <= 64
 __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     __shared__ float sq[64];
@@ -438,8 +517,12 @@ hipError_t attention(const AttnArgs& a, bool bf16, hipStream_t st, int part) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || part == 1) return e;
     }
-    hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, (a.Hq + kCombHeads - 1) / kCombHeads), dim3(32 * kCombHeads),
-                       0, st, a);
+    // few rows (one session's block): the wide form, one workgroup per (row, q head)
+    if (a.nrows * ((a.Hq + kCombHeads - 1) / kCombHeads) < kCombWideBelow)
+        hipLaunchKernelGGL(k_attn_combine_w, dim3(a.nrows, a.Hq), dim3(32 * kCombGroups), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_attn_combine, dim3(a.nrows, (a.Hq + kCombHeads - 1) / kCombHeads),
+                           dim3(32 * kCombHeads), 0, st, a);
     return hipGetLastError();
 }
 
