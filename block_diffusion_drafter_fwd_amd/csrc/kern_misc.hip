@@ -103,15 +103,18 @@ __device__ __forceinline__ void st4_any(void* p, size_t i, float4 v, int bf16) {
 // chunk are issued together, eight at a time (the latency of one L2 round
 // trip, not of one per slice), and added in slice order.
 constexpr int kNormSliceBatch = 8;
-__global__ __launch_bounds__(512) void k_rmsnorm4(NormArgs a) {
-    __shared__ float sh[8];
+// NT threads per row: 1024 when the row has more than 512 four-element
+// columns, so that every thread's loads go out in one batch
+template <int NT>
+__global__ __launch_bounds__(NT) void k_rmsnorm4(NormArgs a) {
+    __shared__ float sh[NT / 64];
     __shared__ float4 xs[kNormMaxW / 4];
     const int orow = blockIdx.x, grp = blockIdx.y;
     const int irow = a.row_src ? a.row_src[orow] : orow;
     const int W = a.width / a.groups, W4 = W >> 2;
     const size_t ibase = (size_t)irow * a.in_stride + (size_t)grp * W;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < W4; i += 512) {
+    for (int i = threadIdx.x; i < W4; i += NT) {
         float4 x = a.in ? ld4_any(a.in, ibase + 4 * i, a.in_bf16) : float4{0.f, 0.f, 0.f, 0.f};
         const float* __restrict__ p = a.part + ibase + 4 * i;
         for (int s0 = 0; s0 < a.nsplit; s0 += kNormSliceBatch) {
@@ -134,11 +137,11 @@ __global__ __launch_bounds__(512) void k_rmsnorm4(NormArgs a) {
     ss = block_sum(ss, sh);
     const float rstd = 1.f / sqrtf(ss / (float)W + a.eps);
     if (a.writeback)
-        for (int i = threadIdx.x; i < W4; i += 512) *(float4*)(a.writeback + ibase + 4 * i) = xs[i];
+        for (int i = threadIdx.x; i < W4; i += NT) *(float4*)(a.writeback + ibase + 4 * i) = xs[i];
     const size_t obase = (size_t)orow * a.out_stride + (size_t)grp * W;
     const size_t gbase = (size_t)grp * a.gain_group_stride;
     for (int o = 0; o < a.nout; ++o)
-        for (int i = threadIdx.x; i < W4; i += 512) {
+        for (int i = threadIdx.x; i < W4; i += NT) {
             const float4 gn = ld4_any(a.gain[o], gbase + 4 * i, a.gain_bf16);
             const float4 x = xs[i];
             st4_any(a.out[o], obase + 4 * i,
@@ -148,6 +151,11 @@ __global__ __launch_bounds__(512) void k_rmsnorm4(NormArgs a) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+#ifndef DFLASH_NORM_WIDE
+#define DFLASH_NORM_WIDE 1
+#endif
+constexpr bool kNormWide = DFLASH_NORM_WIDE;
+
 hipError_t rmsnorm(const NormArgs& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
     const int W = a.width / a.groups;
@@ -155,7 +163,10 @@ hipError_t rmsnorm(const NormArgs& a, hipStream_t st) {
               a.out_stride % 4 == 0 && a.gain_group_stride % 4 == 0 && aligned16(a.in) && aligned16(a.part) &&
               aligned16(a.writeback);
     for (int o = 0; o < a.nout; ++o) v4 = v4 && aligned16(a.gain[o]) && aligned16(a.out[o]);
-    if (v4) hipLaunchKernelGGL(k_rmsnorm4, dim3(a.rows, a.groups), dim3(512), 0, st, a);
+    if (v4 && W / 4 > 512 && kNormWide)
+        hipLaunchKernelGGL(k_rmsnorm4<1024>, dim3(a.rows, a.groups), dim3(1024), 0, st, a);
+    else if (v4)
+        hipLaunchKernelGGL(k_rmsnorm4<512>, dim3(a.rows, a.groups), dim3(512), 0, st, a);
     else hipLaunchKernelGGL(k_rmsnorm, dim3(a.rows, a.groups), dim3(512), 0, st, a);
     return hipGetLastError();
 }
