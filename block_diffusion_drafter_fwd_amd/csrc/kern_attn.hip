@@ -448,11 +448,13 @@ __global__ __launch_bounds__(32 * kCombGroups) void k_attn_combine_w(AttnArgs a)
     }
 }
 
-// fp32: one workgroup of 64 threads per (block row, q head); D <= 64
+// fp32: one workgroup (one wave) per (block row, q head); D <= 64.  Keys go
+// in tiles of 64, one per lane: the lane's score, the tile's maximum and sum
+// by wave reductions (online softmax), then lane d < D accumulates output
+// dimension d over the tile's values.  Every per-lane quantity is a scalar.
 __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     __shared__ float sq[64];
-    __shared__ float sm[64], sl[64];
-    __shared__ float so[64][65];
+    __shared__ float sp[64];
     const int brow = blockIdx.x, hq = blockIdx.y, t = threadIdx.x;
     const RowInfo ri = a.rows[brow];
     const SeqDesc sd = a.seqs[ri.seq];
@@ -464,42 +466,50 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     const size_t headsz = (size_t)sd.cap * D;
     const float* Kc = (const float*)sd.cache + ((size_t)(a.layer * 2 + 0) * a.Hkv + g) * headsz;
     const float* Vc = (const float*)sd.cache + ((size_t)(a.layer * 2 + 1) * a.Hkv + g) * headsz;
-    float m = -INFINITY, l = 0.f, o[64];
-    for (int d = 0; d < 64; ++d) o[d] = 0.f;
-    for (int s = sd.key_lo + t; s < kend; s += 64) {
-        if (!visible(s, p, kend, a.causal, a.window)) continue;
-        const int slot = sd.ring ? s % sd.cap : s;
-        const float* kr = Kc + (size_t)slot * D;
-        const float* vr = Vc + (size_t)slot * D;
-        float dot = 0.f;
-        for (int d = 0; d < D; ++d) dot = fmaf(sq[d], kr[d], dot);
-        dot *= a.scale;
-        const float mn = fmaxf(m, dot);
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int s0 = sd.key_lo; s0 < kend; s0 += 64) {
+        const int s = s0 + t;
+        float dot = -INFINITY;
+        if (s < kend && visible(s, p, kend, a.causal, a.window)) {
+            const float* kr = Kc + (size_t)(sd.ring ? s % sd.cap : s) * D;
+            dot = 0.f;
+            for (int d = 0; d < D; ++d) dot = fmaf(sq[d], kr[d], dot);
+            dot *= a.scale;
+        }
+        float tm = dot;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
+        const float mn = fmaxf(m, tm);
+        if (mn == -INFINITY) continue;                 // nothing visible yet (the same on every lane)
         const float al = m == -INFINITY ? 0.f : expf(m - mn);
-        const float pe = expf(dot - mn);
-        l = l * al + pe;
-        for (int d = 0; d < D; ++d) o[d] = o[d] * al + pe * vr[d];
+        const float pe = dot == -INFINITY ? 0.f : expf(dot - mn);
+        float ts = pe;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ts += __shfl_xor(ts, off);
+        l = l * al + ts;
+        sp[t] = pe;
+        __syncthreads();
+        if (t < D) {
+            float acc = o * al;
+            const int n = min(64, kend - s0);
+            for (int j = 0; j < n; ++j) {
+                const float pj = sp[j];
+                if (pj != 0.f) {
+                    const int sj = s0 + j;
+                    acc = fmaf(pj, Vc[(size_t)(sd.ring ? sj % sd.cap : sj) * D + t], acc);
+                }
+            }
+            o = acc;
+        }
         m = mn;
+        __syncthreads();
     }
-    sm[t] = m;
-    sl[t] = l;
-    for (int d = 0; d < D; ++d) so[t][d] = o[d];
-    __syncthreads();
     if (t >= D) return;
-    float M = -INFINITY;
-    for (int j = 0; j < 64; ++j) M = fmaxf(M, sm[j]);
-    float L = 0.f, acc = 0.f;
-    for (int j = 0; j < 64; ++j) {
-        if (sm[j] == -INFINITY) continue;
-        const float w = expf(sm[j] - M);
-        L += sl[j] * w;
-        acc += so[j][t] * w;
-    }
-    float out = acc / L;
+    float out = o / l;
     if (a.gate) {
         float gv = 0.f;
-        for (int sp = 0; sp < a.gate_nsplit; ++sp)
-            gv += a.gate_src[(size_t)sp * a.gate_stride + (size_t)brow * a.gate_ld + a.gate_col + hq];
+        for (int sp2 = 0; sp2 < a.gate_nsplit; ++sp2)
+            gv += a.gate_src[(size_t)sp2 * a.gate_stride + (size_t)brow * a.gate_ld + a.gate_col + hq];
         out *= 1.f / (1.f + expf(-gv));
     }
     ((float*)a.out)[(size_t)brow * a.Hq * D + (size_t)hq * D + t] = out;
