@@ -31,7 +31,10 @@ workload after the long one and reports it under ``kernels.batched``
 The JSON line carries the roofline of the dominant kernel (the one with the
 most time per round), timed with HIP events on its stream inside the timed
 region, per-stage rooflines from the same hooks (``kernels``), and the CPU
-oracle's rate on a bounded sample of the same workload.
+oracle's rate on a bounded sample of the same workload.  On the long workload
+``kernels.share_of_8`` times the attention, unembedding and sampler at one
+GPU's share of an eight-GPU split (131072 / 8 context slots, 262144 / 8
+vocabulary ids), the shapes each GPU would run if the session were sharded.
 """
 from __future__ import annotations
 
@@ -385,6 +388,8 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
                 kernels[name] = mfma_line(flops[name], avg, rows=rows, avg_launch_us=round(avg * 1e6, 2),
                                           launches=l_k, target_frac=0.5)
 
+    if not args.no_stages and wl.name == "long":
+        kernels["share_of_8"] = share_of_gpus(cfg, wl, w_dev, pool, n, torch, np, synth)
     sweep = None if args.no_width_sweep else width_sweep(s, cfg, state["current"], logits, torch, np)
     spec = None if args.no_spec_loop else spec_loop(s, cfg, wl, pool, n, state["current"], logits, torch, np)
     policy = None
@@ -538,6 +543,73 @@ def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8
             "emitted_tokens_per_s": round((sum(acc) + rounds) / el, 1),
             "ms_per_round": round(el / rounds * 1e3, 4),
             "note": "drafter + verification + commit per round; the target's forward is synthetic and not timed"}
+
+
+def share_of_gpus(cfg, wl, w_dev, pool, n, torch, np, synth, gpus=8, rounds=16):
+    """The long session's kernels at one GPU's share of a split over `gpus`
+    GPUs (context sharded by slot, vocabulary by id): the attention over
+    context / gpus slots, the unembedding and the sampler over vocab / gpus
+    ids, each timed over `rounds` rounds at the workload's width.  A drafter
+    with the first vocab / gpus rows of the embedding and lm_head stands for
+    one GPU's vocabulary shard; the layer weights are shared."""
+    from block_diffusion_drafter_fwd_amd import Drafter, sample
+
+    dev = torch.device("cuda:0")
+    V = cfg.vocab // gpus
+    ctx = wl.context // gpus
+    c = cfg.replace(vocab=V)
+    w = dict(w_dev)
+    w["embed"] = w_dev["embed"][:V]
+    w["lm_head"] = w_dev["lm_head"][:V]
+    d = Drafter(c, w)
+    st = Stage(d.lib, d.ctx)
+    B = cfg.block_size
+    stages = ("attention_partial", "attention", "unembed", "sampler")
+    s = d.session(ctx + (len(stages) + 1) * rounds * B + 64)
+    for p in range(0, ctx, wl.commit_rows):
+        tk, ft = pool.at(p, wl.commit_rows)
+        s.committed((tk % V).astype(np.int32), ft, p)
+    s.flush()
+    logits = torch.empty((B - 1, V), dtype=torch.float32, device=dev)
+    rs = synth.RoundScript(cfg, wl, 0, 0)
+    state = {"current": rs.first_anchor() % V, "r": 0, "F": []}
+
+    def step():
+        r = state["r"]
+        n_, lg, _ = s.propose(state["current"], n, logits=logits)
+        sample([s], [0, n_], lg, wl.temperature, wl.rep_penalty, wl.history, r, probs=wl.probs)
+        a = rs.accept(n)
+        s.commit_block()
+        F = s.state()[0]
+        state["F"].append(F)
+        tk, ft = pool.at(F, a + 1)
+        run = np.concatenate([[state["current"]], tk[1:a + 1] % V]).astype(np.int32)
+        s.committed(run, ft, F)
+        state["current"] = rs.bonus() % V
+        state["r"] = r + 1
+
+    for _ in range(rounds // 2):
+        step()
+    out = {"gpus": gpus, "context_slots": ctx, "vocab": V}
+    for name in stages:
+        state["F"].clear()
+        st.begin(name)
+        for _ in range(rounds):
+            step()
+        ms, launches = st.end()
+        avg = ms / 1e3 / max(1, launches)
+        vis = float(np.mean(state["F"])) + n + 1
+        if name.startswith("attention"):
+            b = int(2 * cfg.kv_heads * vis * cfg.head_dim * 2)
+        elif name == "unembed":
+            b = V * cfg.hidden * 2 + n * cfg.hidden * 2 + n * V * 4
+        else:
+            b = n * V * 4 * (2 if wl.probs and wl.temperature > 0 else 1)
+        out[name] = hbm_line(b, avg, alg_bytes_per_launch=b, avg_launch_us=round(avg * 1e6, 2), launches=launches,
+                             us_per_round=round(ms * 1e3 / rounds, 1))
+    s.close()
+    d.close()
+    return out
 
 
 def width_sweep(s, cfg, current, logits, torch, np, reps=20):
