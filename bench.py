@@ -335,7 +335,7 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
     kernels = {dom: roofline}
     stage_rounds = 16
     if not args.no_stages:
-        for name in ("unembed", "attention_partial", "attention", "sampler"):
+        for name in ("unembed", "attention_partial", "attention", "sampler", "layer_gemms"):
             if name in kernels or (name == "attention_partial" and cfg.dtype != "bf16"):
                 continue
             st.begin(name)
@@ -343,7 +343,14 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
                 step()
             ms_s, l_s = st.end()
             avg = ms_s / 1e3 / max(1, l_s)
-            if name == "sampler":
+            if name == "layer_gemms":
+                # every layer's projection weights once per round (+ the block
+                # rows' activations, negligible), over the summed launch time
+                lb = layer_weight_bytes(cfg) + (n + 1) * cfg.hidden * elem * 4 * cfg.layers
+                kernels[name] = hbm_line(lb, ms_s / 1e3 / stage_rounds, alg_bytes_per_round=lb,
+                                         launches_per_round=round(l_s / stage_rounds, 1),
+                                         us_per_round=round(ms_s * 1e3 / stage_rounds, 1))
+            elif name == "sampler":
                 sb = n * cfg.vocab * 4 * (2 if wl.probs and wl.temperature > 0 else 1)
                 kernels[name] = hbm_line(sb, avg, alg_bytes_per_launch=sb, avg_launch_us=round(avg * 1e6, 2),
                                          launches=l_s)
@@ -543,6 +550,14 @@ def spec_loop(s, cfg, wl, pool, n, current, logits, torch, np, rounds=64, warm=8
             "emitted_tokens_per_s": round((sum(acc) + rounds) / el, 1),
             "ms_per_round": round(el / rounds * 1e3, 4),
             "note": "drafter + verification + commit per round; the target's forward is synthetic and not timed"}
+
+
+def layer_weight_bytes(cfg):
+    """Bytes of every layer's projection weights (q|k|v(|g), o_proj, gate|up, down)."""
+    elem = 2 if cfg.dtype == "bf16" else 4
+    qd, kd, H, I = cfg.q_heads * cfg.head_dim, cfg.kv_heads * cfg.head_dim, cfg.hidden, cfg.intermediate
+    per = (qd + 2 * kd + (cfg.q_heads if cfg.gate else 0)) * H + H * qd + 2 * I * H + H * I
+    return per * cfg.layers * elem
 
 
 def share_of_gpus(cfg, wl, w_dev, pool, n, torch, np, synth, gpus=8, rounds=16):
@@ -746,13 +761,18 @@ def bench_batched(args, cfg, wl, w_dev, steps, warmup, torch, synth):
                     kernel="k_attn_partial (all sessions, one layer)", alg_bytes_per_launch=int(kv_bytes_layer),
                     avg_launch_us=round(avg_a * 1e6, 2), launches=l_a, us_per_round=round(ms_a * 1e3 / steps, 1))
     kernels = {"attention_partial": attn}
-    for name in ("attention", "unembed", "sampler"):
+    for name in ("attention", "unembed", "sampler", "layer_gemms"):
         st.begin(name)
         for _ in range(4):
             step()
         ms_s, l_s = st.end()
         avg = ms_s / 1e3 / max(1, l_s)
-        if name == "unembed":
+        if name == "layer_gemms":
+            # ~487 block rows: the projections are dense contractions
+            fl = 2.0 * R * layer_weight_bytes(cfg) / elem
+            kernels[name] = mfma_line(fl, ms_s / 1e3 / 4, rows=round(R, 1), launches_per_round=round(l_s / 4, 1),
+                                      us_per_round=round(ms_s * 1e3 / 4, 1), target_frac=0.5)
+        elif name == "unembed":
             kernels[name] = mfma_line(2.0 * R * cfg.hidden * cfg.vocab, avg, rows=round(R, 1),
                                       avg_launch_us=round(avg * 1e6, 2), launches=l_s, target_frac=0.5)
         elif name == "attention":

@@ -650,6 +650,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             g.seg[2] = GemmSeg{x, lw.v, H, H, kd, qd + kd, 0, 0};
             g.nseg = 3;
             if (c.gate) g.seg[g.nseg++] = GemmSeg{x, lw.g, H, H, c.q_heads, qd + 2 * kd, 0, 0};
+            Timed tg(this, "layer_gemms", st);
             HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &qkv_slices));
         }
         {
@@ -724,6 +725,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             GemmArgs g = gemm_args(R, qd, hpart, H, kPartial, part, w.blk_slices);
             g.seg[0] = GemmSeg{base + w.blk_attn, lw.o, qd, qd, H, 0, 0, 0};
             g.nseg = 1;
+            Timed tg(this, "layer_gemms", st);
             HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &o_slices));
         }
         {   // h += attention output; x = post-attention norm of h
@@ -745,6 +747,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             g.out = base + w.blk_act;        // act = silu(x W_gate^T) * (x W_up^T)
             g.ldo = I;
             g.out_bf16 = bf16();
+            Timed tg(this, "layer_gemms", st);
             HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st));
         }
         int d_slices = 1;
@@ -752,6 +755,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             GemmArgs g = gemm_args(R, I, hpart, H, kPartial, part, w.blk_slices);
             g.seg[0] = GemmSeg{base + w.blk_act, lw.down, I, I, H, 0, 0, 0};
             g.nseg = 1;
+            Timed tg(this, "layer_gemms", st);
             HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &d_slices));
         }
         {   // h += MLP output; x = next layer's input norm (the final norm after the last)

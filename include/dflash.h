@@ -383,7 +383,9 @@ int dflash_cache_read(const dflash_session* s, int32_t layer, int32_t position0,
  * bracketed by HIP events on the stream it runs on.  Stages: "unembed" (the
  * lm_head GEMM), "attention" (partials + combine), "attention_partial" (the
  * partials kernel alone, bf16), "flush_fc" and "flush_kv" (the context-path
- * GEMMs), "sampler", "verify" (one pair per dflash_verify).  dflash_profile_end waits for the
+ * GEMMs), "layer_gemms" (the block path's per-layer projections: q|k|v(|g),
+ * o_proj, gate|up, down), "sampler", "verify" (one pair per dflash_verify).
+ * dflash_profile_end waits for the
  * recorded events and returns the summed kernel time (ms) and the number of
  * launches since dflash_profile_begin.  Errors: E_ARG (unknown stage),
  * E_HIP. */
