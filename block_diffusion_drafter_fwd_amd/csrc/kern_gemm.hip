@@ -691,6 +691,109 @@ __global__ __launch_bounds__(512) void k_gemm_w8(GA a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_gemm_w8 (256 x 128 tiles, 8 waves of 64 x 64) with 64-wide k tiles:
+// every copy instruction moves whole 128-byte rows (8 rows x 128 bytes
+// instead of 16 x 64), three stages of 48 KiB, two in flight; pieces of a
+// row XOR-permuted by (row / 2) mod 8 as in k_gemm_mt.
+// ---------------------------------------------------------------------------
+constexpr int kW8KBK = 64, kW8KStage = (256 + kW8BN) * kW8KBK;
+
+template <int TAG, class GA>
+__global__ __launch_bounds__(512) void k_gemm_w8k(GA a) {
+    constexpr int BM = 256, NA = 4, NB = 2;        // copy instructions per wave per stage (A, B)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[3 * kW8KStage];
+    const TileItem it = tile_item(a.xcd_remap);
+    const int tile = it.tile, mt = it.mt, split = it.split;
+    const GemmSeg g = a.seg[find_seg(a, tile)];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave >> 1, wn = wave & 1, r = lane & 15, q = lane >> 4;
+    const int m0 = mt * BM, n0 = (tile - g.tile0) * kW8BN;
+    // lane l of a 1 KiB copy block stores position l % 8 of the block's row
+    // l / 8, holding the logical piece (l % 8) ^ swz(row); rows past M or N
+    // repeat the last one (computed, never stored)
+    const uint16_t* pa[NA];
+    const uint16_t* pb[NB];
+    {
+        const int rl = lane >> 3, pp = lane & 7;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int row = (wave * NA + i) * 8 + rl;
+            const int am = min(m0 + row, a.M - 1);
+            const int ar = a.a_rows ? a.a_rows[am] : am;
+            pa[i] = (const uint16_t*)g.A + (size_t)ar * g.lda + ((pp ^ mt_swz<kW8KBK>(row)) << 3);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int row = (wave * NB + i) * 8 + rl;
+            pb[i] = (const uint16_t*)g.B + (size_t)min(n0 + row, g.N - 1) * g.ldb + ((pp ^ mt_swz<kW8KBK>(row)) << 3);
+        }
+    }
+    const int kb = split * a.kc, ke = min(a.K, kb + a.kc);
+    const int nk = (ke - kb) / kW8KBK;
+    auto load = [&](int kt) {
+        uint16_t* st = smem + (kt % 3) * kW8KStage;
+        const int k0 = kb + min(kt, nk - 1) * kW8KBK;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) dma16(pa[i] + k0, st + (wave * NA + i) * 512);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) dma16(pb[i] + k0, st + BM * kW8KBK + (wave * NB + i) * 512);
+    };
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint32_t offA[4], offB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        offA[i] = (uint32_t)mt_off<kW8KBK>(wm * 64 + i * 16 + r, q) * 2;
+        offB[i] = (uint32_t)mt_off<kW8KBK>(BM + wn * 64 + i * 16 + r, q) * 2;
+    }
+    if (nk > 0) {
+        load(0);
+        load(1);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt landed when only stage kt + 1's copies (6 per wave) are in
+        // flight; the barrier also tells that every wave is done reading the
+        // stage of kt - 1, which the copy of kt + 2 refills
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        load(kt + 2);
+        const uint32_t base = lds_addr(smem + (kt % 3) * kW8KStage);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // piece kk * 4 + q sits at (q ^ swz) ^ (kk * 4)
+            u32x4_t af[4], bf[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = lds_read16(base + (offB[j] ^ (kk * 64)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = lds_read16(base + (offA[i] ^ (kk * 64)));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]),
+                           "+v"(bf[3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + j * 16 + r;
+            const bool nok = n < g.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * 64 + i * 16 + 4 * q + e;
+                if (nok && m < a.M) store_out(a, split, m, g.c_col0 + n, acc[i][j][e]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // 8 waves on 256 x 256 tiles (waves as 2 x 4, 128 x 64 each: the wave tile
 // of k_gemm_w8<8>).  Per 32-wide k step a workgroup copies 32 KiB (A and B
 // 16 KiB each) for the products that cost k_gemm_w8<8> 40 KiB, and these
@@ -1189,6 +1292,13 @@ static hipError_t gemm_impl(GA a, bool bf16, size_t part_cap_floats, int num_cus
         if (w8big) {
             if (tag == 1) hipLaunchKernelGGL((k_gemm_w8<1, GA, 8>), grid3, dim3(512), 0, st, a);
             else hipLaunchKernelGGL((k_gemm_w8<0, GA, 8>), grid3, dim3(512), 0, st, a);
+        } else if (w8 && kc >= 1024) {
+            // K slices of 16 or more 64-wide steps: whole 128-byte rows per
+            // copy (the long flush's fc 66.9 -> 57.9 us, k|v 40.1 -> 37.0 by
+            // events; at 8-12 steps the extra pipeline fill loses: 18.0 ->
+            // 18.8 us at 487 x 4096 -> 2048, qwen's k|v 26.6 -> 27.4)
+            if (tag == 1) hipLaunchKernelGGL((k_gemm_w8k<1, GA>), grid3, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_gemm_w8k<0, GA>), grid3, dim3(512), 0, st, a);
         } else if (w8) {
             if (tag == 1) hipLaunchKernelGGL((k_gemm_w8<1, GA, 4>), grid3, dim3(512), 0, st, a);
             else hipLaunchKernelGGL((k_gemm_w8<0, GA, 4>), grid3, dim3(512), 0, st, a);
