@@ -14,7 +14,9 @@ rows ride in the next propose's context pass), propose (pending rows ->
 context K/V; anchor + n mask rows through every layer; rows 1..n
 unembedded) and sample the rows.  value = drafted blocks/s (for the batched
 workload one block per session per batched call).  The prompt phase is timed
-separately and reported as flushed context rows/s (at least 32768 rows).
+separately and reported as flushed context rows/s (at least 32768 rows); the
+prompt is handed over 4096 rows per committed call and flushed in 256-row
+chunks (the windowed laguna prompt in flush-sized calls).
 All inputs (weights, feature rows, tokens, accept lengths) are resident on
 the device or host before the timed region, and Python's cyclic garbage
 collector is paused inside every timed region.
@@ -54,6 +56,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 POOL_ROWS = 4096
+PROMPT_CALL_ROWS = 4096   # prompt rows per committed call (POOL_ROWS: a call never straddles the pool)
 # the kernel timed live inside the timed region: the one with the most time
 # per round (the attention partials of five layers on the long workload, the
 # unembedding elsewhere)
@@ -254,9 +257,16 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
     torch.cuda.synchronize()
 
     # ---- prompt phase: flushed context rows/s (a fresh session per pass)
-    def prompt(session):
-        for p in range(0, wl.context, wl.commit_rows):
-            T = min(wl.commit_rows, wl.context - p)
+    # the prompt is handed over PROMPT_CALL_ROWS rows per committed call (the
+    # library flushes it in wl.commit_rows-row chunks, two chunks at a time
+    # on two streams); a windowed config projects only the rows its window
+    # keeps, so its prompt goes in flush-sized calls as every row is projected
+    call_rows = wl.commit_rows if cfg.window else max(wl.commit_rows, PROMPT_CALL_ROWS)
+
+    def prompt(session, rows_per_call=None):
+        step_rows = rows_per_call or call_rows
+        for p in range(0, wl.context, step_rows):
+            T = min(step_rows, wl.context - p)
             tk, ft = pool.at(p, T)
             session.committed(tk, ft, p)
         session.flush()
@@ -386,7 +396,7 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
             s2 = d.session(capacity)
             torch.cuda.synchronize()
             st.begin(name)
-            prompt(s2)
+            prompt(s2, wl.commit_rows)       # one chunk per call: each GEMM alone on the GPU
             torch.cuda.synchronize()
             ms_k, l_k = st.end()
             s2.close()
@@ -693,9 +703,10 @@ def bench_batched(args, cfg, wl, w_dev, steps, warmup, torch, synth):
     logits = torch.empty((S * (B - 1), cfg.vocab), dtype=torch.float32, device=dev)
 
     def prompt(sessions):
+        call_rows = max(wl.commit_rows, PROMPT_CALL_ROWS)
         for k, sess in enumerate(sessions):
-            for p in range(0, lens[k], wl.commit_rows):
-                T = min(wl.commit_rows, lens[k] - p)
+            for p in range(0, lens[k], call_rows):
+                T = min(call_rows, lens[k] - p)
                 tk, ft = pool.at(p, T)
                 sess.committed(tk, ft, p)
             sess.flush()

@@ -68,6 +68,10 @@ struct dflash_session {
     std::vector<int32_t> hist_shadow;
     int32_t hist_dirty = 0;
     ArenaLayout lay;
+    // the backend's second stream for the context passes of one call (lane
+    // 1), opened with the session (creating a stream costs more than a flush
+    // chunk) and closed with it; without one every pass runs on lane 0
+    void* aux = nullptr;
 
     SessView view() const {
         SessView v;
@@ -266,6 +270,7 @@ extern "C" int dflash_session_open(dflash_ctx* ctx, void* arena, size_t arena_by
     s->ctx_offset = s->cache_len = restored_offset;
     s->lay = lay;
     s->hist_shadow.assign(kHistory, 0);
+    if (ctx->engine->aux_open(&s->aux)) s->aux = nullptr;   // then every context pass on lane 0
     *out = s;
     return 0;
 }
@@ -337,10 +342,40 @@ static void commit_block(dflash_session* s) {
     s->outstanding = false;
 }
 
+// Joins the session's second stream back into its own stream when a call
+// that forked it returns (on every path, errors included).
+class AuxJoin {
+public:
+    explicit AuxJoin(dflash_session* s) : s_(s) {}
+    int fork() {
+        if (forked_) return 0;
+        if (int rc = s_->ctx->engine->aux_fork(s_->aux, s_->stream)) return rc;
+        forked_ = true;
+        return 0;
+    }
+    bool forked() const { return forked_; }
+    int join() {
+        if (!forked_) return 0;
+        forked_ = false;
+        return s_->ctx->engine->aux_join(s_->aux, s_->stream);
+    }
+    ~AuxJoin() { (void)join(); }
+
+private:
+    dflash_session* s_;
+    bool forked_ = false;
+};
+
 // Write the pending rows plus `extra_rows` more rows from `extra` (device,
 // contiguous) to the cache and advance ctxOffset past all of them.  Rows pass
 // through the pending buffer in chunks of at most flush_rows; on a windowed
 // config only rows at or above frontier - (window - 1) are projected.
+// Chunks are independent (a context row depends only on its own features
+// and position): every second chunk read straight from the caller's rows
+// goes to the session's second stream with the workspace's second set of
+// context buffers, so consecutive chunks overlap; that stream is forked from
+// the session's stream before its first chunk and joined back before the
+// call returns, so the call's work stays ordered with the session's stream.
 static int write_context(dflash_session* s, const char* extra, int32_t extra_rows) {
     dflash_ctx* ctx = s->ctx;
     const dflash_config& c = ctx->model.cfg;
@@ -354,6 +389,10 @@ static int write_context(dflash_session* s, const char* extra, int32_t extra_row
     int32_t pos = s->ctx_offset;       // position of buffer row 0
     int32_t used = 0;                  // extra rows consumed
     int64_t written = 0;
+    int32_t chunk = 0;                 // chunks projected so far
+    AuxJoin aux(s);
+    if (extra && total > c.flush_rows && ctx->engine->aux_stream(s->aux))   // two chunks or more
+        if (int rc = aux.fork()) return rc;
     while (true) {
         int32_t take = std::min(c.flush_rows - in_buf, extra_rows - used);
         int32_t rows = in_buf + take;
@@ -375,15 +414,19 @@ static int write_context(dflash_session* s, const char* extra, int32_t extra_row
             }
             const char* src = from_caller ? direct : s->pending_buf() + (size_t)first * rb;
             std::vector<CtxSeg> segs{{0, src, rows - first, pos + first}};
-            int rc = ctx->engine->ctx_forward(views, segs, s->ws, s->ws_sessions, s->stream);
+            const int lane = (chunk & 1) && from_caller && aux.forked() ? 1 : 0;
+            int rc = ctx->engine->ctx_forward(views, segs, s->ws, s->ws_sessions,
+                                              lane ? ctx->engine->aux_stream(s->aux) : s->stream, lane);
             if (rc) return rc;
             written += rows - first;
+            ++chunk;
         }
         used += take;
         pos += rows;
         in_buf = 0;
         if (used >= extra_rows) break;
     }
+    if (int rc = aux.join()) return rc;
     s->rows_written += written;
     s->ctx_offset = frontier;
     s->pending = 0;
@@ -578,7 +621,7 @@ extern "C" int dflash_flush_batch(dflash_session* const* ss, int32_t count) {
         kept[k] = P - first;
     }
     if (!segs.empty()) {
-        int rc = ctx->engine->ctx_forward(views, segs, ss[0]->ws, ss[0]->ws_sessions, ss[0]->stream);
+        int rc = ctx->engine->ctx_forward(views, segs, ss[0]->ws, ss[0]->ws_sessions, ss[0]->stream, 0);
         if (rc) return guard.restore(rc);
     }
     for (int32_t k = 0; k < count; ++k) {
@@ -601,6 +644,7 @@ extern "C" int dflash_commit_block(dflash_session* s) {
 extern "C" int dflash_session_close(dflash_session* s) {
     if (!s) return fail(DFLASH_E_ARG, "null session");
     int rc = dflash_flush(s);
+    if (s->aux) s->ctx->engine->aux_close(s->aux);
     delete s;
     return rc;
 }
@@ -656,7 +700,7 @@ static int propose_many(dflash_session* const* ss, int32_t count, const int32_t*
     if (seqs.empty()) return 0;
     dflash_session* s0 = ss[0];
     if (!segs.empty()) {
-        int rc = ctx->engine->ctx_forward(views, segs, s0->ws, s0->ws_sessions, s0->stream);
+        int rc = ctx->engine->ctx_forward(views, segs, s0->ws, s0->ws_sessions, s0->stream, 0);
         if (rc) return guard.restore(rc);
     }
     for (int32_t k = 0; k < count; ++k) {

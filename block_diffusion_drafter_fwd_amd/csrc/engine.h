@@ -109,8 +109,22 @@ public:
         }
         return 0;
     }
+    // lane 0 or 1: which of the workspace's two sets of context-path buffers
+    // the pass uses (the passes of one call may run on two streams at once)
     virtual int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs,
-                            void* ws, int32_t ws_sessions, void* stream) = 0;
+                            void* ws, int32_t ws_sessions, void* stream, int lane) = 0;
+    // A second stream for a session (lane 1 of its context passes): opened
+    // with the session, closed with it; a call forks it from the session's
+    // stream before its first lane-1 pass and joins it back before returning.
+    // The default backend has none (every pass on lane 0).
+    virtual int aux_open(void** aux) {
+        *aux = nullptr;
+        return 0;
+    }
+    virtual void aux_close(void*) {}
+    virtual void* aux_stream(void*) { return nullptr; }
+    virtual int aux_fork(void*, void*) { return 0; }
+    virtual int aux_join(void*, void*) { return 0; }
     virtual int block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs,
                               float* logits, float* hidden, void* ws, int32_t ws_sessions,
                               void* stream) = 0;

@@ -77,9 +77,16 @@ constexpr size_t kPartCapFloats = size_t(8) << 20;   // tiled split-K partials: 
 constexpr int kMaxSlicesFc = 8;                      // K slices of the fc GEMM
 constexpr int kMaxSlicesKv = 4;                      // K slices of the context k|v GEMM
 
+// The context-path buffers come twice (lane 0 and lane 1): the passes of one
+// call alternate between the session's stream and a second one, which run
+// them at the same time.
+struct CtxBufs {
+    size_t tables, stage, fc, c, x, kv;
+};
 struct WsLayout {
     size_t tables;
     size_t ctx_stage, ctx_fc, ctx_c, ctx_x, ctx_kv;
+    CtxBufs lane1;
     size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_part, blk_mlp, blk_act;
     size_t attn_o, attn_ml, part, bitmap, stats, stats2, sel;
     size_t total;
@@ -118,6 +125,13 @@ public:
         w.ctx_c = put(4 * (size_t)w.r_ctx * H);
         w.ctx_x = put(act * (size_t)(c.ctx_input_norm ? L : 1) * w.r_ctx * H);
         w.ctx_kv = put(4 * (size_t)kMaxSlicesKv * w.r_ctx * L * 2 * m_.kd);
+        w.lane1.tables = put(sizeof(SeqDesc) * (size_t)ms + sizeof(RowInfo) * (size_t)w.r_ctx +
+                             sizeof(uint64_t) * (size_t)w.r_ctx + 128);
+        w.lane1.stage = put(act * (size_t)w.r_ctx * m_.fc_in);
+        w.lane1.fc = put(4 * (size_t)kMaxSlicesFc * w.r_ctx * H);
+        w.lane1.c = put(4 * (size_t)w.r_ctx * H);
+        w.lane1.x = put(act * (size_t)(c.ctx_input_norm ? L : 1) * w.r_ctx * H);
+        w.lane1.kv = put(4 * (size_t)kMaxSlicesKv * w.r_ctx * L * 2 * m_.kd);
         w.blk_h = put(4 * (size_t)w.r_blk * H);
         w.blk_x = put(act * (size_t)w.r_blk * H);
         w.blk_qkv = put(4 * (size_t)w.blk_slices * w.r_blk * qkv_ld());
@@ -204,7 +218,49 @@ public:
     }
 
     int ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs, void* ws,
-                    int32_t ws_sessions, void* stream) override;
+                    int32_t ws_sessions, void* stream, int lane) override;
+
+    struct Aux {
+        hipStream_t st = nullptr;
+        hipEvent_t fork = nullptr, join = nullptr;
+    };
+    int aux_open(void** out) override {
+        *out = nullptr;
+        Aux* a = new Aux;
+        // default priority (a stream of another priority is not used here)
+        if (hipStreamCreateWithFlags(&a->st, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&a->fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&a->join, hipEventDisableTiming) != hipSuccess) {
+            aux_close(a);
+            return fail(DFLASH_E_HIP, "second stream of the session could not be created");
+        }
+        *out = a;
+        return 0;
+    }
+    void aux_close(void* p) override {
+        Aux* a = (Aux*)p;
+        if (!a) return;
+        if (a->st) {
+            (void)hipStreamSynchronize(a->st);
+            (void)hipStreamDestroy(a->st);
+        }
+        if (a->fork) (void)hipEventDestroy(a->fork);
+        if (a->join) (void)hipEventDestroy(a->join);
+        delete a;
+    }
+    void* aux_stream(void* p) override { return p ? (void*)((Aux*)p)->st : nullptr; }
+    int aux_fork(void* p, void* stream) override {
+        Aux* a = (Aux*)p;
+        HIP_OK(hipEventRecord(a->fork, (hipStream_t)stream));
+        HIP_OK(hipStreamWaitEvent(a->st, a->fork, 0));
+        return 0;
+    }
+    int aux_join(void* p, void* stream) override {
+        Aux* a = (Aux*)p;
+        HIP_OK(hipEventRecord(a->join, a->st));
+        HIP_OK(hipStreamWaitEvent((hipStream_t)stream, a->join, 0));
+        return 0;
+    }
     int block_forward(const std::vector<SessView>& sess, const std::vector<BlockSeq>& seqs, float* logits,
                       float* hidden, void* ws, int32_t ws_sessions, void* stream) override;
     int sample(const std::vector<SessView>& sess, const int32_t* row_offsets, const float* logits,
@@ -348,9 +404,10 @@ private:
 };
 
 int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<CtxSeg>& segs, void* ws,
-                           int32_t ws_sessions, void* stream) {
+                           int32_t ws_sessions, void* stream, int lane) {
     const dflash_config& c = m_.cfg;
     const WsLayout w = layout(ws_sessions);
+    const CtxBufs b = lane ? w.lane1 : CtxBufs{w.tables, w.ctx_stage, w.ctx_fc, w.ctx_c, w.ctx_x, w.ctx_kv};
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
     const int32_t H = c.hidden, L = c.layers, kd = m_.kd;
@@ -381,7 +438,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
         // one segment (a session's flush): its rows' positions and cache go
         // to the head finish in the kernel arguments, and no table is uploaded
         const bool one = sj - si == 1;
-        char* tab = base + w.tables;
+        char* tab = base + b.tables;
         const SeqDesc* d_desc = nullptr;
         const RowInfo* d_info = nullptr;
         size_t o_src = 0;
@@ -398,8 +455,8 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
         // A operand of fc: the segment rows themselves, or gathered / aux-normed
         const void* A = segs[si].rows;
         if (sj - si > 1) {
-            HIP_OK(gather_rows(base + w.ctx_stage, (const uint64_t*)(tab + o_src), rows, rb, st));
-            A = base + w.ctx_stage;
+            HIP_OK(gather_rows(base + b.stage, (const uint64_t*)(tab + o_src), rows, rb, st));
+            A = base + b.stage;
         }
         if (c.aux_norms) {
             NormArgs n = norm_args(A, bf16(), m_.fc_in, rows, m_.fc_in);
@@ -407,12 +464,12 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             n.gain_group_stride = c.target_hidden;
             n.nout = 1;
             n.gain[0] = m_.aux_norms;
-            n.out[0] = base + w.ctx_stage;
+            n.out[0] = base + b.stage;
             n.out_stride = m_.fc_in;
             HIP_OK(rmsnorm(n, st));
-            A = base + w.ctx_stage;
+            A = base + b.stage;
         }
-        float* fc_out = (float*)(base + w.ctx_fc);
+        float* fc_out = (float*)(base + b.fc);
         int fc_slices = 1;
         {
             GemmArgs g = gemm_args(rows, m_.fc_in, fc_out, H, kPartial, part, kMaxSlicesFc);
@@ -422,7 +479,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 0, &fc_slices));
         }
         // hidden_norm over the summed slices, then (Laguna) every layer's input_layernorm
-        char* xs = base + w.ctx_x;
+        char* xs = base + b.x;
         const size_t xstride = m_.elem * (size_t)w.r_ctx * H;
         {
             NormArgs n = norm_args(nullptr, 0, H, rows, H);
@@ -432,7 +489,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
             n.nout = 1;
             n.gain[0] = m_.hidden_norm;
             if (c.ctx_input_norm) {
-                n.out[0] = base + w.ctx_c;
+                n.out[0] = base + b.c;
                 n.out_bf16 = 0;
             } else {
                 n.out[0] = xs;
@@ -441,7 +498,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
         }
         if (c.ctx_input_norm) {
             for (int32_t l0 = 0; l0 < L; l0 += kMaxOut) {
-                NormArgs n2 = norm_args(base + w.ctx_c, 0, H, rows, H);
+                NormArgs n2 = norm_args(base + b.c, 0, H, rows, H);
                 n2.nout = std::min(kMaxOut, L - l0);
                 for (int32_t j = 0; j < n2.nout; ++j) {
                     n2.gain[j] = m_.layer[l0 + j].in_ln;
@@ -452,7 +509,7 @@ int HipEngine::ctx_forward(const std::vector<SessView>& sess, const std::vector<
         }
         // every layer's K|V in one GEMM (up to 16 layers per launch)
         const int32_t ldkv = L * 2 * kd;
-        float* kv_out = (float*)(base + w.ctx_kv);
+        float* kv_out = (float*)(base + b.kv);
         for (int32_t l0 = 0; l0 < L; l0 += kMaxSeg / 2) {
             const int32_t nl = std::min<int32_t>(kMaxSeg / 2, L - l0);
             GemmArgs g = gemm_args(rows, H, kv_out, ldkv, kPartial, part, kMaxSlicesKv);

@@ -46,7 +46,7 @@ public:
         return 0;
     }
     int ctx_forward(const std::vector<SessView>&, const std::vector<CtxSeg>& segs, void*, int32_t,
-                    void*) override {
+                    void*, int) override {
         if (int rc = injected()) return rc;
         for (const CtxSeg& g : segs)
             log_line("ctx sess=" + std::to_string(g.sess) + " pos0=" + std::to_string(g.pos0) +

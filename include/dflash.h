@@ -27,7 +27,13 @@
  *  - Device work is enqueued on the session's HIP stream (hipStream_t passed
  *    as void*) and the call returns at once; device outputs are valid after
  *    that stream is synchronized.  Host-visible integers (n, offsets, states)
- *    are exact on return.
+ *    are exact on return.  A call that flushes two chunks or more (a long
+ *    committed run) also runs every second chunk read from the caller's rows
+ *    on a second stream the session opens with itself (default priority,
+ *    destroyed by dflash_session_close); that stream waits for the session's
+ *    stream at the start of the call and the session's stream waits for it
+ *    before the call returns, so the call's work is ordered with the
+ *    session's stream as if it all ran there.
  *  - Return value 0 is success; a negative DFLASH_E_* code is an error, with a
  *    thread-local message from dflash_last_error().  A call that fails leaves
  *    every session's state (offsets, pending rows, cache length, outstanding
@@ -181,13 +187,17 @@ int dflash_draft_limit(const dflash_ctx* ctx);
 size_t dflash_session_bytes(const dflash_ctx* ctx, int32_t capacity);
 
 /* Bytes of a workspace serving batched calls of up to `max_sessions`
- * sessions (1 for single-session use).  Returns 0 on a bad argument. */
+ * sessions (1 for single-session use), two sets of context-path buffers
+ * included (the two streams of a long committed run).  Returns 0 on a bad
+ * argument. */
 size_t dflash_workspace_bytes(const dflash_ctx* ctx, int32_t max_sessions);
 
 /* Open a session (dflash.go open): ctxOffset = restored_offset, i.e. the
  * arena already holds cache slots [0, restored_offset) from earlier work with
  * the same context and capacity.  seed and stream_id key the sampler's
- * Philox stream.  Errors: E_ARG, E_CAPACITY. */
+ * Philox stream.  The session also opens its second HIP stream (see the
+ * conventions); if the runtime refuses one, every flush chunk runs on
+ * hip_stream.  Errors: E_ARG, E_CAPACITY. */
 int dflash_session_open(dflash_ctx* ctx, void* arena, size_t arena_bytes, int32_t capacity,
                         void* workspace, size_t workspace_bytes, int32_t max_sessions,
                         int32_t restored_offset, uint64_t seed, uint64_t stream_id,

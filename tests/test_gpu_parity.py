@@ -403,6 +403,67 @@ def test_long_context_cache_rows_at_full_length(cuda):
 
 
 @pytest.mark.parametrize("name", ["qwen", "laguna"])
+def test_one_call_many_chunks_matches_oracle(cuda, name):
+    """One committed call of 1100 rows after 37 pending ones: the library
+    flushes it in 256-row chunks, every second chunk read from the caller's
+    rows on the session's second stream with the workspace's second set of
+    context buffers (the first chunk, which takes the pending rows through
+    the pending buffer, stays on the session's stream).  Cache rows at slots
+    in every chunk (the window's on laguna: only its last 511 rows are
+    projected, in two chunks) and a propose right after the call (ordered
+    behind both streams) match the oracle; a second large call then
+    continues the context."""
+    from oracle.model import DraftModel
+    from oracle.session import OracleSession
+    cfg = synth.config(name, layers=2, vocab=4099 if name == "laguna" else 5003)
+    w = synth.make_weights(cfg, seed=3, gains="random")
+    d = _drafter(cfg, w)
+    cap = 2400 + 64 if not cfg.window else cfg.window + cfg.block_size - 1
+    s = d.session(cap)
+    src = synth.FeatureSource(cfg, seed=3, session=0)
+    o = OracleSession(DraftModel(cfg, w, emulate_bf16=True))
+    T0, T1, T2 = 37, 1100, 1000
+    feats = src.features(0, T0 + T1 + T2)
+    toks = src.tokens(0, T0 + T1 + T2)
+    fd = feats_dev(cfg, feats)
+    s.committed(toks[:T0], fd[:T0], 0)
+    o.committed(toks[:T0], feats[:T0], 0)
+    s.committed(toks[T0:T0 + T1], fd[T0:T0 + T1], T0)
+    o.committed(toks[T0:T0 + T1], feats[T0:T0 + T1], T0)
+    torch.cuda.synchronize()
+    F = T0 + T1
+    assert s.state()[0] == F and s.state()[1] == 0
+    lo = F - (cfg.window - 1) if cfg.window else 0
+    slots = np.array([x for x in (0, 36, 37, 255, 256, 292, 293, 511, 548, 549, 804, 805, 1060, 1061, F - 2, F - 1)
+                      if x >= lo])
+    model = DraftModel(cfg, w, emulate_bf16=True)
+    ref = model.context_kv(feats[slots], slots)
+    for l in range(cfg.layers):
+        for j, S in enumerate(slots):
+            k, v = s.cache_read(l, int(S), 1)
+            ek = rel_err(k.double().cpu().numpy()[0], ref[l][0][j])
+            ev = rel_err(v.double().cpu().numpy()[0], ref[l][1][j])
+            assert ek < tol(cfg) and ev < tol(cfg), (l, int(S), ek, ev)
+    anchor = int(toks[F])
+    n, logits, _ = s.propose(anchor, cfg.block_size - 1)
+    out = o.propose(anchor, cfg.block_size - 1)
+    err = rel_err(logits.double().cpu().numpy(), out["logits"])
+    say(f"[one call, many chunks] {name}: {len(slots)} slots x {cfg.layers} layers, logits rel err {err:.2e}")
+    assert n == out["logits"].shape[0] and err < tol(cfg), err
+    s.commit_block()
+    o.commit_block()
+    s.committed(toks[F:F + T2], fd[F:F + T2], F)
+    o.committed(toks[F:F + T2], feats[F:F + T2], F)
+    anchor = int(toks[F + T2 - 1])
+    n, logits, _ = s.propose(anchor, cfg.block_size - 1)
+    out = o.propose(anchor, cfg.block_size - 1)
+    err = rel_err(logits.double().cpu().numpy(), out["logits"])
+    assert err < tol(cfg), err
+    s.close()
+    d.close()
+
+
+@pytest.mark.parametrize("name", ["qwen", "laguna"])
 def test_flush_batch_matches_oracle(cuda, name):
     """dflash_flush_batch over sessions sharing a workspace (one with no
     rows, one with an outstanding block, ragged pending counts; the window
