@@ -652,7 +652,8 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         return (int32_t)std::max<int64_t>(kAttnMinChunk, (chunk64 + 63) / 64 * 64);
     };
     int32_t chunk = pick_chunk(attn_target_wg());
-    if (chunk < kAttnShortChunk) chunk = pick_chunk(cus_);
+    const bool long_chunks = chunk >= kAttnShortChunk;
+    if (!long_chunks) chunk = pick_chunk(cus_);
     int32_t items = 0;
     for (SeqDesc& d : descs) {
         const int32_t nk = d.F + d.M - d.key_lo;
@@ -661,6 +662,13 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         items += d.nitems;
     }
     if (bf16() && items > w.items_cap) return fail(DFLASH_E_CAPACITY, "attention work exceeds the workspace");
+    // One resident round of long chunks: each item takes every nitems-th
+    // 64-key tile of its sequence instead of one run, so the workgroups of a
+    // kv head read neighbouring tiles together (131072-key context: 97.1 ->
+    // 94.0 us per layer).  Not over several rounds: there the largest-first
+    // order is built for runs, and interleaved items were slower (batched
+    // 295 -> 319 us).
+    const int32_t strided = long_chunks && (int64_t)items * c.kv_heads <= attn_target_wg();
     if (items > 0xffff || nseq > 0xffff) return fail(DFLASH_E_CAPACITY, "attention work items exceed 16-bit indices");
     // dispatch order of the attention items: largest chunks first (stable),
     // so the partial chunks at the sequences' ends fill the launch's tail
@@ -760,6 +768,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             a.causal = c.causal;
             a.window = c.window;
             a.chunk = chunk;
+            a.strided = strided;
             a.total_items = items;
             a.gate = c.gate;
             a.gate_ld = ldq;

@@ -7,7 +7,9 @@
 // h / (Hq / Hkv).
 //
 // bf16 path (flash-decoding split over the context):
-//   k_attn_partial  one workgroup (4 waves) per (context chunk, kv head).  The
+//   k_attn_partial  one workgroup (4 waves) per (context chunk, kv head); a
+//                   chunk is a run of keys, or, when every item is resident
+//                   at once, every nitems-th 64-key tile of the sequence.  The
 //                   G q heads of that kv head times M block rows form up to 64
 //                   query rows, 16 per wave.  64-key tiles of K and V are
 //                   copied from the cache straight into LDS (global_load_lds,
@@ -92,8 +94,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     const SeqDesc sd = a.seqs[od >> 16];
     const int c = item - sd.item0;
     const int kend = sd.F + sd.M;
-    const int kb = sd.key_lo + c * a.chunk;
-    const int ke = min(kend, kb + a.chunk);
+    // the item's tiles: one run of chunk keys, or (strided) every nitems-th
+    // 64-key tile of the sequence's keys, so that the items of a kv head
+    // stream neighbouring tiles at the same time
+    const int kb = sd.key_lo + c * (a.strided ? kKT : a.chunk);
+    const int ke = a.strided ? kend : min(kend, kb + a.chunk);
+    const int kstep = a.strided ? sd.nitems * kKT : kKT;
     const int G = a.Hq / a.Hkv;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 15, q = lane >> 4;
     const int p_last = sd.F + sd.M - 1;
@@ -136,8 +142,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
 
     // tile copy: instruction i of this wave fills LDS pieces (8 wave + i) * 64
     // + lane, i.e. key 4 (8 wave + i) + lane / 16, position lane % 16, with the
-    // piece the XOR permutation puts there.  Keys past the chunk end copy the
-    // chunk's last key (masked below, probability zero).
+    // piece the XOR permutation puts there.  Keys past the end copy the last
+    // key (masked below, probability zero).
     auto load_tile = [&](int t0, uint16_t* dK, uint16_t* dV) {
 #pragma unroll
         for (int i = 0; i < 16 / kAttnWaves; ++i) {
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     auto tile = [&](int t0, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's copies of the tile landed
         __syncthreads();                                    // everyone's have; the other buffer is free
-        if (t0 + kKT < ke) load_tile(t0 + kKT, nK, nV);
+        if (t0 + kstep < ke) load_tile(t0 + kstep, nK, nV);
 
         // S^T[key][row] for 4 key tiles of 16 (4 MFMAs of k = 32 over D) per row group
         f32x4_t s[kRG][4];
@@ -257,9 +263,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
         }
     };
     load_tile(kb, sK0, sV0);
-    for (int t0 = kb; t0 < ke; t0 += 2 * kKT) {
+    for (int t0 = kb; t0 < ke; t0 += 2 * kstep) {
         tile(t0, sK0, sV0, sK1, sV1);
-        if (t0 + kKT < ke) tile(t0 + kKT, sK1, sV1, sK0, sV0);
+        if (t0 + kstep < ke) tile(t0 + kstep, sK1, sV1, sK0, sV0);
     }
 #pragma unroll
     for (int gi = 0; gi < kRG; ++gi) {

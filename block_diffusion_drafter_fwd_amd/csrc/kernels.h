@@ -145,7 +145,8 @@ struct AttnArgs {
     void* out;                // [rows][Hq*D]
     int32_t nseq, nrows, layer, L, Hq, Hkv, D, causal, window, chunk, total_items;
     int32_t gate, gate_ld, gate_col, out_bf16;
-    int32_t gate_nsplit, pad;
+    int32_t gate_nsplit;
+    int32_t strided;          // item c of a sequence takes its tiles c, c + nitems, ... (else one run of chunk keys)
     int64_t gate_stride;
     float scale;
 };
