@@ -670,29 +670,41 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
     // 295 -> 319 us).
     const int32_t strided = long_chunks && (int64_t)items * c.kv_heads <= attn_target_wg();
     if (items > 0xffff || nseq > 0xffff) return fail(DFLASH_E_CAPACITY, "attention work items exceed 16-bit indices");
-    // dispatch order of the attention items: largest chunks first (stable),
-    // so the partial chunks at the sequences' ends fill the launch's tail
-    std::vector<uint32_t> order;
-    order.reserve(items);
-    for (int32_t s = 0; s < nseq; ++s)
-        for (int32_t i = 0; i < descs[s].nitems; ++i) order.push_back(((uint32_t)s << 16) | (uint32_t)(descs[s].item0 + i));
-    auto item_keys = [&](uint32_t od) {
-        const SeqDesc& d = descs[od >> 16];
-        const int32_t i = (int32_t)(od & 0xffffu) - d.item0;
-        return std::min(chunk, d.F + d.M - d.key_lo - i * chunk);
-    };
-    std::stable_sort(order.begin(), order.end(), [&](uint32_t x, uint32_t y) { return item_keys(x) > item_keys(y); });
-    Tables tb;
-    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
-    const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
-    const size_t o_src = tb.add(rowsrc.data(), sizeof(int32_t) * rowsrc.size());
-    const size_t o_ord = tb.add(order.data(), sizeof(uint32_t) * order.size());
-    char* tab = base + w.tables;
-    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
-    const SeqDesc* d_desc = (const SeqDesc*)(tab + o_desc);
-    const RowInfo* d_info = (const RowInfo*)(tab + o_info);
-    const int32_t* d_rowsrc = (const int32_t*)(tab + o_src);
-    const uint32_t* d_order = (const uint32_t*)(tab + o_ord);
+    // One session (bf16): its block's kernels take the descriptor, the anchor
+    // and the first position from their arguments, so no table is uploaded
+    // (one launch fewer, and no kernel starts with two dependent table loads).
+    const bool one = nseq == 1 && bf16();
+    const SeqDesc* d_desc = nullptr;
+    const RowInfo* d_info = nullptr;
+    const int32_t* d_rowsrc = nullptr;
+    const uint32_t* d_order = nullptr;
+    if (!one) {
+        // dispatch order of the attention items: largest chunks first (stable),
+        // so the partial chunks at the sequences' ends fill the launch's tail
+        std::vector<uint32_t> order;
+        order.reserve(items);
+        for (int32_t s = 0; s < nseq; ++s)
+            for (int32_t i = 0; i < descs[s].nitems; ++i)
+                order.push_back(((uint32_t)s << 16) | (uint32_t)(descs[s].item0 + i));
+        auto item_keys = [&](uint32_t od) {
+            const SeqDesc& d = descs[od >> 16];
+            const int32_t i = (int32_t)(od & 0xffffu) - d.item0;
+            return std::min(chunk, d.F + d.M - d.key_lo - i * chunk);
+        };
+        std::stable_sort(order.begin(), order.end(),
+                         [&](uint32_t x, uint32_t y) { return item_keys(x) > item_keys(y); });
+        Tables tb;
+        const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+        const size_t o_info = tb.add(info.data(), sizeof(RowInfo) * info.size());
+        const size_t o_src = tb.add(rowsrc.data(), sizeof(int32_t) * rowsrc.size());
+        const size_t o_ord = tb.add(order.data(), sizeof(uint32_t) * order.size());
+        char* tab = base + w.tables;
+        HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+        d_desc = (const SeqDesc*)(tab + o_desc);
+        d_info = (const RowInfo*)(tab + o_info);
+        d_rowsrc = (const int32_t*)(tab + o_src);
+        d_order = (const uint32_t*)(tab + o_ord);
+    }
 
     float* h = (float*)(base + w.blk_h);
     void* x = base + w.blk_x;
@@ -703,6 +715,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
     {
         // embedding rows and the first layer's input norm in one pass
         EmbedArgs e{m_.embed, h, d_info, d_desc, H, R, c.mask_id, bf16(), m_.layer[0].in_ln, x, c.rms_eps, bf16()};
+        e.current = descs[0].current;   // (rows == nullptr: one block, anchor first)
         HIP_OK(embed(e, st));
     }
     for (int32_t l = 0; l < c.layers; ++l) {
@@ -725,6 +738,12 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             hd.src_stride = (int64_t)R * ldq;
             hd.rows = d_info;
             hd.seqs = d_desc;
+            if (one) {   // rows F, F + 1, ... of the one session
+                hd.pos0 = descs[0].F;
+                hd.cache0 = descs[0].cache;
+                hd.cap0 = descs[0].cap;
+                hd.ring0 = descs[0].ring;
+            }
             hd.q_out = base + w.blk_q;
             hd.q_norm = lw.q_norm;
             hd.k_norm[0] = lw.k_norm;
@@ -755,6 +774,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             a.part_ml = (float*)(base + w.attn_ml);
             a.gate_src = qkv;
             a.order = d_order;
+            a.seq0 = descs[0];              // (rows == nullptr: one session)
             a.gate_nsplit = qkv_slices;
             a.gate_stride = (int64_t)R * ldq;
             a.out = base + w.blk_attn;
@@ -841,6 +861,7 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         GemmArgs g = gemm_args(Rout, H, logits, c.vocab, kStore, part, 1);
         g.a_rows = d_rowsrc;                 // rows 1..n of every block
         g.seg[0] = GemmSeg{x, m_.lm_head, H, H, c.vocab, 0, 0, 0};
+        if (one) g.seg[0].A = (const uint16_t*)x + H;   // one block: rows 1..n are contiguous
         g.nseg = 1;
         Timed tm(this, "unembed", st);
         HIP_OK(gemm(g, bf16(), kPartCapFloats, cus_, st, 1));

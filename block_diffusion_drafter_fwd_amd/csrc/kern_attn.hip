@@ -88,10 +88,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
 
     // work items in the host's order (largest chunks first, so the short
     // ones fill the end of the launch), every kv head of an item together
+    // (one session, rows == nullptr: its descriptor in the arguments, items in order)
     const int rank = blockIdx.x / a.Hkv, g = blockIdx.x - rank * a.Hkv;
-    const uint32_t od = a.order[rank];
-    const int item = (int)(od & 0xffffu);
-    const SeqDesc sd = a.seqs[od >> 16];
+    int item = rank;
+    SeqDesc sd = a.seq0;
+    if (a.rows) {
+        const uint32_t od = a.order[rank];
+        item = (int)(od & 0xffffu);
+        sd = a.seqs[od >> 16];
+    }
     const int c = item - sd.item0;
     const int kend = sd.F + sd.M;
     // the item's tiles: one run of chunk keys, or (strided) every nitems-th
@@ -300,10 +305,15 @@ __global__ __launch_bounds__(32 * kCombHeads) void k_attn_combine(AttnArgs a) {
     const int brow = blockIdx.x, t = threadIdx.x, hl = t >> 5, lane = t & 31;
     const int hq = blockIdx.y * kCombHeads + hl;
     const bool act = hq < a.Hq;
-    const RowInfo ri = a.rows[brow];
-    const SeqDesc sd = a.seqs[ri.seq];
+    SeqDesc sd = a.seq0;                                         // rows == nullptr: one session
+    int pos = sd.F + brow;
+    if (a.rows) {
+        const RowInfo ri = a.rows[brow];
+        sd = a.seqs[ri.seq];
+        pos = ri.pos;
+    }
     const int G = a.Hq / a.Hkv, hqc = act ? hq : 0, g = hqc / G;
-    const int row = (ri.pos - sd.F) * G + hqc % G;
+    const int row = (pos - sd.F) * G + hqc % G;
     const size_t stride = (size_t)a.Hkv * 64;                    // between items
     const size_t base0 = ((size_t)sd.item0 * a.Hkv + g) * 64 + row;
     // the output gate's pre-activation (the sum of the projection's K slices),
@@ -390,10 +400,15 @@ __global__ __launch_bounds__(32 * kCombGroups) void k_attn_combine_w(AttnArgs a)
     __shared__ float gm[kCombGroups], gl[kCombGroups];
     __shared__ float4 go[kCombGroups][32];
     const int brow = blockIdx.x, hq = blockIdx.y, t = threadIdx.x, grp = t >> 5, lane = t & 31;
-    const RowInfo ri = a.rows[brow];
-    const SeqDesc sd = a.seqs[ri.seq];
+    SeqDesc sd = a.seq0;                                         // rows == nullptr: one session
+    int pos = sd.F + brow;
+    if (a.rows) {
+        const RowInfo ri = a.rows[brow];
+        sd = a.seqs[ri.seq];
+        pos = ri.pos;
+    }
     const int G = a.Hq / a.Hkv, g = hq / G;
-    const int row = (ri.pos - sd.F) * G + hq % G;
+    const int row = (pos - sd.F) * G + hq % G;
     const size_t stride = (size_t)a.Hkv * 64;                    // between items
     const size_t base0 = ((size_t)sd.item0 * a.Hkv + g) * 64 + row;
     float gv = 0.f;

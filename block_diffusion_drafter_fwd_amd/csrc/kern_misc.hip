@@ -113,6 +113,17 @@ __global__ __launch_bounds__(NT) void k_rmsnorm4(NormArgs a) {
     const int irow = a.row_src ? a.row_src[orow] : orow;
     const int W = a.width / a.groups, W4 = W >> 2;
     const size_t ibase = (size_t)irow * a.in_stride + (size_t)grp * W;
+    const size_t gbase = (size_t)grp * a.gain_group_stride;
+    // the first output's gains go out with the other loads, not after the
+    // writeback stores (a load issued after a store would wait for it)
+    constexpr int kIt = kNormMaxW / 4 / NT;
+    float4 g0[kIt];
+    if (a.nout > 0)
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int i = threadIdx.x + it * NT;
+            if (i < W4) g0[it] = ld4_any(a.gain[0], gbase + 4 * i, a.gain_bf16);
+        }
     float ss = 0.f;
     for (int i = threadIdx.x; i < W4; i += NT) {
         float4 x = a.in ? ld4_any(a.in, ibase + 4 * i, a.in_bf16) : float4{0.f, 0.f, 0.f, 0.f};
@@ -139,10 +150,12 @@ __global__ __launch_bounds__(NT) void k_rmsnorm4(NormArgs a) {
     if (a.writeback)
         for (int i = threadIdx.x; i < W4; i += NT) *(float4*)(a.writeback + ibase + 4 * i) = xs[i];
     const size_t obase = (size_t)orow * a.out_stride + (size_t)grp * W;
-    const size_t gbase = (size_t)grp * a.gain_group_stride;
     for (int o = 0; o < a.nout; ++o)
-        for (int i = threadIdx.x; i < W4; i += NT) {
-            const float4 gn = ld4_any(a.gain[o], gbase + 4 * i, a.gain_bf16);
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int i = threadIdx.x + it * NT;
+            if (i >= W4) break;
+            const float4 gn = o == 0 ? g0[it] : ld4_any(a.gain[o], gbase + 4 * i, a.gain_bf16);
             const float4 x = xs[i];
             st4_any(a.out[o], obase + 4 * i,
                     float4{x.x * rstd * gn.x, x.y * rstd * gn.y, x.z * rstd * gn.z, x.w * rstd * gn.w}, a.out_bf16);
@@ -184,6 +197,33 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nq = (a.q_col >= 0) ? a.Hq : 0;
     const int task = blockIdx.y * 4 + wave;
+    const bool live = task < nq + 2 * a.Hkv;
+    const int half = a.D >> 1;
+    const bool act = lane < half;
+    const int layer = a.layer[li];
+    int kind, head, col;   // kind 0 q, 1 k, 2 v
+    if (task < nq) { kind = 0; head = task; col = a.q_col + head * a.D; }
+    else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * a.D; }
+    else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * a.D; }
+    // the loads that do not depend on the row's position go out first: the
+    // first kNormSliceBatch slices and the head norm's gains
+    const float* src = a.src + (size_t)row * a.ld + col + lane;
+    const void* gnp = kind == 0 ? a.q_norm : a.k_norm[li];
+    const bool use_norm = kind != 2 && a.qk_norm;
+    float v1[kNormSliceBatch], v2[kNormSliceBatch];
+    float gn1 = 0.f, gn2 = 0.f;
+    if (live && act) {
+#pragma unroll
+        for (int j = 0; j < kNormSliceBatch; ++j) {
+            const size_t o = (size_t)min(j, a.nsplit - 1) * a.src_stride;
+            v1[j] = src[o];
+            v2[j] = src[o + half];
+        }
+        if (use_norm) {
+            gn1 = ld_any(gnp, lane, a.w_bf16);
+            gn2 = ld_any(gnp, lane + half, a.w_bf16);
+        }
+    }
     int pos, cap, ring;
     void* cache;
     if (a.rows) {
@@ -199,7 +239,6 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
         ring = a.ring0;
         cache = a.cache0;
     }
-    const int half = a.D >> 1;
     // the row's rotation angles once for the workgroup's four heads (fp64,
     // rounded to fp32), not once per head
     if (threadIdx.x < half) {
@@ -209,24 +248,18 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
         s_sin[threadIdx.x] = (float)sn_;
     }
     __syncthreads();
-    if (task >= nq + 2 * a.Hkv) return;
+    if (!live) return;
     const int slot = ring ? pos % cap : pos;
-    const bool act = lane < half;
-    const int layer = a.layer[li];
-    int kind, head, col;   // kind 0 q, 1 k, 2 v
-    if (task < nq) { kind = 0; head = task; col = a.q_col + head * a.D; }
-    else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * a.D; }
-    else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * a.D; }
-    const float* src = a.src + (size_t)row * a.ld + col + lane;
     float x1 = 0.f, x2 = 0.f;
-    if (act)   // slices loaded kNormSliceBatch at a time (one L2 round trip each batch), added in order
+    if (act)   // slices added in order; past the first batch, kNormSliceBatch loads per round trip
         for (int s0 = 0; s0 < a.nsplit; s0 += kNormSliceBatch) {
-            float v1[kNormSliceBatch], v2[kNormSliceBatch];
+            if (s0) {
 #pragma unroll
-            for (int j = 0; j < kNormSliceBatch; ++j) {
-                const size_t o = (size_t)min(s0 + j, a.nsplit - 1) * a.src_stride;
-                v1[j] = src[o];
-                v2[j] = src[o + half];
+                for (int j = 0; j < kNormSliceBatch; ++j) {
+                    const size_t o = (size_t)min(s0 + j, a.nsplit - 1) * a.src_stride;
+                    v1[j] = src[o];
+                    v2[j] = src[o + half];
+                }
             }
 #pragma unroll
             for (int j = 0; j < kNormSliceBatch; ++j)
@@ -236,13 +269,12 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
                 }
         }
     if (kind != 2) {
-        if (a.qk_norm) {
+        if (use_norm) {
             const float ss = wave_sum(x1 * x1 + x2 * x2);
             const float rstd = 1.f / sqrtf(ss / (float)a.D + a.eps);
-            const void* gn = kind == 0 ? a.q_norm : a.k_norm[li];
             if (act) {
-                x1 = x1 * rstd * ld_any(gn, lane, a.w_bf16);
-                x2 = x2 * rstd * ld_any(gn, lane + half, a.w_bf16);
+                x1 = x1 * rstd * gn1;
+                x2 = x2 * rstd * gn2;
             }
         }
         if (act) {
@@ -280,25 +312,59 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
     __shared__ float sh[4];
     __shared__ float xs[kNormMaxW];
     const int row = blockIdx.x;
-    const RowInfo ri = a.rows[row];
-    const SeqDesc sd = a.seqs[ri.seq];
-    const int tok = ri.pos == sd.F ? sd.current : a.mask_id;
+    int tok;
+    if (a.rows) {
+        const RowInfo ri = a.rows[row];
+        const SeqDesc sd = a.seqs[ri.seq];
+        tok = ri.pos == sd.F ? sd.current : a.mask_id;
+    } else {
+        tok = row == 0 ? a.current : a.mask_id;
+    }
     const size_t src = (size_t)tok * a.H;
-    // all loads first (into LDS), then the stores: a store to h between two
-    // table loads would make each load wait for the one before
     float ss = 0.f;
     if (a.vec4) {
-        for (int j = 4 * threadIdx.x; j < a.H; j += 1024) {
-            const float4 v = ld4_any(a.table, src + j, a.w_bf16);
-            *(float4*)&xs[j] = v;
-            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        // four elements at j = 4 (t + 256 c): the table row and the gains are
+        // all loaded before the first store (a load after a store to h or out
+        // would wait for the loads before it)
+        constexpr int kC = kNormMaxW / 1024;
+        float4 v[kC], gn[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            const int j = 4 * (threadIdx.x + 256 * c);
+            if (j < a.H) v[c] = ld4_any(a.table, src + j, a.w_bf16);
         }
-    } else {
-        for (int j = threadIdx.x; j < a.H; j += 256) {
-            const float v = ld_any(a.table, src + j, a.w_bf16);
-            xs[j] = v;
-            ss += v * v;
+        if (a.gain)
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                const int j = 4 * (threadIdx.x + 256 * c);
+                if (j < a.H) gn[c] = ld4_any(a.gain, j, a.w_bf16);
+            }
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            const int j = 4 * (threadIdx.x + 256 * c);
+            if (j < a.H) {
+                ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+                *(float4*)(a.h + (size_t)row * a.H + j) = v[c];
+            }
         }
+        if (!a.gain) return;                           // uniform over the launch
+        ss = block_sum(ss, sh);
+        const float rstd = 1.f / sqrtf(ss / (float)a.H + a.eps);
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            const int j = 4 * (threadIdx.x + 256 * c);
+            if (j < a.H)
+                st4_any(a.out, (size_t)row * a.H + j,
+                        float4{v[c].x * rstd * gn[c].x, v[c].y * rstd * gn[c].y, v[c].z * rstd * gn[c].z,
+                               v[c].w * rstd * gn[c].w},
+                        a.out_bf16);
+        }
+        return;
+    }
+    for (int j = threadIdx.x; j < a.H; j += 256) {
+        const float v = ld_any(a.table, src + j, a.w_bf16);
+        xs[j] = v;
+        ss += v * v;
     }
     __syncthreads();
     for (int j = threadIdx.x; j < a.H; j += 256) a.h[(size_t)row * a.H + j] = xs[j];
@@ -312,7 +378,8 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
 hipError_t embed(const EmbedArgs& args, hipStream_t st) {
     if (args.nrows <= 0) return hipSuccess;
     EmbedArgs a = args;
-    a.vec4 = a.H % 4 == 0 && aligned16(a.table);
+    a.vec4 = a.H % 4 == 0 && a.H <= kNormMaxW && aligned16(a.table) && aligned16(a.h) && aligned16(a.gain) &&
+             aligned16(a.out);
     hipLaunchKernelGGL(k_embed, dim3(a.nrows), dim3(256), 0, st, a);
     return hipGetLastError();
 }

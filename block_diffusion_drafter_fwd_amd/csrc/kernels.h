@@ -124,7 +124,7 @@ struct HeadArgs {
 struct EmbedArgs {
     const void* table;
     float* h;
-    const RowInfo* rows;
+    const RowInfo* rows;      // nullptr: one block, row 0 the anchor `current`, the rest mask tokens
     const SeqDesc* seqs;
     int32_t H, nrows, mask_id, w_bf16;
     const void* gain;
@@ -132,6 +132,7 @@ struct EmbedArgs {
     float eps;
     int32_t out_bf16;
     int32_t vec4;             // set by the launcher: rows read four elements at a time
+    int32_t current;
 };
 
 struct AttnArgs {
@@ -149,6 +150,8 @@ struct AttnArgs {
     int32_t strided;          // item c of a sequence takes its tiles c, c + nitems, ... (else one run of chunk keys)
     int64_t gate_stride;
     float scale;
+    int32_t pad2;
+    SeqDesc seq0;             // rows == nullptr: one session, block row r at position seq0.F + r, items in order
 };
 
 struct SampleArgs {
