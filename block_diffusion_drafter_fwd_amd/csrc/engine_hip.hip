@@ -620,7 +620,9 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
             sizes.clear();
             for (const SeqDesc& d : descs) {
                 const int32_t nk = d.F + d.M - d.key_lo;
-                for (int32_t k0 = 0; k0 < nk; k0 += ch) sizes.push_back((std::min(ch, nk - k0) + 63) / 64);
+                // item i of ni takes tiles i, i + ni, ... of the sequence's T tiles
+                const int32_t ni = (nk + ch - 1) / ch, T = (nk + 63) / 64;
+                for (int32_t i = 0; i < ni; ++i) sizes.push_back((T - i + ni - 1) / ni);
             }
             if ((int64_t)sizes.size() > w.items_cap) continue;
             std::sort(sizes.begin(), sizes.end(), std::greater<int32_t>());
@@ -662,13 +664,12 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         items += d.nitems;
     }
     if (bf16() && items > w.items_cap) return fail(DFLASH_E_CAPACITY, "attention work exceeds the workspace");
-    // One resident round of long chunks: each item takes every nitems-th
-    // 64-key tile of its sequence instead of one run, so the workgroups of a
-    // kv head read neighbouring tiles together (131072-key context: 97.1 ->
-    // 94.0 us per layer).  Not over several rounds: there the largest-first
-    // order is built for runs, and interleaved items were slower (batched
-    // 295 -> 319 us).
-    const int32_t strided = long_chunks && (int64_t)items * c.kv_heads <= attn_target_wg();
+    // Long chunks: each item takes every nitems-th 64-key tile of its
+    // sequence instead of one run, so the workgroups of a kv head read
+    // neighbouring tiles together (131072-key context: 97.1 -> 94.2 us per
+    // layer; batched, several rounds: 295 -> 292 us, with the schedule model
+    // and the dispatch order below counting the interleaved items' tiles).
+    const int32_t strided = long_chunks;
     if (items > 0xffff || nseq > 0xffff) return fail(DFLASH_E_CAPACITY, "attention work items exceed 16-bit indices");
     // One session (bf16): its block's kernels take the descriptor, the anchor
     // and the first position from their arguments, so no table is uploaded
@@ -686,9 +687,10 @@ int HipEngine::block_forward(const std::vector<SessView>& sess, const std::vecto
         for (int32_t s = 0; s < nseq; ++s)
             for (int32_t i = 0; i < descs[s].nitems; ++i)
                 order.push_back(((uint32_t)s << 16) | (uint32_t)(descs[s].item0 + i));
-        auto item_keys = [&](uint32_t od) {
+        auto item_keys = [&](uint32_t od) {   // (in 64-key tiles when the items interleave)
             const SeqDesc& d = descs[od >> 16];
             const int32_t i = (int32_t)(od & 0xffffu) - d.item0;
+            if (strided) return ((d.F + d.M - d.key_lo + 63) / 64 - i + d.nitems - 1) / d.nitems;
             return std::min(chunk, d.F + d.M - d.key_lo - i * chunk);
         };
         std::stable_sort(order.begin(), order.end(),

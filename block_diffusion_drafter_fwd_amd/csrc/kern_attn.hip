@@ -8,8 +8,8 @@
 //
 // bf16 path (flash-decoding split over the context):
 //   k_attn_partial  one workgroup (4 waves) per (context chunk, kv head); a
-//                   chunk is a run of keys, or, when every item is resident
-//                   at once, every nitems-th 64-key tile of the sequence.  The
+//                   chunk is a run of keys or (chunks of 256 keys and more)
+//                   every nitems-th 64-key tile of the sequence.  The
 //                   G q heads of that kv head times M block rows form up to 64
 //                   query rows, 16 per wave.  64-key tiles of K and V are
 //                   copied from the cache straight into LDS (global_load_lds,
