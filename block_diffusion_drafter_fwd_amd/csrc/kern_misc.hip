@@ -297,10 +297,126 @@ __global__ __launch_bounds__(256) void k_head_finish(HeadArgs a) {
     }
 }
 
+// The same finish for 128-wide heads with 16-byte accesses: 16 lanes per
+// head, four heads per wave, lane l holding dims 4l .. 4l + 3 and their
+// rotation partners 64 + 4l .. (a quarter of the load instructions, each
+// four times wider; the flush's 256-row context pass reads 31.5 MB of K
+// slices here).  The slice sums and the rotation are those of k_head_finish
+// element by element; the head norm's sum of squares runs over 16 lanes.
+__global__ __launch_bounds__(256) void k_head_finish4(HeadArgs a) {
+    __shared__ float4 s_cs[16], s_sn[16];   // cos, sin of dims 4i .. 4i + 3
+    const int row = blockIdx.x, li = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l = lane & 15;
+    const int nq = (a.q_col >= 0) ? a.Hq : 0;
+    const int task = blockIdx.y * 16 + wave * 4 + (lane >> 4);
+    const bool live = task < nq + 2 * a.Hkv;   // (uniform over each 16-lane group)
+    const int layer = a.layer[li];
+    int kind, head, col;   // kind 0 q, 1 k, 2 v
+    if (task < nq) { kind = 0; head = task; col = a.q_col + head * 128; }
+    else if (task < nq + a.Hkv) { kind = 1; head = task - nq; col = a.k_col[li] + head * 128; }
+    else { kind = 2; head = task - nq - a.Hkv; col = a.v_col[li] + head * 128; }
+    // position-independent loads first: a batch of slices and the gains
+    constexpr int kB = 4;
+    const float* src = a.src + (size_t)row * a.ld + col + 4 * l;
+    const void* gnp = kind == 0 ? a.q_norm : a.k_norm[li];
+    const bool use_norm = kind != 2 && a.qk_norm;
+    float4 v1[kB], v2[kB];
+    float4 g1 = {0.f, 0.f, 0.f, 0.f}, g2 = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const size_t o = (size_t)min(j, a.nsplit - 1) * a.src_stride;
+            v1[j] = *(const float4*)(src + o);
+            v2[j] = *(const float4*)(src + o + 64);
+        }
+        if (use_norm) {
+            g1 = ld4_any(gnp, 4 * l, a.w_bf16);
+            g2 = ld4_any(gnp, 64 + 4 * l, a.w_bf16);
+        }
+    }
+    int pos, cap, ring;
+    void* cache;
+    if (a.rows) {
+        const RowInfo ri = a.rows[row];
+        const SeqDesc sd = a.seqs[ri.seq];
+        pos = ri.pos;
+        cap = sd.cap;
+        ring = sd.ring;
+        cache = sd.cache;
+    } else {
+        pos = a.pos0 + row;
+        cap = a.cap0;
+        ring = a.ring0;
+        cache = a.cache0;
+    }
+    if (threadIdx.x < 64) {
+        double sn_, cs_;
+        sincos((double)pos * a.inv_freq[threadIdx.x], &sn_, &cs_);
+        ((float*)s_cs)[threadIdx.x] = (float)cs_;
+        ((float*)s_sn)[threadIdx.x] = (float)sn_;
+    }
+    __syncthreads();
+    if (!live) return;
+    float4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.nsplit; s0 += kB) {
+        if (s0) {
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                const size_t o = (size_t)min(s0 + j, a.nsplit - 1) * a.src_stride;
+                v1[j] = *(const float4*)(src + o);
+                v2[j] = *(const float4*)(src + o + 64);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+            if (s0 + j < a.nsplit) {
+                x1 = float4{x1.x + v1[j].x, x1.y + v1[j].y, x1.z + v1[j].z, x1.w + v1[j].w};
+                x2 = float4{x2.x + v2[j].x, x2.y + v2[j].y, x2.z + v2[j].z, x2.w + v2[j].w};
+            }
+    }
+    if (kind != 2) {
+        if (use_norm) {
+            float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w + x2.x * x2.x + x2.y * x2.y +
+                       x2.z * x2.z + x2.w * x2.w;
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+            const float rstd = 1.f / sqrtf(ss / 128.f + a.eps);
+            x1 = float4{x1.x * rstd * g1.x, x1.y * rstd * g1.y, x1.z * rstd * g1.z, x1.w * rstd * g1.w};
+            x2 = float4{x2.x * rstd * g2.x, x2.y * rstd * g2.y, x2.z * rstd * g2.z, x2.w * rstd * g2.w};
+        }
+        const float4 cs = s_cs[l], sn = s_sn[l];
+        const float4 y1 = {x1.x * cs.x - x2.x * sn.x, x1.y * cs.y - x2.y * sn.y, x1.z * cs.z - x2.z * sn.z,
+                           x1.w * cs.w - x2.w * sn.w};
+        const float4 y2 = {x2.x * cs.x + x1.x * sn.x, x2.y * cs.y + x1.y * sn.y, x2.z * cs.z + x1.z * sn.z,
+                           x2.w * cs.w + x1.w * sn.w};
+        x1 = y1;
+        x2 = y2;
+    }
+    if (kind == 0) {
+        const size_t o = ((size_t)row * a.Hq + head) * 128;
+        st4_any(a.q_out, o + 4 * l, x1, a.q_bf16);
+        st4_any(a.q_out, o + 64 + 4 * l, x2, a.q_bf16);
+    } else {
+        const int slot = ring ? pos % cap : pos;
+        const size_t o = ((((size_t)layer * 2 + (kind - 1)) * a.Hkv + head) * cap + slot) * 128;
+        st4_any(cache, o + 4 * l, x1, a.cache_bf16);
+        st4_any(cache, o + 64 + 4 * l, x2, a.cache_bf16);
+    }
+}
+
 hipError_t head_finish(const HeadArgs& a, int nlayer, hipStream_t st) {
     if (a.nrows <= 0 || nlayer <= 0) return hipSuccess;
     const int ntask = (a.q_col >= 0 ? a.Hq : 0) + 2 * a.Hkv;
-    hipLaunchKernelGGL(k_head_finish, dim3(a.nrows, (ntask + 3) / 4, nlayer), dim3(256), 0, st, a);
+    // 128-wide heads with every slice row and column 16-byte aligned: the
+    // vector form (the cache and query rows are 256-byte multiples)
+    bool v4 = a.D == 128 && a.ld % 4 == 0 && a.src_stride % 4 == 0 && aligned16(a.src) && (a.q_col < 0 || a.q_col % 4 == 0) &&
+              aligned16(a.q_out) && aligned16(a.q_norm);
+    for (int j = 0; j < nlayer; ++j) v4 = v4 && a.k_col[j] % 4 == 0 && a.v_col[j] % 4 == 0 && aligned16(a.k_norm[j]);
+    if (v4)
+        hipLaunchKernelGGL(k_head_finish4, dim3(a.nrows, (ntask + 15) / 16, nlayer), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_head_finish, dim3(a.nrows, (ntask + 3) / 4, nlayer), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
