@@ -877,8 +877,21 @@ __global__ __launch_bounds__(256) void k_verify_stats(VerifyArgs a) {
     const float* z = a.target + (size_t)r * a.V;
     const float inv_t = a.temperature > 0.f ? 1.f / a.temperature : 1.f;
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
-    for (int t = t_lo + threadIdx.x; t < t_hi; t += 256) {
-        const float zt = z[t];
+    // the thread's tokens t_lo + threadIdx.x + 256 i, kVerBatch loads issued
+    // together (one round trip), then the online pass in ascending order
+    constexpr int kVerBatch = 16;
+    for (int b0 = t_lo + threadIdx.x; b0 < t_hi; b0 += 256 * kVerBatch) {
+        float zb[kVerBatch];
+#pragma unroll
+        for (int i = 0; i < kVerBatch; ++i) {
+            const int t = b0 + 256 * i;
+            zb[i] = t < t_hi ? z[t] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kVerBatch; ++i) {
+        const int t = b0 + 256 * i;
+        if (t >= t_hi) break;
+        const float zt = zb[i];
         if (a.temperature > 0.f) {
             const float sv = zt * inv_t;
             if (sv > s.m) {
@@ -891,6 +904,7 @@ __global__ __launch_bounds__(256) void k_verify_stats(VerifyArgs a) {
         if (zt > s.best) {      // threads walk ascending ids: a tie keeps the lower one
             s.best = zt;
             s.idx = t;
+        }
         }
     }
     s = block_stat(s);
@@ -957,27 +971,45 @@ __global__ __launch_bounds__(256) void k_verify_next(VerifyArgs a) {
     const float* q = i < n ? a.draft_probs + (size_t)(verify_off<ONE>(a, ri.seq) + i) * a.V : nullptr;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
-    for (int qd = (t_lo >> 2) + threadIdx.x; qd * 4 < t_hi; qd += 256) {
+    // the thread's groups of four tokens qd = t_lo / 4 + threadIdx.x + 256 u:
+    // kNextBatch groups' target and draft loads issued together
+    constexpr int kNextBatch = 4;
+    for (int qb = (t_lo >> 2) + threadIdx.x; qb * 4 < t_hi; qb += 256 * kNextBatch) {
+    float zb[kNextBatch][4], qb_[kNextBatch][4];
+#pragma unroll
+    for (int u = 0; u < kNextBatch; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = (qb + 256 * u) * 4 + j;
+            zb[u][j] = t < t_hi ? z[t] : 0.f;
+            qb_[u][j] = (q && t < t_hi) ? q[t] : 0.f;
+        }
+#pragma unroll
+    for (int u = 0; u < kNextBatch; ++u) {
+        const int qd = qb + 256 * u;
+        if (qd * 4 >= t_hi) break;
         uint64_t w[4] = {(uint64_t)qd, (uint64_t)i, (uint64_t)a.round, 2};
         philox4x64_10(w, sd.seed, sd.stream);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int t = qd * 4 + j;
             if (t >= t_hi) break;
-            const float sv = z[t] * inv_t;
+            const float sv = zb[u][j] * inv_t;
             float key;
             if (q) {
-                const float d = __expf(sv - M) * inv_z - q[t];
-                key = d > 0.f ? logf(d) : -INFINITY;
+                const float d = __expf(sv - M) * inv_z - qb_[u][j];
+                // (the hardware base-2 logarithm, as for the Gumbel noise)
+                key = d > 0.f ? __builtin_amdgcn_logf(d) * 0.6931471805599453f : -INFINITY;
             } else {
                 key = sv;
             }
-            key -= logf(-logf(u23(w[j])));
+            key += gumbel(u23(w[j]));
             if (key > s.best || (key == s.best && t < s.idx)) {
                 s.best = key;
                 s.idx = t;
             }
         }
+    }
     }
     s = block_stat(s);
     if (threadIdx.x == 0) {
@@ -989,31 +1021,47 @@ __global__ __launch_bounds__(256) void k_verify_next(VerifyArgs a) {
     }
 }
 
+// Acceptance: every drafted row's test is independent of the others (its own
+// counter), so each wave takes rows wave, wave + kVerWaves, ... (statistics
+// merge, draft id, the accept draw), the tests land in LDS, and the accepted
+// run is their first failure; next is the rejected (or bonus) row's draw.
+constexpr int kVerWaves = 16;
+constexpr int kVerMaxRows = 512;       // n_k + 1 <= blockSize <= 512
 template <bool ONE>
-__global__ __launch_bounds__(64) void k_verify_final(VerifyArgs a) {
-    const int k = blockIdx.x;
-    const int off = verify_off<ONE>(a, k), n = verify_off<ONE>(a, k + 1) - off, r0 = off + k;
+__global__ __launch_bounds__(64 * kVerWaves) void k_verify_final(VerifyArgs a) {
+    __shared__ uint8_t s_ok[kVerMaxRows];
+    __shared__ int s_next[kVerMaxRows];
+    const int k = blockIdx.x, wave = threadIdx.x >> 6;
+    const int off = verify_off<ONE>(a, k), r0 = off + k;
+    const int n = min(verify_off<ONE>(a, k + 1) - off, kVerMaxRows - 1);   // (the API bounds it by blockSize - 1)
     const SeqDesc sd = verify_seq<ONE>(a, k);
-    int acc = 0;
-    for (; acc < n; ++acc) {
-        const Stat s = row_stat(a.stats, a.nchunk, r0 + acc);
-        const int x = a.draft_ids[off + acc];
-        bool ok;
-        if (a.temperature == 0.f) {
-            ok = s.idx == x;
-        } else {
-            const float p = __expf(a.target[(size_t)(r0 + acc) * a.V + x] / a.temperature - s.m) / s.l;
-            const float q = a.draft_probs[(size_t)(off + acc) * a.V + x];
-            uint64_t w[4] = {0, (uint64_t)acc, (uint64_t)a.round, 1};
-            philox4x64_10(w, sd.seed, sd.stream);
-            ok = u23(w[0]) * q <= p;
+    for (int j = wave; j <= n; j += kVerWaves) {
+        const Stat s = row_stat(a.stats, a.nchunk, r0 + j);
+        bool ok = false;
+        if (j < n) {
+            const int x = a.draft_ids[off + j];
+            if (a.temperature == 0.f) {
+                ok = s.idx == x;
+            } else {
+                const float p = __expf(a.target[(size_t)(r0 + j) * a.V + x] / a.temperature - s.m) / s.l;
+                const float q = a.draft_probs[(size_t)(off + j) * a.V + x];
+                uint64_t w[4] = {0, (uint64_t)j, (uint64_t)a.round, 1};
+                philox4x64_10(w, sd.seed, sd.stream);
+                ok = u23(w[0]) * q <= p;
+            }
         }
-        if (!ok) break;
+        const int nx = a.temperature == 0.f ? s.idx : row_stat(a.stats2, a.nchunk, r0 + j).idx;
+        if ((threadIdx.x & 63) == 0) {
+            s_ok[j] = ok;
+            s_next[j] = nx;
+        }
     }
-    const Stat s = row_stat(a.temperature == 0.f ? a.stats : a.stats2, a.nchunk, r0 + acc);
+    __syncthreads();
     if (threadIdx.x == 0) {
+        int acc = 0;
+        while (acc < n && s_ok[acc]) ++acc;
         a.accepted[k] = acc;
-        a.next[k] = s.idx;
+        a.next[k] = s_next[acc];
     }
 }
 
@@ -1218,7 +1266,7 @@ static hipError_t verify_launch(const VerifyArgs& a, hipStream_t st) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_verify_final<ONE>, dim3(a.nseq), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_verify_final<ONE>, dim3(a.nseq), dim3(64 * kVerWaves), 0, st, a);
     return hipGetLastError();
 }
 

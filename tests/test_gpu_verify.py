@@ -167,3 +167,60 @@ def test_one_session_verify_equals_batched_and_oracle(setup, n, temperature):
                                      np.sort(info["scores"][np.isfinite(info["scores"])])))
     if not close:
         assert one == (a, x), (one, a, x)
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7, 1.0])
+def test_long_drafts_verify_matches_oracle(temperature):
+    """Drafts longer than the acceptance pass's 16 waves (48-token blocks:
+    40 and 23 drafted rows, so waves take a second and third row): greedy
+    drafts that follow the target's argmax to row 37 (of 40) and through all
+    23 rows; sampled drafts from the target's own p with a confident draft on
+    a token the target shuns at row 33 (40 rows) and none in the other."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_fwd_amd import Drafter, abi, verify
+    from tests.parity import device_tensors
+    abi.load("hip")
+    cfg = synth.config("tiny", vocab=V, block_size=48)
+    d = Drafter(cfg, device_tensors(cfg, synth.make_weights(cfg, seed=9)), max_sessions=2)
+    sessions = [d.session(128, seed=300 + k, stream_id=k) for k in range(2)]
+    drafts = [40, 23]
+    offs = np.array([0, 40, 63], np.int32)
+    rng = np.random.default_rng(77 + int(10 * temperature))
+    target = rng.normal(scale=2.0, size=(63 + 2, V)).astype(np.float32)
+    ids = np.zeros(63, np.int32)
+    q = np.zeros((63, V), np.float32)
+    for k, (n, brk) in enumerate(zip(drafts, [37, 23])):
+        r0 = offs[k] + k
+        for i in range(n):
+            if temperature == 0.0:
+                am = int(np.argmax(target[r0 + i]))
+                ids[offs[k] + i] = am if i < brk else (am + 1) % V
+            else:
+                if k == 0 and i == 33:
+                    qi = np.full(V, 1e-6)
+                    qi[int(np.argmin(target[r0 + i]))] = 1.0
+                    qi /= qi.sum()
+                else:
+                    qi = softmax(target[r0 + i], temperature)
+                q[offs[k] + i] = qi.astype(np.float32)
+                qi64 = q[offs[k] + i].astype(np.float64)
+                ids[offs[k] + i] = int(rng.choice(V, p=qi64 / qi64.sum()))
+    acc, nxt = verify(sessions, offs, torch.from_numpy(target).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(q).cuda() if temperature > 0 else None, temperature, 4)
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    compared = 0
+    for k, n in enumerate(drafts):
+        r0 = offs[k] + k
+        a, x, info = verify_block(target[r0:r0 + n + 1], ids[offs[k]:offs[k] + n],
+                                  q[offs[k]:offs[k] + n] if temperature > 0 else None, temperature, 300 + k, k, 4)
+        if temperature > 0:
+            sc = np.sort(info["scores"][np.isfinite(info["scores"])])
+            if any(abs(uq - p) <= 1e-5 * max(uq, p, 1e-30) for uq, p in info["tests"]) or \
+                    (sc.size > 1 and sc[-1] - sc[-2] < 1e-4):
+                continue
+        compared += 1
+        assert (acc[k], nxt[k]) == (a, x), (k, acc[k], nxt[k], a, x)
+        if temperature == 0.0:
+            assert a == (37 if k == 0 else 23)
+    assert compared >= 1
