@@ -89,10 +89,17 @@ CASES = {
                                  vocab=3001),
                     W("l32k", "long", context=32768, commit_rows=256, rounds=3, max_tokens=7, temperature=1.0,
                       probs=True), 32768 + 4 * 8 + 64),
+    # a 32768-key sliding window over a ring that has wrapped (34000 context
+    # rows in 32775 slots): the attention split takes chunks of 256 keys or
+    # more whose items interleave their tiles, each key's slot its position
+    # modulo the capacity
+    "laguna_ring32k": (synth.config("laguna", hidden=1024, target_hidden=256, intermediate=3072, layers=1,
+                                    vocab=3001, window=32768),
+                       W("lr32", "laguna", context=34000, commit_rows=256, rounds=3), 32768 + 8 - 1),
 }
 # cases whose prompt is long: the oracle runs its bf16-emulating twin only and
 # the caches are checked at sampled slots
-LONG_CASES = {"long_ctx32k": 48}
+LONG_CASES = {"long_ctx32k": 48, "laguna_ring32k": 48}
 
 
 @pytest.mark.parametrize("name", list(CASES))
