@@ -32,8 +32,10 @@ workload after the long one and reports it under ``kernels.batched``
 
 The JSON line carries the roofline of the dominant kernel (the one with the
 most time per round), timed with HIP events on its stream inside the timed
-region, per-stage rooflines from the same hooks (``kernels``), and the CPU
-oracle's rate on a bounded sample of the same workload.  On the long workload
+region, per-stage rooflines from the same hooks (``kernels``; ``select`` is
+the DFlash2 selector on the block's drafted rows, with 8 candidates and
+64-wide tables), and the CPU oracle's rate on a bounded sample of the same
+workload.  On the long workload
 ``kernels.share_of_8`` times the attention, unembedding and sampler at one
 GPU's share of an eight-GPU split (131072 / 8 context slots, 262144 / 8
 vocabulary ids), the shapes each GPU would run if the session were sharded.
@@ -100,7 +102,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=None, help="context rows of the oracle sample")
     ap.add_argument("--cpu-rounds", type=int, default=None, help="propose + sample rounds of the oracle sample")
     ap.add_argument("--no-stages", action="store_true",
-                    help="time only the dominant kernel (skip the attention, sampler, verify and flush stages)")
+                    help="time only the dominant kernel (skip the attention, sampler, verify, select and flush stages)")
     ap.add_argument("--no-spec-loop", action="store_true", help="skip the closed speculative round")
     ap.add_argument("--no-secondary", action="store_true",
                     help="default run: skip the batched workload timed after the long one")
@@ -126,6 +128,42 @@ class Stage:
         ms, launches = ctypes.c_double(), ctypes.c_int32()
         check(self.lib, self.lib.dflash_profile_end(self.ctx, ctypes.byref(ms), ctypes.byref(launches)))
         return ms.value, launches.value
+
+
+SEL_K, SEL_DS = 8, 64      # the selector stage's candidates per row and table width
+
+
+def select_stage(cfg, w_dev, lg, n, temperature, anchor, torch):
+    """The DFlash2 selector (dflash_select) on the block's drafted rows as
+    the last round left them: a drafter of this configuration with SEL_K
+    candidates per row and SEL_DS-wide selector tables (the workload's
+    weights plus two seeded tables), with the dense rows verification takes
+    when sampling.  Bytes: the rows' logits read once (and the dense rows
+    written when sampling)."""
+    from block_diffusion_drafter_fwd_amd import Drafter, select
+    c2 = cfg.replace(sel_candidates=SEL_K, sel_dim=SEL_DS)
+    dev = lg.device
+    gen = torch.Generator(device=dev).manual_seed(5)
+    w2 = dict(w_dev)
+    for k in ("sel_prev", "sel_next"):
+        w2[k] = (torch.randn((cfg.vocab, SEL_DS), generator=gen, device=dev) * 0.02).to(w_dev["embed"].dtype)
+    d2 = Drafter(c2, w2)
+    st2 = Stage(d2.lib, d2.ctx)
+    s2 = d2.session(cfg.window + cfg.block_size - 1 if cfg.window else cfg.block_size + 64)
+    lgc = lg.contiguous()
+    dense = temperature > 0
+    for r in range(3):
+        select([s2], [0, n], lgc, [anchor], temperature, r, dense=dense)
+    st2.begin("select")
+    for r in range(20):
+        select([s2], [0, n], lgc, [anchor], temperature, r, dense=dense)
+    ms, launches = st2.end()
+    s2.close()
+    d2.close()
+    avg = ms / 1e3 / max(1, launches)
+    sb = n * cfg.vocab * 4 * (2 if dense else 1)
+    return hbm_line(sb, avg, alg_bytes_per_launch=sb, avg_launch_us=round(avg * 1e6, 2), launches=launches,
+                    candidates=SEL_K, table_dim=SEL_DS, dense=dense)
 
 
 def hbm_line(alg_bytes, avg_s, **extra):
@@ -388,6 +426,8 @@ def bench_single(args, cfg, wl, w_dev, steps, warmup, torch, synth):
             vb = (n + 1) * cfg.vocab * 4 + (n * cfg.vocab * 4 if T > 0 else 0)
             kernels["verify"] = hbm_line(vb, avg, alg_bytes_per_launch=vb, avg_launch_us=round(avg * 1e6, 2),
                                          launches=l_v)
+        if cfg.dtype == "bf16":
+            kernels["select"] = select_stage(cfg, w_dev, logits[:n], n, wl.temperature, state["current"], torch)
         # the context-path GEMMs over one more prompt each (fresh sessions)
         rows = wl.commit_rows
         flops = {"flush_fc": 2.0 * rows * cfg.fc_in * cfg.hidden,

@@ -151,7 +151,7 @@ public:
 // Stages that can be timed.
 inline bool known_stage(const std::string& s) {
     return s == "unembed" || s == "attention" || s == "attention_partial" || s == "flush_fc" || s == "flush_kv" || s == "sampler" ||
-           s == "verify" || s == "layer_gemms";
+           s == "verify" || s == "layer_gemms" || s == "select";
 }
 
 // Defined by the backend translation unit that is linked in.

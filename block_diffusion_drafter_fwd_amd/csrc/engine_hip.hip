@@ -88,7 +88,7 @@ struct WsLayout {
     size_t ctx_stage, ctx_fc, ctx_c, ctx_x, ctx_kv;
     CtxBufs lane1;
     size_t blk_h, blk_x, blk_qkv, blk_q, blk_attn, blk_part, blk_mlp, blk_act;
-    size_t attn_o, attn_ml, part, bitmap, stats, stats2, sel;
+    size_t attn_o, attn_ml, part, bitmap, stats, stats2, sel, sel_prep;
     size_t total;
     int32_t r_ctx, r_blk, items_cap, nchunk_max, blk_slices;
 };
@@ -148,6 +148,7 @@ public:
         w.stats = put(16 * (size_t)w.r_blk * w.nchunk_max);
         w.stats2 = put(16 * (size_t)w.r_blk * w.nchunk_max);   // verification's second pass
         w.sel = put(c.sel_candidates ? 8 * (size_t)kSelMaxK * w.r_blk * w.nchunk_max : 0);
+        w.sel_prep = put(c.sel_candidates ? 4 * (size_t)kSelPrepStride * w.r_blk : 0);
         w.total = o;
         return w;
     }
@@ -971,6 +972,7 @@ int HipEngine::select(const std::vector<SessView>& sess, const int32_t* row_offs
     if (R > w.r_blk) return fail(DFLASH_E_CAPACITY, "selected rows exceed the workspace");
     std::vector<SeqDesc> descs(count);
     for (int32_t k = 0; k < count; ++k) descs[k] = desc_of(sess[k]);
+    Timed tm(this, "select", st);   // (the whole call, its table upload included)
     Tables tb;
     const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
     const size_t o_offs = tb.add(row_offsets, sizeof(int32_t) * (size_t)(count + 1));
@@ -985,6 +987,7 @@ int HipEngine::select(const std::vector<SessView>& sess, const int32_t* row_offs
     a.offs = (const int32_t*)(tab + o_offs);
     a.anchors = (const int32_t*)(tab + o_anch);
     a.cand = (float*)(base + w.sel);
+    a.prep = (float*)(base + w.sel_prep);
     a.tokens = tokens;
     a.cand_ids = cand_ids;
     a.cand_probs = cand_probs;

@@ -1070,12 +1070,14 @@ __global__ __launch_bounds__(64 * kVerWaves) void k_verify_final(VerifyArgs a) {
 // chunk's K best logits (value descending, id ascending), by K rounds of a
 // workgroup argmax over the 16 values each thread holds; with dense output
 // the chunk of the row's dense distribution is zeroed on the way.  Pass 2,
-// one wave per session, its rows in order: merge the chunks' candidates into
-// the row's K best, score candidate c by z(c) + <P[prev], Q[c]> (prev: the
-// anchor, then the token chosen at the row before), softmax over the K
-// candidates at temperature T and a Gumbel-max draw (u of rank j from
-// Philox4x64-10 counter (j div 4, position, round, 3), word j mod 4), or the
-// best score when T = 0; the choice is the next row's prev.
+// per row: merge the chunks' candidates into the row's K best and, as the
+// row's predecessor is one of the K candidates of the row before (the
+// anchor first), the bigram term <P[p], Q[c]> of every predecessor
+// candidate p and candidate c.  Pass 3, per session, its rows in order:
+// candidate c scores z(c) + the term of the row before's choice, softmax
+// over the K candidates at temperature T and a Gumbel-max draw (u of rank j
+// from Philox4x64-10 counter (j div 4, position, round, 3), word j mod 4),
+// or the best score when T = 0; the choice is the next row's predecessor.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
@@ -1142,117 +1144,187 @@ __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
     }
 }
 
-__global__ __launch_bounds__(64) void k_sel_walk(SelectArgs a) {
-    const int k = blockIdx.x, lane = threadIdx.x;
-    const SeqDesc sd = a.seqs[k];
-    const int r0 = a.offs[k], n = a.offs[k + 1] - r0;
+// The K best of row r over its chunks' candidates (rank j held by lane j of
+// the calling wave; ties to the lower id).
+__device__ __forceinline__ void sel_merge_row(const SelectArgs& a, int r, int lane, int& cid, float& cz) {
+    const float* ent = a.cand + (size_t)r * a.nchunk * kSelMaxK * 2;
     const int E = a.nchunk * a.K;                        // <= kSelMaxEntries: 16 entries per lane
-    const float inv_t = a.temperature > 0.f ? 1.f / a.temperature : 0.f;
-    int prev = a.anchors[k];
-    for (int i = 0; i < n; ++i) {
-        const int r = r0 + i;
-        const float* ent = a.cand + (size_t)r * a.nchunk * kSelMaxK * 2;
-        float ev[16];
-        int ei[16];
+    float ev[16];
+    int ei[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = lane + 64 * u;
-            if (e < E) {
-                const float* o = ent + ((size_t)(e / a.K) * kSelMaxK + e % a.K) * 2;
-                ev[u] = o[0];
-                ei[u] = __float_as_int(o[1]);
-            } else {
+    for (int u = 0; u < 16; ++u) {
+        const int e = lane + 64 * u;
+        if (e < E) {
+            const float* o = ent + ((size_t)(e / a.K) * kSelMaxK + e % a.K) * 2;
+            ev[u] = o[0];
+            ei[u] = __float_as_int(o[1]);
+        } else {
+            ev[u] = -INFINITY;
+            ei[u] = INT_MAX;
+        }
+    }
+    cid = INT_MAX;
+    cz = -INFINITY;
+    for (int j = 0; j < a.K; ++j) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (better(ev[u], ei[u], bv, bi)) {
+                bv = ev[u];
+                bi = ei[u];
+            }
+        wave_best(bv, bi);
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (ei[u] == bi) {
                 ev[u] = -INFINITY;
                 ei[u] = INT_MAX;
             }
+        if (lane == j) {
+            cid = bi;
+            cz = bv;
         }
-        // the row's K best, rank j held by lane j
-        int cid = INT_MAX;
-        float cz = -INFINITY;
-        for (int j = 0; j < a.K; ++j) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (better(ev[u], ei[u], bv, bi)) {
-                    bv = ev[u];
-                    bi = ei[u];
-                }
-            wave_best(bv, bi);
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (ei[u] == bi) {
-                    ev[u] = -INFINITY;
-                    ei[u] = INT_MAX;
-                }
-            if (lane == j) {
-                cid = bi;
-                cz = bv;
+    }
+}
+
+// Pass 2, one workgroup per drafted row (session k, position i): nothing a
+// row's choice depends on except its predecessor, and that is one of the
+// K candidates of the row before (the anchor at i = 0), so every row's
+// candidates and the bigram terms <P[p], Q[c]> for each predecessor
+// candidate p and candidate c are computed here, all rows at once.
+__global__ __launch_bounds__(256) void k_sel_prep(SelectArgs a) {
+    __shared__ int s_cid[kSelMaxK], s_pid[kSelMaxK];
+    __shared__ float s_cz[kSelMaxK];
+    __shared__ float s_p[kSelMaxK][kSelMaxDs + 1], s_q[kSelMaxK][kSelMaxDs + 1];
+    __shared__ int s_k;
+    const int r = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave == 0) {   // the row's session: offs[k] <= r < offs[k + 1]
+        int k = 0;
+        for (int k0 = 0; k0 < a.nseq; k0 += 64) {
+            const int kk = k0 + lane;
+            const bool hit = kk < a.nseq && a.offs[kk] <= r && r < a.offs[kk + 1];
+            const uint64_t m = __ballot(hit);
+            if (m) {
+                k = k0 + __ffsll((unsigned long long)m) - 1;
+                break;
             }
         }
-        // bigram scores <P[prev], Q[c]>: lanes over the Ds dimensions, one
-        // sum per candidate
-        float acc[kSelMaxK];
-#pragma unroll
-        for (int j = 0; j < kSelMaxK; ++j) acc[j] = 0.f;
-        for (int d = lane; d < a.Ds; d += 64) {
-            const float pd = ld_any(a.P, (size_t)prev * a.Ds + d, a.w_bf16);
-#pragma unroll
-            for (int j = 0; j < kSelMaxK; ++j) {
-                const int cj = __shfl(cid, j);
-                if (j < a.K) acc[j] += pd * ld_any(a.Q, (size_t)cj * a.Ds + d, a.w_bf16);
-            }
-        }
-        float s = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kSelMaxK; ++j) {
-            float t = acc[j];
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-            if (lane == j && j < a.K) s = cz + t;
-        }
-        float key = s, prob = 0.f;
-        if (a.temperature > 0.f) {
-            const float x = lane < a.K ? s * inv_t : -INFINITY;
-            float m = x;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            const float e = lane < a.K ? __expf(x - m) : 0.f;
-            float sum = e;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-            prob = e / sum;
-            uint64_t w[4] = {(uint64_t)(lane >> 2), (uint64_t)(i + 1), (uint64_t)a.round, 3};
-            philox4x64_10(w, sd.seed, sd.stream);
-            const uint64_t wj = (lane & 3) == 0 ? w[0] : (lane & 3) == 1 ? w[1] : (lane & 3) == 2 ? w[2] : w[3];
-            key = lane < a.K ? x - logf(-logf(u23(wj))) : -INFINITY;
-        } else if (lane >= a.K) {
-            key = -INFINITY;
-        }
-        float bk = key;
-        int br = lane < a.K ? lane : INT_MAX;
-        wave_best(bk, br);                               // ties: the lower rank
-        const int tok = __shfl(cid, br);
+        if (lane == 0) s_k = k;
+    }
+    __syncthreads();
+    const int k = s_k, i = r - a.offs[k];
+    const int Kp = i == 0 ? 1 : a.K;                     // predecessor candidates
+    if (wave == 0) {
+        int cid;
+        float cz;
+        sel_merge_row(a, r, lane, cid, cz);
         if (lane < a.K) {
-            a.cand_ids[(size_t)r * a.K + lane] = cid;
-            if (a.cand_probs && a.temperature > 0.f) a.cand_probs[(size_t)r * a.K + lane] = prob;
-            if (a.dense && a.temperature > 0.f) a.dense[(size_t)r * a.V + cid] = prob;
+            s_cid[lane] = cid;
+            s_cz[lane] = cz;
         }
-        if (lane == 0) a.tokens[r] = tok;
-        prev = tok;
+    } else if (wave == 1) {
+        if (i == 0) {
+            if (lane == 0) s_pid[0] = a.anchors[k];
+        } else {
+            int cid;
+            float cz;
+            sel_merge_row(a, r - 1, lane, cid, cz);
+            if (lane < a.K) s_pid[lane] = cid;
+        }
+    }
+    __syncthreads();
+    // the predecessor rows of P and the candidate rows of Q, as fp32 in LDS
+    for (int e = tid; e < (Kp + a.K) * a.Ds; e += 256) {
+        const int row = e / a.Ds, d = e - row * a.Ds;
+        if (row < Kp) s_p[row][d] = ld_any(a.P, (size_t)s_pid[row] * a.Ds + d, a.w_bf16);
+        else s_q[row - Kp][d] = ld_any(a.Q, (size_t)s_cid[row - Kp] * a.Ds + d, a.w_bf16);
+    }
+    __syncthreads();
+    float* o = a.prep + (size_t)r * kSelPrepStride;
+    if (tid < a.K) {
+        o[tid] = __int_as_float(s_cid[tid]);
+        o[kSelMaxK + tid] = s_cz[tid];
+    }
+    for (int pc = tid; pc < Kp * a.K; pc += 256) {
+        const int pi = pc / a.K, c = pc - pi * a.K;
+        float t = 0.f;
+        for (int d = 0; d < a.Ds; ++d) t += s_p[pi][d] * s_q[c][d];
+        o[2 * kSelMaxK + pi * kSelMaxK + c] = t;
+    }
+}
+
+// Pass 3, one workgroup per session: its rows' prepared candidates, logits
+// and bigram terms staged through LDS kSelWalkRows rows at a time, then one
+// wave walks the rows in order: score z + <P[prev], Q[c]> (the term for the
+// rank of the row before's choice), softmax over the K at T and a
+// Gumbel-max draw (u of rank j from Philox4x64-10 counter (j div 4, i + 1,
+// round, 3), word j mod 4), or the best score when T = 0; no memory access
+// is left in the chain from one row to the next.
+constexpr int kSelWalkRows = 32;
+__global__ __launch_bounds__(256) void k_sel_walk(SelectArgs a) {
+    __shared__ float sp[kSelWalkRows * kSelPrepStride];
+    const int k = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const SeqDesc sd = a.seqs[k];
+    const int r0 = a.offs[k], n = a.offs[k + 1] - r0;
+    const float inv_t = a.temperature > 0.f ? 1.f / a.temperature : 0.f;
+    int p = 0;                                           // rank of the row before's choice (the anchor: 0)
+    for (int i0 = 0; i0 < n; i0 += kSelWalkRows) {
+        const int m = min(kSelWalkRows, n - i0);
+        __syncthreads();
+        for (int e = tid; e < m * kSelPrepStride; e += 256) sp[e] = a.prep[(size_t)(r0 + i0) * kSelPrepStride + e];
+        __syncthreads();
+        if (wave != 0) continue;
+        for (int ii = 0; ii < m; ++ii) {
+            const int i = i0 + ii, r = r0 + i;
+            const float* q = sp + ii * kSelPrepStride;
+            const bool act = lane < a.K;
+            const int cid = act ? __float_as_int(q[lane]) : INT_MAX;
+            const float s = act ? q[kSelMaxK + lane] + q[2 * kSelMaxK + p * kSelMaxK + lane] : -INFINITY;
+            float key = s, prob = 0.f;
+            if (a.temperature > 0.f) {
+                const float x = act ? s * inv_t : -INFINITY;
+                float mx = x;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+                const float e = act ? __expf(x - mx) : 0.f;
+                float sum = e;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+                prob = e / sum;
+                uint64_t w[4] = {(uint64_t)(lane >> 2), (uint64_t)(i + 1), (uint64_t)a.round, 3};
+                philox4x64_10(w, sd.seed, sd.stream);
+                const uint64_t wj = (lane & 3) == 0 ? w[0] : (lane & 3) == 1 ? w[1] : (lane & 3) == 2 ? w[2] : w[3];
+                key = act ? x - logf(-logf(u23(wj))) : -INFINITY;
+            }
+            float bk = key;
+            int br = act ? lane : INT_MAX;
+            wave_best(bk, br);                               // ties: the lower rank
+            const int tok = __shfl(cid, br);
+            if (act) {
+                a.cand_ids[(size_t)r * a.K + lane] = cid;
+                if (a.cand_probs && a.temperature > 0.f) a.cand_probs[(size_t)r * a.K + lane] = prob;
+                if (a.dense && a.temperature > 0.f) a.dense[(size_t)r * a.V + cid] = prob;
+            }
+            if (lane == 0) a.tokens[r] = tok;
+            p = br;
+        }
     }
 }
 
 hipError_t select(const SelectArgs& a, hipStream_t st) {
     if (a.R <= 0 || a.nseq <= 0) return hipSuccess;
-    if (a.K < 1 || a.K > kSelMaxK || a.nchunk * a.K > kSelMaxEntries || a.chunk != 4096 || !a.seqs || !a.offs ||
-        !a.anchors)
+    if (a.K < 1 || a.K > kSelMaxK || a.Ds < 1 || a.Ds > kSelMaxDs || a.nchunk * a.K > kSelMaxEntries ||
+        a.chunk != 4096 || !a.seqs || !a.offs || !a.anchors || !a.prep)
         return hipErrorInvalidValue;
     if (a.dense) hipLaunchKernelGGL(k_sel_topk<true>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(k_sel_topk<false>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sel_walk, dim3(a.nseq), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_sel_prep, dim3(a.R), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sel_walk, dim3(a.nseq), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -192,6 +192,12 @@ struct VerifyArgs {
 // bigram scores against the previous choice, softmax / Gumbel-max).
 constexpr int kSelMaxK = 16;            // candidates per row, at most
 constexpr int kSelMaxEntries = 1024;    // chunk candidates merged per row (nchunk * K), at most
+constexpr int kSelMaxDs = 256;          // selector table width, at most
+// per row, written by the preparation pass and read by the walk: the row's
+// candidate ids (int bits) and logits by rank, then the bigram terms
+// <P[p], Q[c]> for candidate rank p of the row before (the anchor: p = 0)
+// and rank c of this row, p-major
+constexpr int kSelPrepStride = 2 * kSelMaxK + kSelMaxK * kSelMaxK;
 struct SelectArgs {
     const float* logits;      // [R][V]
     const void* P;            // [V][Ds] predecessor table (bf16 or fp32)
@@ -204,6 +210,7 @@ struct SelectArgs {
     int32_t* cand_ids;        // [R][K]
     float* cand_probs;        // [R][K] or null
     float* dense;             // [R][V] or null: zeroed, then the candidates' probabilities
+    float* prep;              // [R][kSelPrepStride]
     int32_t V, R, nseq, K, Ds, chunk, nchunk, round, w_bf16, pad;
     float temperature;
 };

@@ -394,7 +394,8 @@ int dflash_cache_read(const dflash_session* s, int32_t layer, int32_t position0,
  * lm_head GEMM), "attention" (partials + combine), "attention_partial" (the
  * partials kernel alone, bf16), "flush_fc" and "flush_kv" (the context-path
  * GEMMs), "layer_gemms" (the block path's per-layer projections: q|k|v(|g),
- * o_proj, gate|up, down), "sampler", "verify" (one pair per dflash_verify).
+ * o_proj, gate|up, down), "sampler", "verify" (one pair per dflash_verify),
+ * "select" (one pair per dflash_select).
  * dflash_profile_end waits for the
  * recorded events and returns the summed kernel time (ms) and the number of
  * launches since dflash_profile_begin.  Errors: E_ARG (unknown stage),
