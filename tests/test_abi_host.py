@@ -659,3 +659,19 @@ def test_selector_tables_and_state(host):
     assert host.dflash_select(hs2, 1, offs, out.ctypes.data, cur, byref(p), out.ctypes.data, out.ctypes.data,
                               None, None) == abi.E_STATE
     host.dflash_destroy(ctx2)
+
+
+def test_profile_stages(host):
+    """Every stage the header documents opens and closes (no launches on the
+    trace backend: zero time, zero launches); an unknown stage is E_ARG."""
+    fm = FakeModel(host)
+    rc, ctx = fm.create()
+    assert rc == 0
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    for stage in ("unembed", "attention", "attention_partial", "flush_fc", "flush_kv", "layer_gemms", "sampler",
+                  "verify", "select"):
+        assert host.dflash_profile_begin(ctx, stage.encode()) == 0, stage
+        assert host.dflash_profile_end(ctx, ctypes.byref(ms), ctypes.byref(n)) == 0, stage
+        assert n.value == 0
+    assert host.dflash_profile_begin(ctx, b"no_such_stage") == abi.E_ARG
+    host.dflash_destroy(ctx)
