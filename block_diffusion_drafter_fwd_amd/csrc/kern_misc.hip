@@ -1103,10 +1103,16 @@ __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     const float* z = a.logits + (size_t)r * a.V;
     float v[16];
+    // the thread's tokens not yet taken: every one stays eligible, -inf
+    // included (a NaN logit counts as -inf), so each chunk hands out
+    // min(K, its tokens) real ids and a row's K best are always real tokens
+    uint32_t live = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int t = t_lo + tid + 256 * j;
-        v[j] = t < t_hi ? z[t] : -INFINITY;
+        const float x = t < t_hi ? z[t] : -INFINITY;
+        v[j] = x == x ? x : -INFINITY;
+        if (t < t_hi) live |= 1u << j;
         if (DENSE && t < t_hi) a.dense[(size_t)r * a.V + t] = 0.f;
     }
     for (int k = 0; k < a.K; ++k) {
@@ -1114,7 +1120,7 @@ __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
         int bi = INT_MAX;
 #pragma unroll
         for (int j = 0; j < 16; ++j)                     // ids ascend with j: ties keep the lower id
-            if (v[j] > bv) {
+            if (((live >> j) & 1u) && (v[j] > bv || bi == INT_MAX)) {
                 bv = v[j];
                 bi = t_lo + tid + 256 * j;
             }
@@ -1135,7 +1141,7 @@ __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            if (wi == t_lo + tid + 256 * j) v[j] = -INFINITY;
+            if (wi == t_lo + tid + 256 * j) live &= ~(1u << j);
         if (tid == 0) {
             float* o = a.cand + (((size_t)r * a.nchunk + c) * kSelMaxK + k) * 2;
             o[0] = wv;

@@ -295,7 +295,9 @@ int dflash_sample(dflash_session* const* sessions, int32_t count, const int32_t*
  * row_offsets[k+1]) of logits (device fp32 [R, V], as dflash_propose returns
  * them) are session k's drafted rows 1..n_k and current[k] (host) its anchor.
  * Position i's candidates are the K = sel_candidates highest logits of its
- * row (ties to the lower id), ranked by logit; candidate c scores
+ * row (ties to the lower id), ranked by logit (a NaN logit counts as -inf,
+ * and a row with fewer than K finite logits is filled with the lowest ids
+ * among the rest: they score -inf and get probability 0); candidate c scores
  * s_i(c) = z_i(c) + <sel_prev[t_{i-1}], sel_next[c]> with t_0 the anchor and
  * t_{i-1} the token chosen at position i-1 (so the positions are chosen in
  * order); the position's distribution is softmax over its candidates of

@@ -169,3 +169,48 @@ def test_select_on_drafted_rows_matches_oracle(cuda):
         o.commit_block()
     print(f"[select e2e] tokens compared {compared}, ties {ties}, candidate rows {cand_rows}", flush=True)
     assert compared >= 1 and cand_rows >= 4
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+def test_select_rows_with_fewer_finite_logits_than_candidates(cuda, temperature):
+    """Rows masked to -inf except for fewer than K tokens (a caller's banned
+    tokens; one row with a single finite logit, one row whose finite logits
+    all sit in the last, partial 4096-token chunk) and, greedy only, a row
+    with no finite logit at all.  The K best are still K real tokens: the
+    finite ones by value, then the lowest ids among the -inf ones, as the
+    oracle's value-then-id order gives them; a -inf candidate gets
+    probability 0 and is never drawn."""
+    from block_diffusion_drafter_fwd_amd import select
+    V, K = 9001, 8
+    cfg = synth.config("qwen", layers=1, hidden=256, intermediate=768, target_hidden=64, block_size=8).replace(
+        vocab=V, sel_candidates=K, sel_dim=64)
+    d, w = _drafter(cfg, seed=5, table_scale=0.6)
+    # finite tokens per row (all < K); greedy adds a row with none
+    finite = [5, 1, 7, 3, 6] + ([] if temperature > 0 else [0])
+    rows = [3, 2] + ([] if temperature > 0 else [1])
+    sessions = [d.session(64, seed=40 + k, stream_id=k) for k in range(len(rows))]
+    rng = np.random.default_rng(17)
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    logits = np.full((int(offs[-1]), V), -np.inf, dtype=np.float32)
+    for r, m in enumerate(finite):
+        lo = 8192 if r == 3 else 0                        # row 3: only the last chunk's tokens
+        ids = rng.choice(np.arange(lo, V), size=m, replace=False)
+        logits[r, ids] = rng.normal(scale=1.5, size=m).astype(np.float32)
+    anchors = [int(x) for x in rng.integers(0, V, len(rows))]
+    tok, cid, cpr, den = select(sessions, offs, torch.from_numpy(logits).cuda(), anchors, temperature, 2, dense=True)
+    tok, cid = tok.cpu().numpy(), cid.cpu().numpy()
+    assert np.all((cid >= 0) & (cid < V))
+    for k, n in enumerate(rows):
+        sl = slice(offs[k], offs[k + 1])
+        t_o, c_o, p_o, s_o = select_block(logits[sl], anchors[k], w["sel_prev"], w["sel_next"], K, temperature,
+                                          40 + k, k, 2)
+        pr = cpr.cpu().numpy()[sl] if temperature > 0 else None
+        rep = {"ties": 0}
+        assert _compare(rep, tok[sl], cid[sl], pr, t_o, c_o, p_o, s_o, temperature) == n, rep
+        for i in range(n):
+            r = offs[k] + i
+            assert np.isfinite(logits[r, tok[r]]) or finite[r] == 0
+            if temperature > 0:
+                assert np.all(pr[i][~np.isfinite(logits[r, cid[r]])] == 0.0)
+                row = den.cpu().numpy()[r]
+                assert np.count_nonzero(row) == finite[r] and abs(row.sum() - 1.0) < 1e-5
