@@ -1040,7 +1040,9 @@ __global__ __launch_bounds__(64 * kVerWaves) void k_verify_final(VerifyArgs a) {
         bool ok = false;
         if (j < n) {
             const int x = a.draft_ids[off + j];
-            if (a.temperature == 0.f) {
+            if (x < 0 || x >= a.V) {
+                ok = false;              // outside the vocabulary: never accepted, nothing loaded
+            } else if (a.temperature == 0.f) {
                 ok = s.idx == x;
             } else {
                 const float p = __expf(a.target[(size_t)(r0 + j) * a.V + x] / a.temperature - s.m) / s.l;

@@ -336,6 +336,8 @@ int dflash_select(dflash_session* const* sessions, int32_t count, const int32_t*
  *     the target.  Draws are keyed by the session's (seed, stream_id):
  *     u_i from Philox4x64-10 counter (0, i, round, 1), the draw from row a by
  *     Gumbel-max with counter (t div 4, a, round, 2).
+ * A draft id outside [0, V) is never accepted (greedy or not; nothing is read
+ * at it) and next_k is drawn at its row as after any rejection.
  * accepted_out and next_out are device int32 [count].  The session state is
  * not touched (commit the accepted run with dflash_committed).  Sessions
  * share context, workspace and stream.  Errors: E_ARG. */

@@ -22,7 +22,11 @@ readings taken here:
   bits of word 0 at counter (0, i, round, 1)) + 1/2, times 2**-23; ``next``
   from row a by Gumbel-max over the row's scores (log of the residual mass,
   or row/T for the bonus row) with g_t from counter (t div 4, a, round, 2),
-  word t mod 4, mapped to u as the drafter's sampler maps its draws.
+  word t mod 4, mapped to u as the drafter's sampler maps its draws;
+* a draft id outside [0, V) (the pages' drafts are always tokens; the call
+  takes the ids as device data it cannot check first) is never accepted, as
+  a draft the target gives probability zero would not be, and ``next`` is
+  then drawn at that row as after any rejection.
 """
 from __future__ import annotations
 
@@ -78,8 +82,12 @@ def verify_block(target: np.ndarray, draft_ids, draft_probs: Optional[np.ndarray
         return a, int(np.argmax(target[a])), info
     a = 0
     p_rows = [softmax(target[i], temperature) for i in range(n + 1)]
+    V = target.shape[1]
     while a < n:
         x = int(draft_ids[a])
+        if not 0 <= x < V:
+            info["tests"].append((np.inf, 0.0))
+            break
         p, q = p_rows[a][x], float(draft_probs[a][x])
         u = accept_uniform(seed, stream, rnd, a)
         info["tests"].append((u * q, p))

@@ -105,6 +105,58 @@ def test_sampling_verify_matches_oracle(setup, rnd, temperature):
     assert compared >= 3 and skipped <= 1, (compared, skipped)
 
 
+@pytest.mark.parametrize("temperature", [0.0, 0.8])
+def test_out_of_vocabulary_draft_ids_are_rejected_like_the_oracle(setup, temperature):
+    """Draft ids outside [0, V) (-1, V, V + 1000) at the first, a middle and
+    the last drafted row of different sessions: the draft is rejected there
+    without reading the target or draft rows at that id, and the correction
+    is drawn as after any rejection (the oracle's reading)."""
+    from block_diffusion_drafter_fwd_amd import verify
+    cfg, d, sessions = setup
+    rng = np.random.default_rng(21)
+    offs = _offsets()
+    R = int(offs[-1])
+    target = rng.normal(scale=2.0, size=(R + len(DRAFTS), V)).astype(np.float32)
+    q = np.zeros((max(1, R), V), np.float32)
+    ids = np.zeros(max(1, R), np.int32)
+    bad = {0: (0, -1), 2: (1, V), 3: (6, V + 1000), 4: (4, -7)}        # session: (row, id)
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        for i in range(n):
+            if temperature > 0:
+                # before the bad row the draft proposes from the target itself
+                # (accepted); from it on from an unrelated distribution, so the
+                # residual the correction is drawn from is well away from zero
+                before = k in bad and i < bad[k][0]
+                qi = softmax(target[r0 + i], temperature) if before else softmax(rng.normal(scale=2.0, size=V), 1.0)
+                q[offs[k] + i] = qi.astype(np.float32)
+                qi = q[offs[k] + i].astype(np.float64)
+                ids[offs[k] + i] = int(rng.choice(V, p=qi / qi.sum()))
+            else:
+                ids[offs[k] + i] = int(np.argmax(target[r0 + i]))
+    for k, (i, x) in bad.items():
+        ids[offs[k] + i] = x
+    probs = torch.from_numpy(q).cuda() if temperature > 0 else None
+    acc, nxt = verify(sessions, offs, torch.from_numpy(target).cuda(), torch.from_numpy(ids).cuda(), probs,
+                      temperature, 5)
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    compared = 0
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        a, x, info = verify_block(target[r0:r0 + n + 1], ids[offs[k]:offs[k] + n],
+                                  q[offs[k]:offs[k] + n] if temperature > 0 else None, temperature, 100 + k, k, 5)
+        if k in bad:
+            assert acc[k] <= bad[k][0]
+        close_test = any(abs(uq - p) <= 1e-5 * max(uq, p, 1e-30) for uq, p in info["tests"] if np.isfinite(uq))
+        sc = np.sort(info["scores"][np.isfinite(info["scores"])])
+        if close_test or (temperature > 0 and sc.size > 1 and sc[-1] - sc[-2] < 1e-4):
+            continue
+        compared += 1
+        assert (acc[k], nxt[k]) == (a, x), (k, acc[k], nxt[k], a, x)
+        assert 0 <= nxt[k] < V
+    assert compared >= 4, compared
+
+
 def test_verify_rejects_sampling_without_draft_probabilities(setup):
     from block_diffusion_drafter_fwd_amd import DFlashError, verify
     cfg, d, sessions = setup

@@ -55,6 +55,31 @@ def test_zero_target_mass_is_rejected_and_never_emitted():
     assert seen == {0, 1, 3, 4, 5}                  # the residual is p_0 itself: uniform over the rest
 
 
+def test_out_of_vocabulary_draft_acts_as_a_zero_probability_draft():
+    """A draft id outside [0, V) is never accepted: the outcome equals that of
+    a real token y the target row gives probability 0 (its logit -inf) while
+    the draft distribution gives it mass, with the same rows otherwise (so the
+    residual the correction is drawn from is the same).  Greedy: the same as
+    any draft that is not the row's argmax."""
+    rng = np.random.default_rng(4)
+    V, y = 13, 6
+    for rnd in range(40):
+        z = rng.normal(size=(4, V)) * 1.5
+        z[1, y] = -np.inf
+        q = np.stack([softmax(rng.normal(size=V), 1.0) for _ in range(3)])
+        ids = [int(rng.choice(V, p=softmax(z[0], 0.8))), y, 2]
+        ref = verify_block(z, ids, q, 0.8, 7, 1, rnd)
+        assert ref[0] <= 1
+        for bad in (-1, V, V + 1000):
+            out = verify_block(z, [ids[0], bad, 2], q, 0.8, 7, 1, rnd)
+            assert out[:2] == ref[:2], (rnd, bad, out[:2], ref[:2])
+        zg = z.copy()
+        zg[1, y] = 0.0
+        gref = verify_block(zg, [int(np.argmax(zg[0])), (int(np.argmax(zg[1])) + 1) % V, 2], None, 0.0, 7, 1, rnd)
+        for bad in (-1, V):
+            assert verify_block(zg, [int(np.argmax(zg[0])), bad, 2], None, 0.0, 7, 1, rnd)[:2] == gref[:2] == (1, int(np.argmax(zg[1])))
+
+
 @pytest.mark.parametrize("temperature", [1.0, 0.6])
 def test_emitted_token_is_an_exact_draw_from_the_target(temperature):
     """n = 1: the first emitted token (the draft if accepted, else the
