@@ -1097,57 +1097,66 @@ __device__ __forceinline__ void wave_best(float& bv, int& bi) {
     }
 }
 
+// Order-preserving int32 image of a float (-0 taken as +0, as the float
+// comparison does): a > b as floats iff key(a) > key(b); -inf maps above
+// INT_MIN, which therefore marks a slot holding no token.
+__device__ __forceinline__ int sel_key(float f) {
+    const int u = __float_as_int(f + 0.f);
+    return u >= 0 ? u : u ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float sel_unkey(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
+constexpr int kSelGone = INT_MIN;
+// (key, id) as one int64 whose order is key first, then the lower id
+__device__ __forceinline__ long long sel_pack(int key, int id) {
+    return (long long)(((unsigned long long)(unsigned)key << 32) | (unsigned)(0x7FFFFFFF - id));
+}
+
 template <bool DENSE>
 __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
+    __shared__ long long sw[4];
     const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     const float* z = a.logits + (size_t)r * a.V;
-    float v[16];
-    // the thread's tokens not yet taken: every one stays eligible, -inf
-    // included (a NaN logit counts as -inf), so each chunk hands out
-    // min(K, its tokens) real ids and a row's K best are always real tokens
-    uint32_t live = 0;
+    // every token of the chunk stays eligible, -inf included (a NaN logit
+    // counts as -inf), so each chunk hands out min(K, its tokens) real ids
+    // and a row's K best are always real tokens; slots past the vocabulary
+    // and tokens already taken hold kSelGone, which no comparison picks
+    int kv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int t = t_lo + tid + 256 * j;
-        const float x = t < t_hi ? z[t] : -INFINITY;
-        v[j] = x == x ? x : -INFINITY;
-        if (t < t_hi) live |= 1u << j;
+        const float x = t < t_hi ? z[t] : 0.f;
+        kv[j] = t < t_hi ? sel_key(x == x ? x : -INFINITY) : kSelGone;
         if (DENSE && t < t_hi) a.dense[(size_t)r * a.V + t] = 0.f;
     }
     for (int k = 0; k < a.K; ++k) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
+        int bk = kSelGone, bi = INT_MAX;
 #pragma unroll
         for (int j = 0; j < 16; ++j)                     // ids ascend with j: ties keep the lower id
-            if (((live >> j) & 1u) && (v[j] > bv || bi == INT_MAX)) {
-                bv = v[j];
+            if (kv[j] > bk) {
+                bk = kv[j];
                 bi = t_lo + tid + 256 * j;
             }
-        wave_best(bv, bi);
-        if ((tid & 63) == 0) {
-            sv[wave] = bv;
-            si[wave] = bi;
-        }
-        __syncthreads();
-        float wv = sv[0];
-        int wi = si[0];
+        long long b = sel_pack(bk, bi);
 #pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (better(sv[w], si[w], wv, wi)) {
-                wv = sv[w];
-                wi = si[w];
-            }
+        for (int o = 32; o > 0; o >>= 1) {
+            const long long ob = __shfl_xor(b, o);
+            b = ob > b ? ob : b;
+        }
+        if ((tid & 63) == 0) sw[wave] = b;
         __syncthreads();
+        b = sw[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) b = sw[w] > b ? sw[w] : b;
+        __syncthreads();
+        const int wk = (int)(b >> 32), wi = 0x7FFFFFFF - (int)(unsigned)(b & 0xFFFFFFFFll);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            if (wi == t_lo + tid + 256 * j) live &= ~(1u << j);
+            if (wi == t_lo + tid + 256 * j) kv[j] = kSelGone;
         if (tid == 0) {
             float* o = a.cand + (((size_t)r * a.nchunk + c) * kSelMaxK + k) * 2;
-            o[0] = wv;
-            o[1] = __int_as_float(wi);
+            o[0] = wk == kSelGone ? -INFINITY : sel_unkey(wk);   // no token left: sorts last in the merge
+            o[1] = __int_as_float(wk == kSelGone ? INT_MAX : wi);
         }
     }
 }
