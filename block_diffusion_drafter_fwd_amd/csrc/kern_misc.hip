@@ -1081,22 +1081,6 @@ __global__ __launch_bounds__(64 * kVerWaves) void k_verify_final(VerifyArgs a) {
 // from Philox4x64-10 counter (j div 4, position, round, 3), word j mod 4),
 // or the best score when T = 0; the choice is the next row's predecessor.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-}
-
 // Order-preserving int32 image of a float (-0 taken as +0, as the float
 // comparison does): a > b as floats iff key(a) > key(b); -inf maps above
 // INT_MIN, which therefore marks a slot holding no token.
@@ -1109,6 +1093,42 @@ constexpr int kSelGone = INT_MIN;
 // (key, id) as one int64 whose order is key first, then the lower id
 __device__ __forceinline__ long long sel_pack(int key, int id) {
     return (long long)(((unsigned long long)(unsigned)key << 32) | (unsigned)(0x7FFFFFFF - id));
+}
+__device__ __forceinline__ int sel_pack_key(long long b) { return (int)(b >> 32); }
+__device__ __forceinline__ int sel_pack_id(long long b) { return 0x7FFFFFFF - (int)(unsigned)(b & 0xFFFFFFFFll); }
+constexpr long long kSelNone = -0x7FFFFFFFFFFFFFFFll - 1;   // sel_pack(kSelGone, INT_MAX): below every real entry
+
+// Wave maxima of packed entries by DPP lane moves (no LDS round trip per
+// step): quad swaps, half-row and row mirrors give every lane of a 16-lane
+// row its row's maximum; two row broadcasts carry rows 0-2 into row 3.  The
+// whole wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ long long sel_dpp_max(long long v) {
+    const int lo = (int)(unsigned)v, hi = (int)(v >> 32);
+    const int lo2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+    const int hi2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+    const long long o = (long long)(((unsigned long long)(unsigned)hi2 << 32) | (unsigned)lo2);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ long long sel_lane(long long v, int l) {
+    const int lo = __builtin_amdgcn_readlane((int)(unsigned)v, l), hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ long long sel_row_max(long long v) {   // lanes 0..15, returned to every lane
+    v = sel_dpp_max<0xB1, 0xF>(v);      // quad_perm [1, 0, 3, 2]
+    v = sel_dpp_max<0x4E, 0xF>(v);      // quad_perm [2, 3, 0, 1]
+    v = sel_dpp_max<0x141, 0xF>(v);     // row_half_mirror
+    v = sel_dpp_max<0x140, 0xF>(v);     // row_mirror
+    return sel_lane(v, 0);
+}
+__device__ __forceinline__ long long sel_wave_max(long long v) {  // all 64 lanes, returned to every lane
+    v = sel_dpp_max<0xB1, 0xF>(v);
+    v = sel_dpp_max<0x4E, 0xF>(v);
+    v = sel_dpp_max<0x141, 0xF>(v);
+    v = sel_dpp_max<0x140, 0xF>(v);
+    v = sel_dpp_max<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+    v = sel_dpp_max<0x143, 0xC>(v);     // row_bcast:31 into rows 2 and 3
+    return sel_lane(v, 63);
 }
 
 template <bool DENSE>
@@ -1137,19 +1157,14 @@ __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
                 bk = kv[j];
                 bi = t_lo + tid + 256 * j;
             }
-        long long b = sel_pack(bk, bi);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const long long ob = __shfl_xor(b, o);
-            b = ob > b ? ob : b;
-        }
+        long long b = sel_wave_max(sel_pack(bk, bi));
         if ((tid & 63) == 0) sw[wave] = b;
         __syncthreads();
         b = sw[0];
 #pragma unroll
         for (int w = 1; w < 4; ++w) b = sw[w] > b ? sw[w] : b;
         __syncthreads();
-        const int wk = (int)(b >> 32), wi = 0x7FFFFFFF - (int)(unsigned)(b & 0xFFFFFFFFll);
+        const int wk = sel_pack_key(b), wi = sel_pack_id(b);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             if (wi == t_lo + tid + 256 * j) kv[j] = kSelGone;
@@ -1162,45 +1177,33 @@ __global__ __launch_bounds__(256) void k_sel_topk(SelectArgs a) {
 }
 
 // The K best of row r over its chunks' candidates (rank j held by lane j of
-// the calling wave; ties to the lower id).
+// the calling wave; ties to the lower id).  The whole wave calls it.
 __device__ __forceinline__ void sel_merge_row(const SelectArgs& a, int r, int lane, int& cid, float& cz) {
     const float* ent = a.cand + (size_t)r * a.nchunk * kSelMaxK * 2;
     const int E = a.nchunk * a.K;                        // <= kSelMaxEntries: 16 entries per lane
-    float ev[16];
-    int ei[16];
+    long long eb[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int e = lane + 64 * u;
+        eb[u] = kSelNone;
         if (e < E) {
             const float* o = ent + ((size_t)(e / a.K) * kSelMaxK + e % a.K) * 2;
-            ev[u] = o[0];
-            ei[u] = __float_as_int(o[1]);
-        } else {
-            ev[u] = -INFINITY;
-            ei[u] = INT_MAX;
+            const int id = __float_as_int(o[1]);
+            if (id != INT_MAX) eb[u] = sel_pack(sel_key(o[0]), id);
         }
     }
     cid = INT_MAX;
     cz = -INFINITY;
     for (int j = 0; j < a.K; ++j) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
+        long long b = kSelNone;
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-            if (better(ev[u], ei[u], bv, bi)) {
-                bv = ev[u];
-                bi = ei[u];
-            }
-        wave_best(bv, bi);
+        for (int u = 0; u < 16; ++u) b = eb[u] > b ? eb[u] : b;
+        b = sel_wave_max(b);
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-            if (ei[u] == bi) {
-                ev[u] = -INFINITY;
-                ei[u] = INT_MAX;
-            }
+        for (int u = 0; u < 16; ++u) eb[u] = eb[u] == b ? kSelNone : eb[u];
         if (lane == j) {
-            cid = bi;
-            cz = bv;
+            cid = sel_pack_id(b);
+            cz = sel_unkey(sel_pack_key(b));
         }
     }
 }
@@ -1271,61 +1274,76 @@ __global__ __launch_bounds__(256) void k_sel_prep(SelectArgs a) {
     }
 }
 
-// Pass 3, one workgroup per session: its rows' prepared candidates, logits
-// and bigram terms staged through LDS kSelWalkRows rows at a time, then one
-// wave walks the rows in order: score z + <P[prev], Q[c]> (the term for the
-// rank of the row before's choice), softmax over the K at T and a
-// Gumbel-max draw (u of rank j from Philox4x64-10 counter (j div 4, i + 1,
-// round, 3), word j mod 4), or the best score when T = 0; no memory access
-// is left in the chain from one row to the next.
+// Pass 3, one workgroup per session, its rows kSelWalkRows at a time: the
+// prepared rows are staged in LDS and the Gumbel noise of every (row, rank)
+// is drawn at once (u of rank j from Philox4x64-10 counter (j div 4, i + 1,
+// round, 3), word j mod 4); then one wave walks the rows in order, lane c
+// scoring candidate c as z + <P[prev], Q[c]> (the term of the rank chosen at
+// the row before), at T > 0 divided by T plus its noise, and the best by a
+// DPP maximum (the lower rank on a tie): that maximum is all the chain from
+// one row to the next holds.  All threads then write the rows' outputs: the
+// candidate ids, the chosen token and, at T > 0, the softmax over the K of
+// score / T as probabilities and dense rows.
 constexpr int kSelWalkRows = 32;
 __global__ __launch_bounds__(256) void k_sel_walk(SelectArgs a) {
     __shared__ float sp[kSelWalkRows * kSelPrepStride];
+    __shared__ float sg[kSelWalkRows * kSelMaxK];
+    __shared__ int sch[kSelWalkRows + 1];   // rank chosen at each row of the chunk; [0]: at the row before it
     const int k = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const SeqDesc sd = a.seqs[k];
     const int r0 = a.offs[k], n = a.offs[k + 1] - r0;
-    const float inv_t = a.temperature > 0.f ? 1.f / a.temperature : 0.f;
+    const bool sampling = a.temperature > 0.f;
+    const float inv_t = sampling ? 1.f / a.temperature : 0.f;
+    const int K = a.K, nq = (K + 3) >> 2;
     int p = 0;                                           // rank of the row before's choice (the anchor: 0)
     for (int i0 = 0; i0 < n; i0 += kSelWalkRows) {
         const int m = min(kSelWalkRows, n - i0);
         __syncthreads();
         for (int e = tid; e < m * kSelPrepStride; e += 256) sp[e] = a.prep[(size_t)(r0 + i0) * kSelPrepStride + e];
-        __syncthreads();
-        if (wave != 0) continue;
-        for (int ii = 0; ii < m; ++ii) {
-            const int i = i0 + ii, r = r0 + i;
-            const float* q = sp + ii * kSelPrepStride;
-            const bool act = lane < a.K;
-            const int cid = act ? __float_as_int(q[lane]) : INT_MAX;
-            const float s = act ? q[kSelMaxK + lane] + q[2 * kSelMaxK + p * kSelMaxK + lane] : -INFINITY;
-            float key = s, prob = 0.f;
-            if (a.temperature > 0.f) {
-                const float x = act ? s * inv_t : -INFINITY;
-                float mx = x;
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-                const float e = act ? __expf(x - mx) : 0.f;
-                float sum = e;
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-                prob = e / sum;
-                uint64_t w[4] = {(uint64_t)(lane >> 2), (uint64_t)(i + 1), (uint64_t)a.round, 3};
+        if (sampling)
+            for (int e = tid; e < m * nq; e += 256) {
+                const int ii = e / nq, qd = e - ii * nq;
+                uint64_t w[4] = {(uint64_t)qd, (uint64_t)(i0 + ii + 1), (uint64_t)a.round, 3};
                 philox4x64_10(w, sd.seed, sd.stream);
-                const uint64_t wj = (lane & 3) == 0 ? w[0] : (lane & 3) == 1 ? w[1] : (lane & 3) == 2 ? w[2] : w[3];
-                key = act ? x - logf(-logf(u23(wj))) : -INFINITY;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (4 * qd + jj < K) sg[ii * kSelMaxK + 4 * qd + jj] = -logf(-logf(u23(w[jj])));
             }
-            float bk = key;
-            int br = act ? lane : INT_MAX;
-            wave_best(bk, br);                               // ties: the lower rank
-            const int tok = __shfl(cid, br);
-            if (act) {
-                a.cand_ids[(size_t)r * a.K + lane] = cid;
-                if (a.cand_probs && a.temperature > 0.f) a.cand_probs[(size_t)r * a.K + lane] = prob;
-                if (a.dense && a.temperature > 0.f) a.dense[(size_t)r * a.V + cid] = prob;
+        if (tid == 0) sch[0] = p;
+        __syncthreads();
+        if (wave == 0) {                                 // the whole wave: the DPP maximum needs every lane
+            const bool act = lane < K;
+            for (int ii = 0; ii < m; ++ii) {
+                const float* q = sp + ii * kSelPrepStride;
+                long long b = kSelNone;
+                if (act) {
+                    const float sc = q[kSelMaxK + lane] + q[2 * kSelMaxK + p * kSelMaxK + lane];
+                    b = sel_pack(sel_key(sampling ? sc * inv_t + sg[ii * kSelMaxK + lane] : sc), lane);
+                }
+                p = sel_pack_id(sel_row_max(b));
+                if (lane == 0) sch[ii + 1] = p;
             }
-            if (lane == 0) a.tokens[r] = tok;
-            p = br;
         }
+        __syncthreads();
+        for (int e = tid; e < m * K; e += 256) {
+            const int ii = e / K, c = e - ii * K, r = r0 + i0 + ii;
+            const float* q = sp + ii * kSelPrepStride;
+            const int cid = __float_as_int(q[c]);
+            a.cand_ids[(size_t)r * K + c] = cid;
+            if (c == sch[ii + 1]) a.tokens[r] = cid;
+            if (sampling && (a.cand_probs || a.dense)) {
+                const float* tz = q + kSelMaxK;
+                const float* tb = q + 2 * kSelMaxK + sch[ii] * kSelMaxK;
+                float mx = -INFINITY;
+                for (int c2 = 0; c2 < K; ++c2) mx = fmaxf(mx, (tz[c2] + tb[c2]) * inv_t);
+                float sum = 0.f;
+                for (int c2 = 0; c2 < K; ++c2) sum += __expf((tz[c2] + tb[c2]) * inv_t - mx);
+                const float prob = __expf((tz[c] + tb[c]) * inv_t - mx) / sum;
+                if (a.cand_probs) a.cand_probs[(size_t)r * K + c] = prob;
+                if (a.dense) a.dense[(size_t)r * a.V + cid] = prob;
+            }
+        }
+        p = sch[m];
     }
 }
 
