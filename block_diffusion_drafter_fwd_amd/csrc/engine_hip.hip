@@ -973,19 +973,24 @@ int HipEngine::select(const std::vector<SessView>& sess, const int32_t* row_offs
     std::vector<SeqDesc> descs(count);
     for (int32_t k = 0; k < count; ++k) descs[k] = desc_of(sess[k]);
     Timed tm(this, "select", st);   // (the whole call, its table upload included)
-    Tables tb;
-    const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
-    const size_t o_offs = tb.add(row_offsets, sizeof(int32_t) * (size_t)(count + 1));
-    const size_t o_anch = tb.add(current, sizeof(int32_t) * (size_t)count);
-    char* tab = base + w.tables;
-    HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
     SelectArgs a{};
+    if (count == 1) {
+        a.seq0 = descs[0];            // seqs, offs and anchors stay null: no table upload
+        a.seq0.current = current[0];
+    } else {
+        Tables tb;
+        const size_t o_desc = tb.add(descs.data(), sizeof(SeqDesc) * descs.size());
+        const size_t o_offs = tb.add(row_offsets, sizeof(int32_t) * (size_t)(count + 1));
+        const size_t o_anch = tb.add(current, sizeof(int32_t) * (size_t)count);
+        char* tab = base + w.tables;
+        HIP_OK(upload(tab, tb.blob.data(), tb.blob.size(), st));
+        a.seqs = (const SeqDesc*)(tab + o_desc);
+        a.offs = (const int32_t*)(tab + o_offs);
+        a.anchors = (const int32_t*)(tab + o_anch);
+    }
     a.logits = logits;
     a.P = m_.sel_prev;
     a.Q = m_.sel_next;
-    a.seqs = (const SeqDesc*)(tab + o_desc);
-    a.offs = (const int32_t*)(tab + o_offs);
-    a.anchors = (const int32_t*)(tab + o_anch);
     a.cand = (float*)(base + w.sel);
     a.prep = (float*)(base + w.sel_prep);
     a.tokens = tokens;

@@ -1208,6 +1208,13 @@ __device__ __forceinline__ void sel_merge_row(const SelectArgs& a, int r, int la
     }
 }
 
+// a call's sessions: from its tables, or one session from the arguments
+__device__ __forceinline__ int sel_off(const SelectArgs& a, int k) { return a.offs ? a.offs[k] : (k == 0 ? 0 : a.R); }
+__device__ __forceinline__ SeqDesc sel_seq(const SelectArgs& a, int k) { return a.seqs ? a.seqs[k] : a.seq0; }
+__device__ __forceinline__ int sel_anchor(const SelectArgs& a, int k) {
+    return a.anchors ? a.anchors[k] : a.seq0.current;
+}
+
 // Pass 2, one workgroup per drafted row (session k, position i): nothing a
 // row's choice depends on except its predecessor, and that is one of the
 // K candidates of the row before (the anchor at i = 0), so every row's
@@ -1221,7 +1228,7 @@ __global__ __launch_bounds__(256) void k_sel_prep(SelectArgs a) {
     const int r = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (wave == 0) {   // the row's session: offs[k] <= r < offs[k + 1]
         int k = 0;
-        for (int k0 = 0; k0 < a.nseq; k0 += 64) {
+        for (int k0 = 0; a.offs && k0 < a.nseq; k0 += 64) {
             const int kk = k0 + lane;
             const bool hit = kk < a.nseq && a.offs[kk] <= r && r < a.offs[kk + 1];
             const uint64_t m = __ballot(hit);
@@ -1233,7 +1240,7 @@ __global__ __launch_bounds__(256) void k_sel_prep(SelectArgs a) {
         if (lane == 0) s_k = k;
     }
     __syncthreads();
-    const int k = s_k, i = r - a.offs[k];
+    const int k = s_k, i = r - sel_off(a, k);
     const int Kp = i == 0 ? 1 : a.K;                     // predecessor candidates
     if (wave == 0) {
         int cid;
@@ -1245,7 +1252,7 @@ __global__ __launch_bounds__(256) void k_sel_prep(SelectArgs a) {
         }
     } else if (wave == 1) {
         if (i == 0) {
-            if (lane == 0) s_pid[0] = a.anchors[k];
+            if (lane == 0) s_pid[0] = sel_anchor(a, k);
         } else {
             int cid;
             float cz;
@@ -1290,8 +1297,8 @@ __global__ __launch_bounds__(256) void k_sel_walk(SelectArgs a) {
     __shared__ float sg[kSelWalkRows * kSelMaxK];
     __shared__ int sch[kSelWalkRows + 1];   // rank chosen at each row of the chunk; [0]: at the row before it
     const int k = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const SeqDesc sd = a.seqs[k];
-    const int r0 = a.offs[k], n = a.offs[k + 1] - r0;
+    const SeqDesc sd = sel_seq(a, k);
+    const int r0 = sel_off(a, k), n = sel_off(a, k + 1) - r0;
     const bool sampling = a.temperature > 0.f;
     const float inv_t = sampling ? 1.f / a.temperature : 0.f;
     const int K = a.K, nq = (K + 3) >> 2;
@@ -1350,7 +1357,7 @@ __global__ __launch_bounds__(256) void k_sel_walk(SelectArgs a) {
 hipError_t select(const SelectArgs& a, hipStream_t st) {
     if (a.R <= 0 || a.nseq <= 0) return hipSuccess;
     if (a.K < 1 || a.K > kSelMaxK || a.Ds < 1 || a.Ds > kSelMaxDs || a.nchunk * a.K > kSelMaxEntries ||
-        a.chunk != 4096 || !a.seqs || !a.offs || !a.anchors || !a.prep)
+        a.chunk != 4096 || !a.prep || (a.seqs ? !a.offs || !a.anchors : a.nseq != 1 || a.offs || a.anchors))
         return hipErrorInvalidValue;
     if (a.dense) hipLaunchKernelGGL(k_sel_topk<true>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(k_sel_topk<false>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);

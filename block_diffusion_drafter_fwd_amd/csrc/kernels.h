@@ -202,7 +202,7 @@ struct SelectArgs {
     const float* logits;      // [R][V]
     const void* P;            // [V][Ds] predecessor table (bf16 or fp32)
     const void* Q;            // [V][Ds] candidate table
-    const SeqDesc* seqs;      // [nseq]: seed, stream
+    const SeqDesc* seqs;      // [nseq]: seed, stream (null with offs and anchors: one session, seq0)
     const int32_t* offs;      // [nseq + 1] row offsets
     const int32_t* anchors;   // [nseq]
     float* cand;              // [R][nchunk][kSelMaxK][2]: chunk top-K (value, id bits)
@@ -213,6 +213,7 @@ struct SelectArgs {
     float* prep;              // [R][kSelPrepStride]
     int32_t V, R, nseq, K, Ds, chunk, nchunk, round, w_bf16, pad;
     float temperature;
+    SeqDesc seq0;             // one session (seqs null): rows 0..R-1, anchor seq0.current
 };
 
 struct UploadArgs {

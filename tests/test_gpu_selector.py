@@ -214,3 +214,30 @@ def test_select_rows_with_fewer_finite_logits_than_candidates(cuda, temperature)
                 assert np.all(pr[i][~np.isfinite(logits[r, cid[r]])] == 0.0)
                 row = den.cpu().numpy()[r]
                 assert np.count_nonzero(row) == finite[r] and abs(row.sum() - 1.0) < 1e-5
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.7])
+def test_one_session_select_equals_the_same_session_in_a_batch(cuda, temperature):
+    """A one-session call (its descriptor and anchor in the kernel arguments,
+    no table upload) gives bit for bit what the same session gets inside a
+    four-session call: tokens, candidate ids, probabilities and dense rows."""
+    from block_diffusion_drafter_fwd_amd import select
+    V, K = 9001, 8
+    cfg = synth.config("qwen", layers=1, hidden=256, intermediate=768, target_hidden=64, block_size=8).replace(
+        vocab=V, sel_candidates=K, sel_dim=64)
+    d, w = _drafter(cfg, seed=6, table_scale=0.6)
+    sessions = [d.session(64, seed=50 + k, stream_id=k) for k in range(len(ROWS))]
+    rng = np.random.default_rng(31)
+    offs = np.concatenate([[0], np.cumsum(ROWS)]).astype(np.int32)
+    logits = torch.from_numpy(rng.normal(scale=1.5, size=(int(offs[-1]), V)).astype(np.float32)).cuda()
+    anchors = [int(x) for x in rng.integers(0, V, len(ROWS))]
+    tok, cid, cpr, den = select(sessions, offs, logits, anchors, temperature, 4, dense=True)
+    for k, n in enumerate(ROWS):
+        if n == 0:
+            continue
+        sl = slice(int(offs[k]), int(offs[k + 1]))
+        t1, c1, p1, d1 = select([sessions[k]], [0, n], logits[sl].contiguous(), [anchors[k]], temperature, 4,
+                                dense=True)
+        assert torch.equal(t1, tok[sl]) and torch.equal(c1, cid[sl])
+        if temperature > 0:
+            assert torch.equal(p1, cpr[sl]) and torch.equal(d1, den[sl])
