@@ -65,6 +65,7 @@ def _compare(rep, tok_g, cid_g, cpr_g, tok_o, cid_o, cpr_o, scores_o, temperatur
     compared = 0
     for i in range(n):
         sc = np.sort(np.asarray(scores_o[i], dtype=np.float64))
+        sc = sc[np.isfinite(sc)]                # (a row masked to -inf has no finite score to tie)
         if sc.size > 1 and sc[-1] - sc[-2] < 1e-4:
             rep["ties"] += 1
             break                           # the next positions depend on this choice
