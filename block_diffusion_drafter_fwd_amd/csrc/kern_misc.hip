@@ -689,14 +689,39 @@ __device__ __forceinline__ float penalized(const SampleArgs& a, const uint32_t* 
     return z;
 }
 
+// A lane's Stat moved by DPP (no LDS round trip); a lane with no source in
+// the move (rows left out of a row broadcast) gets the empty Stat, which
+// merges as nothing
+template <int CTRL, int ROWS>
+__device__ __forceinline__ Stat stat_dpp(const Stat& s) {
+    return Stat{__int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(s.m), CTRL, ROWS,
+                                                           0xF, false)),
+                __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s.l), CTRL, ROWS, 0xF, false)),
+                __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(s.best), CTRL,
+                                                           ROWS, 0xF, false)),
+                __builtin_amdgcn_update_dpp(0x7fffffff, s.idx, CTRL, ROWS, 0xF, false)};
+}
+
+// The wave's Stat, every lane getting lane 63's: quad swaps, half-row and
+// row mirrors merge each 16-lane row, two row broadcasts carry rows 0-2
+// into row 3.  The whole wave must be active.
+__device__ __forceinline__ Stat wave_stat(Stat s) {
+    stat_merge(s, stat_dpp<0xB1, 0xF>(s));    // quad_perm [1, 0, 3, 2]
+    stat_merge(s, stat_dpp<0x4E, 0xF>(s));    // quad_perm [2, 3, 0, 1]
+    stat_merge(s, stat_dpp<0x141, 0xF>(s));   // row_half_mirror
+    stat_merge(s, stat_dpp<0x140, 0xF>(s));   // row_mirror
+    stat_merge(s, stat_dpp<0x142, 0xA>(s));   // row_bcast:15 into rows 1 and 3
+    stat_merge(s, stat_dpp<0x143, 0xC>(s));   // row_bcast:31 into rows 2 and 3
+    return Stat{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.m), 63)),
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.l), 63)),
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.best), 63)),
+                __builtin_amdgcn_readlane(s.idx, 63)};
+}
+
 __device__ Stat block_stat(Stat s) {
     __shared__ float sm[4], sl[4], sb[4];
     __shared__ int si[4];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        Stat b{__shfl_xor(s.m, o), __shfl_xor(s.l, o), __shfl_xor(s.best, o), __shfl_xor(s.idx, o)};
-        stat_merge(s, b);
-    }
+    s = wave_stat(s);
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     __syncthreads();
     if (l == 0) {
@@ -813,11 +838,7 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
             const float* o = a.stats + ((size_t)r * a.nchunk + j) * 4;
             stat_merge(s, Stat{o[0], o[1], o[2], __float_as_int(o[3])});
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            Stat b{__shfl_xor(s.m, o), __shfl_xor(s.l, o), __shfl_xor(s.best, o), __shfl_xor(s.idx, o)};
-            stat_merge(s, b);
-        }
+        s = wave_stat(s);
         if (threadIdx.x == 0) {
             tot[0] = s.m;
             tot[1] = s.l;
@@ -924,12 +945,7 @@ __device__ Stat row_stat(const float* stats, int nchunk, int r) {
         const float* o = stats + ((size_t)r * nchunk + j) * 4;
         stat_merge(s, Stat{o[0], o[1], o[2], __float_as_int(o[3])});
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        Stat b{__shfl_xor(s.m, o), __shfl_xor(s.l, o), __shfl_xor(s.best, o), __shfl_xor(s.idx, o)};
-        stat_merge(s, b);
-    }
-    return s;
+    return wave_stat(s);
 }
 
 // ONE: a one-session call (descriptor and draft count in the arguments, no
