@@ -26,10 +26,25 @@ __device__ __forceinline__ void st_any(void* p, size_t i, float v, int bf16) {
     else ((float*)p)[i] = v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+// Sums by DPP lane moves (no LDS round trip): quad swaps, half-row and row
+// mirrors give every lane of a 16-lane row its row's sum (the row uniformly
+// active); two row broadcasts (lanes left out add 0) carry rows 0-2 into
+// row 3, whose lane 63 then holds the wave's sum.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    return dpp_add<0x140, 0xF>(v);   // row_mirror
+}
+__device__ __forceinline__ float wave_sum(float v) {   // the whole wave; every lane gets lane 63's sum
+    v = row16_sum(v);
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float block_sum(float v, float* sh) {
@@ -379,8 +394,7 @@ __global__ __launch_bounds__(256) void k_head_finish4(HeadArgs a) {
         if (use_norm) {
             float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w + x2.x * x2.x + x2.y * x2.y +
                        x2.z * x2.z + x2.w * x2.w;
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+            ss = row16_sum(ss);   // the head's 16 lanes are one DPP row
             const float rstd = 1.f / sqrtf(ss / 128.f + a.eps);
             x1 = float4{x1.x * rstd * g1.x, x1.y * rstd * g1.y, x1.z * rstd * g1.z, x1.w * rstd * g1.w};
             x2 = float4{x2.x * rstd * g2.x, x2.y * rstd * g2.y, x2.z * rstd * g2.z, x2.w * rstd * g2.w};
