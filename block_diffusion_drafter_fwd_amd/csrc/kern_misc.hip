@@ -697,10 +697,15 @@ __device__ __forceinline__ void stat_merge(Stat& a, const Stat& b) {
     }
 }
 
+// The repetition penalty of a token in the history: a positive logit times
+// 1 / rho, any other times rho (a multiply and two selects, no branch; the
+// sampling pass and the probability pass use this same form)
+__device__ __forceinline__ float penalize(float z, bool hit, float rho, float inv_rho) {
+    return hit ? z * (z > 0.f ? inv_rho : rho) : z;
+}
 __device__ __forceinline__ float penalized(const SampleArgs& a, const uint32_t* bm, int r, int t) {
-    float z = a.logits[(size_t)r * a.V + t];
-    if (a.use_penalty && ((bm[t >> 5] >> (t & 31)) & 1u)) z = z > 0.f ? z / a.rho : z * a.rho;
-    return z;
+    const float z = a.logits[(size_t)r * a.V + t];
+    return a.use_penalty ? penalize(z, (bm[t >> 5] >> (t & 31)) & 1u, a.rho, 1.f / a.rho) : z;
 }
 
 // A lane's Stat moved by DPP (no LDS round trip); a lane with no source in
@@ -761,7 +766,13 @@ __device__ __forceinline__ float gumbel(float u) {
 // Gumbel-max candidate (or the argmax when greedy).  Eight consecutive tokens
 // per thread: two 16-byte logits loads, one history-bitmap word, one Philox
 // call whose four words carry the eight draws (two 23-bit fields a word).
-template <bool ONE>
+// FULL: every group of eight tokens lies inside the vocabulary (V and the
+// chunk bounds multiples of 8), so no token needs a bounds check.  A
+// thread visits its tokens in ascending id, so on equal keys it keeps the
+// one it holds unless it holds none yet.  The running max and sum of
+// exponentials serve the probabilities only and are skipped without them
+// (a -inf logit adds nothing to the sum).
+template <bool ONE, bool FULL>
 __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int c = blockIdx.x, r = blockIdx.y;
     const RowInfo ri = sample_row<ONE>(a, r);
@@ -770,13 +781,14 @@ __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
     const int t_lo = c * a.chunk, t_hi = min(a.V, t_lo + a.chunk);
     Stat s{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     const bool greedy = a.temperature == 0.f;
+    const bool want_l = a.probs != nullptr;
     const float inv_t = greedy ? 0.f : 1.f / a.temperature;
-    const bool vec = (a.V & 7) == 0;
+    const float inv_rho = 1.f / a.rho;
     const float* zr = a.logits + (size_t)r * a.V;
     for (int oc = (t_lo >> 3) + threadIdx.x; oc * 8 < t_hi; oc += 256) {
         const int t0 = oc * 8;
         float z[8];
-        if (vec) {   // t0 + 7 < V: V and the chunk bounds are multiples of 8
+        if constexpr (FULL) {
             const float4 v0 = *(const float4*)(zr + t0), v1 = *(const float4*)(zr + t0 + 4);
             z[0] = v0.x;
             z[1] = v0.y;
@@ -793,43 +805,43 @@ __global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
         if (a.use_penalty) {
             const uint32_t word = bm[t0 >> 5] >> (t0 & 31);   // the eight tokens share one word
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if ((word >> j) & 1u) z[j] = z[j] > 0.f ? z[j] / a.rho : z[j] * a.rho;
+            for (int j = 0; j < 8; ++j) z[j] = penalize(z[j], (word >> j) & 1u, a.rho, inv_rho);
         }
         if (greedy) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (t0 + j < t_hi && (z[j] > s.best || (z[j] == s.best && t0 + j < s.idx))) {
-                    s.best = z[j];
-                    s.idx = t0 + j;
-                }
+            for (int j = 0; j < 8; ++j) {
+                const bool take = (FULL || t0 + j < t_hi) &&
+                                  (z[j] > s.best || (z[j] == s.best && s.idx == 0x7fffffff));
+                s.best = take ? z[j] : s.best;
+                s.idx = take ? t0 + j : s.idx;
+            }
             continue;
         }
         uint64_t w[4] = {(uint64_t)oc, (uint64_t)ri.pos, (uint64_t)a.round, 0};
         philox4x64_10(w, sd.seed, sd.stream);
         float sv[8];
-        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = (FULL || t0 + j < t_hi) ? z[j] * inv_t : -INFINITY;
+        if (want_l) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+            if (mx > s.m) {
+                s.l = s.m == -INFINITY ? 0.f : s.l * __expf(s.m - mx);
+                s.m = mx;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s.l += sv[j] == -INFINITY ? 0.f : __expf(sv[j] - s.m);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            sv[j] = t0 + j < t_hi ? z[j] * inv_t : -INFINITY;
-            mx = fmaxf(mx, sv[j]);
-        }
-        if (mx > s.m) {
-            s.l = s.m == -INFINITY ? 0.f : s.l * __expf(s.m - mx);
-            s.m = mx;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (t0 + j >= t_hi) break;
-            s.l += __expf(sv[j] - s.m);
             const uint64_t wj = w[j >> 1];
             const uint32_t bits = (j & 1) ? (uint32_t)((wj >> 18) & 0x7FFFFFu) : (uint32_t)(wj >> 41);
             const float u = ((float)bits + 0.5f) * 0x1p-23f;
             const float key = sv[j] + gumbel(u);
-            if (key > s.best || (key == s.best && t0 + j < s.idx)) {
-                s.best = key;
-                s.idx = t0 + j;
-            }
+            const bool take = (FULL || t0 + j < t_hi) && (key > s.best || (key == s.best && s.idx == 0x7fffffff));
+            s.best = take ? key : s.best;
+            s.idx = take ? t0 + j : s.idx;
         }
     }
     s = block_stat(s);
@@ -879,7 +891,10 @@ static hipError_t sample_launch(const SampleArgs& a, hipStream_t st) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_sample_stats<ONE>, dim3(a.nchunk, a.R), dim3(256), 0, st, a);
+    if ((a.V & 7) == 0 && (a.chunk & 7) == 0)
+        hipLaunchKernelGGL((k_sample_stats<ONE, true>), dim3(a.nchunk, a.R), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_sample_stats<ONE, false>), dim3(a.nchunk, a.R), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool probs = a.probs && a.temperature != 0.f;

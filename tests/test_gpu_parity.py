@@ -503,6 +503,52 @@ def test_flush_batch_matches_oracle(cuda, name):
     say(f"[parity] flush_batch {name} worst {rep.worst}")
 
 
+@pytest.mark.parametrize("V", [3001, 8192])
+def test_sample_rows_with_masked_logits(cuda, V):
+    """Rows whose logits are mostly -inf (a caller's banned tokens: the first
+    2048 ids of every row, so whole groups of eight that a thread meets first,
+    and half of the rest), with the penalty on: the probabilities are those of
+    the oracle (zero on the masked ids, summing to one: no NaN from a thread
+    that has seen only -inf), and the ids are never masked and equal the
+    oracle's draws where the top-2 gap exceeds the tie margin.  V = 3001 takes
+    the bounds-checked pass, V = 8192 the one for whole groups of eight."""
+    from block_diffusion_drafter_fwd_amd import sample
+    from oracle.sampler import sample_row
+    cfg = synth.config("qwen", layers=1, vocab=V)
+    w = synth.make_weights(cfg, seed=8, gains="random")
+    d = _drafter(cfg, w, max_sessions=1)
+    s = d.session(1024, seed=8, stream_id=0)
+    fs = synth.FeatureSource(cfg, 8, 0)
+    toks = 2040 + (np.arange(40) * 13) % 90          # history straddling the masked prefix, penalised
+    s.committed(toks, feats_dev(cfg, fs.features(0, 40)), 0)
+    rng = np.random.default_rng(V)
+    z = rng.normal(scale=2.0, size=(12, V)).astype(np.float32)
+    z[:, :2048] = -np.inf
+    z[:, 2048:][rng.random((12, V - 2048)) < 0.5] = -np.inf
+    logits = torch.from_numpy(z).cuda()
+    rep = Report()
+    for rnd, (T, probs) in enumerate(((0.0, False), (0.7, True))):
+        ids, pr = sample([s], [0, 12], logits, T, 1.3, 512, rnd, probs=probs)
+        ids = ids.cpu().numpy()
+        assert np.all(np.isfinite(z[np.arange(12), ids])), ids
+        zd = z.astype(np.float64)
+        zf = np.where(np.isfinite(zd), zd, 0.0)         # (the margins look at the finite logits)
+        ref, orows = [], []
+        for i in range(12):
+            oid, op, sc = sample_row(zd[i], list(toks), T, 1.3, 8, 0, rnd, i)
+            ref.append((oid, sc, id_margin(cfg, zf[i], zf[i], T, 1.3)))
+            orows.append(op)
+        check_ids(ids, ref, rep, orows if probs else None)
+        if probs:
+            pg = pr.double().cpu().numpy()
+            assert np.all(np.isfinite(pg))
+            assert np.all(pg[~np.isfinite(z)] == 0.0)
+            np.testing.assert_allclose(pg.sum(axis=1), 1.0, atol=1e-5)
+            np.testing.assert_allclose(pg, np.stack(orows), rtol=1e-4, atol=1e-8)
+    say(f"[parity] masked sampling V={V}: ids compared {rep.ids_compared}")
+    assert rep.ids_compared >= 18
+
+
 def test_one_session_sample_equals_table_path_and_sees_deferred_history(cuda):
     """A one-session sample call (its descriptor in the kernel arguments, no
     tables) draws exactly what the same session draws inside a two-session
