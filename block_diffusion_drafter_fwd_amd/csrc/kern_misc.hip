@@ -947,7 +947,7 @@ __global__ __launch_bounds__(256) void k_verify_stats(VerifyArgs a) {
             if (sv > s.m) {
                 s.l = s.l * (s.m == -INFINITY ? 0.f : __expf(s.m - sv)) + 1.f;
                 s.m = sv;
-            } else {
+            } else if (sv != -INFINITY) {   // (a -inf logit adds nothing, also before any finite one)
                 s.l += __expf(sv - s.m);
             }
         }

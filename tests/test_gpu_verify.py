@@ -157,6 +157,59 @@ def test_out_of_vocabulary_draft_ids_are_rejected_like_the_oracle(setup, tempera
     assert compared >= 4, compared
 
 
+@pytest.mark.parametrize("temperature", [0.0, 0.9])
+def test_masked_target_rows_verify_like_the_oracle(setup, temperature):
+    """Target rows masked to -inf on most ids (the first 2048, so whole runs a
+    thread meets first, and half of the rest), drafts proposed from the
+    masked target itself up to a point and from an unrelated distribution
+    over the unmasked ids after it: (accepted, next) equal the oracle's, the
+    normaliser stays finite (no NaN from a thread that has seen only -inf),
+    and next is never a masked id."""
+    from block_diffusion_drafter_fwd_amd import verify
+    cfg, d, sessions = setup
+    rng = np.random.default_rng(33)
+    offs = _offsets()
+    R = int(offs[-1])
+    target = rng.normal(scale=2.0, size=(R + len(DRAFTS), V)).astype(np.float32)
+    target[:, :2048] = -np.inf
+    target[:, 2048:][rng.random((R + len(DRAFTS), V - 2048)) < 0.5] = -np.inf
+    q = np.zeros((max(1, R), V), np.float32)
+    ids = np.zeros(max(1, R), np.int32)
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        brk = int(rng.integers(0, n + 1))
+        for i in range(n):
+            ok = np.isfinite(target[r0 + i])
+            if temperature > 0:
+                if i < brk:
+                    qi = softmax(target[r0 + i], temperature)
+                else:
+                    qi = np.where(ok, softmax(np.where(ok, rng.normal(scale=2.0, size=V), -np.inf), 1.0), 0.0)
+                q[offs[k] + i] = qi.astype(np.float32)
+                qi = q[offs[k] + i].astype(np.float64)
+                ids[offs[k] + i] = int(rng.choice(V, p=qi / qi.sum()))
+            else:
+                am = int(np.argmax(target[r0 + i]))
+                ids[offs[k] + i] = am if i < brk else int(rng.choice(np.flatnonzero(ok & (np.arange(V) != am))))
+    probs = torch.from_numpy(q).cuda() if temperature > 0 else None
+    acc, nxt = verify(sessions, offs, torch.from_numpy(target).cuda(), torch.from_numpy(ids).cuda(), probs,
+                      temperature, 7)
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    compared = 0
+    for k, n in enumerate(DRAFTS):
+        r0 = offs[k] + k
+        assert np.isfinite(target[r0 + acc[k], nxt[k]]), (k, acc[k], nxt[k])
+        a, x, info = verify_block(target[r0:r0 + n + 1], ids[offs[k]:offs[k] + n],
+                                  q[offs[k]:offs[k] + n] if temperature > 0 else None, temperature, 100 + k, k, 7)
+        close_test = any(abs(uq - p) <= 1e-5 * max(uq, p, 1e-30) for uq, p in info["tests"] if np.isfinite(uq))
+        sc = np.sort(info["scores"][np.isfinite(info["scores"])])
+        if close_test or (sc.size > 1 and sc[-1] - sc[-2] < 1e-4):
+            continue
+        compared += 1
+        assert (acc[k], nxt[k]) == (a, x), (k, acc[k], nxt[k], a, x)
+    assert compared >= 4, compared
+
+
 def test_verify_rejects_sampling_without_draft_probabilities(setup):
     from block_diffusion_drafter_fwd_amd import DFlashError, verify
     cfg, d, sessions = setup
