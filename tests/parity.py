@@ -210,19 +210,21 @@ class Pair:
 
 
 def id_margin(cfg, z_gpu, z_ref, temperature: float, rho: float = 1.0) -> float:
-    """Gap above which the GPU must return the oracle's id.  Greedy rows: the
-    tie margin (one bf16 ulp of the top logit).  Sampled rows: that margin
-    over T, or twice the row's measured logit deviation in score units when
-    larger — both sides score token t as z'_t/T + g_t with the same g_t, z'
-    moves by at most rho times the logit deviation (the penalty), and two
+    """Gap above which the GPU must return the oracle's id: the tie margin (one
+    bf16 ulp of the top logit, over T when sampling), or twice the row's
+    measured logit deviation in score units when larger.  Both sides score
+    token t as z'_t (greedy) or z'_t/T + g_t with the same g_t (sampling);
+    z' moves by at most rho times the logit deviation (the penalty), and two
     score vectors within d of each other per token agree on the argmax
-    whenever the oracle's top-1/top-2 gap exceeds 2d."""
+    whenever the oracle's top-1/top-2 gap exceeds 2d — greedy rows as much
+    as sampled ones (the bf16 path's logits deviate by up to ~0.1, several
+    ulps of the top logit)."""
     zr = np.asarray(z_ref, dtype=np.float64)
     m = margin(cfg, float(np.max(np.abs(zr))), temperature)
+    d = float(np.max(np.abs(np.asarray(z_gpu, dtype=np.float64) - zr))) * max(1.0, rho)
     if temperature <= 0:
-        return m
-    d = float(np.max(np.abs(np.asarray(z_gpu, dtype=np.float64) - zr))) * max(1.0, rho) / temperature
-    return max(m, 2.0 * d + 1e-4)
+        return max(m, 2.0 * d)
+    return max(m, 2.0 * d / temperature + 1e-4)
 
 
 def check_ids(gpu_ids, ref_rows, rep: Report, probs=None):

@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 
 from tests.parity import Report, tie_probability
 
@@ -53,3 +54,35 @@ def test_greedy_tie_probability_matches_monte_carlo():
         est = float(np.mean([greedy_tie_probability(z, tau) for z in zs]))
         freq = float(np.mean([np.diff(np.partition(z, -2)[-2:])[0] <= tau for z in zs]))
         assert abs(est - freq) <= 0.25 * freq + 3 * math.sqrt(freq * (1 - freq) / rows), (V, tau, est, freq)
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.8])
+def test_id_margin_is_the_argmax_stability_bound(temperature):
+    """Two score vectors within d of each other per token agree on the argmax
+    whenever the reference's top-1/top-2 gap exceeds the margin id_margin
+    returns (greedy rows included): perturb seeded rows by up to d per logit,
+    adversarially on the top two and at random elsewhere, and check every
+    row whose gap clears the margin keeps its argmax; the margin is never
+    below the one-ulp tie margin and does not exceed 2d (+ 1e-4 / T)."""
+    from tests.parity import id_margin, margin, top2_gap
+    import synth
+    cfg = synth.config("qwen", layers=1, vocab=2000)
+    rng = np.random.default_rng(3)
+    kept = 0
+    for trial in range(400):
+        z = rng.normal(scale=3.0, size=2000)
+        d = float(rng.choice([0.0, 0.01, 0.05, 0.1]))
+        delta = rng.uniform(-d, d, size=2000)
+        top = np.argsort(z)[-2:]
+        delta[top[1]], delta[top[0]] = -d, d                  # the worst case for the top two
+        zg = z + delta
+        tau = id_margin(cfg, zg, z, temperature)
+        m = margin(cfg, float(np.max(np.abs(z))), temperature)
+        assert tau >= m - 1e-15
+        assert tau <= max(m, 2 * d / (temperature or 1.0) + (1e-4 if temperature else 0.0)) + 1e-12
+        s = z / temperature if temperature else z
+        sg = zg / temperature if temperature else zg
+        if top2_gap(s) > tau:
+            kept += 1
+            assert int(np.argmax(sg)) == int(np.argmax(s)), (trial, d, tau)
+    assert kept >= 150, kept
