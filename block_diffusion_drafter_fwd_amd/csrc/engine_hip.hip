@@ -110,7 +110,12 @@ public:
         const size_t act = m_.elem;
         w.r_blk = ms * c.block_size;
         w.r_ctx = std::max(c.flush_rows, w.r_blk);
-        w.blk_slices = std::max(1, std::min(8, 4096 / w.r_blk));
+        // K slices of the block path's split GEMMs, at most four: every
+        // slice is read again by the norm or head finish that follows, and
+        // with eight the o_proj / down norms of a 4096-wide model cost more
+        // than the wider splits saved (long 679 -> 689 blocks/s, qwen 1867
+        // -> 1873 at four; at two qwen's 2048-deep GEMMs leave CUs idle, 1781)
+        w.blk_slices = std::max(1, std::min(4, 4096 / w.r_blk));
         const int32_t rmax = std::max(w.r_ctx, w.r_blk);
         const int32_t L = c.layers, H = c.hidden, I = c.intermediate;
         w.items_cap = 4 * std::max(1, attn_target_wg() / c.kv_heads) + ms;
